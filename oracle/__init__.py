@@ -1,0 +1,30 @@
+"""CPU fp64 oracle for page-selected sparse decode attention.
+
+TEST INFRASTRUCTURE ONLY. Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import, call or execute anything in
+this package. The product path (the HIP library and its Python binding) never
+imports it, and this package never imports the product path.
+"""
+
+from .pagesparse_ref import (  # noqa: F401
+    BF16,
+    F32,
+    AMBIGUITY_REL,
+    widen,
+    num_pages,
+    page_token_count,
+    unit_page_meta,
+    page_meta_pool,
+    unit_scores,
+    select_pages,
+    ambiguous_pages,
+    gather_tokens,
+    attend,
+    split_partial,
+    combine_partials,
+    sparse_split_slots,
+    dense_split_pages,
+    unit_step,
+    decode_step,
+    full_decode,
+)

@@ -1,0 +1,363 @@
+"""Plain, slow, fp64 reference of query-aware page-selected sparse decode.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and ``bench.py``'s ``cpu_baseline`` leg, never by the product path. It shares
+no code with the HIP library; the only thing both sides use is the seeded
+input generator in ``workloads/``, which holds none of the arithmetic below.
+
+Sources (cited by page title and section):
+
+* "Don't read the haystack", section "Part two: the skipping": per page keep
+  the elementwise min and max of its keys; the page bound is the sum over d of
+  the larger of q_d*kmin_d and q_d*kmax_d, which upper-bounds every q.k in the
+  page; pages are ranked by the bound, the top k are kept together with the
+  sink page and the last few local pages, and a sparse twin of the dense
+  decode walks that page list.
+* Same page, section "Part one: hitting the wall on purpose": split-KV
+  flash-decoding; each split writes running max, normaliser and unnormalised
+  accumulator in fp32, and a second stage merges them with the log-sum-exp
+  rescale. Contexts need not be multiples of anything.
+* "Attention: Undivided & Uncompressed", section "Traffic": the online
+  softmax merge of two partial softmaxes by rescaling with exp(m1 - m2), whose
+  result equals the full-row softmax exactly.
+* "Training-free sparse attention for long-context LLM decode", section
+  "Strongest signals", item 1: a learned per-head sink logit enters only the
+  softmax denominator, as a virtual key whose value vector is zero.
+* "perf(core): fused sparse-attention decode via page indirection - #1005",
+  sections "The reduction, and why it needed no kernel change" (a token is
+  reached through a page list that need not be adjacent or ordered; one KV
+  head owns its group of query heads) and "Making the selection inspectable
+  and proving it against dense" (output equals a reference restricted to the
+  selected positions).
+
+Readings taken where the pages are silent (each listed again in the design doc):
+
+1. GQA: one page list per (request, KV head); the group's score for a page
+   is the MAX over the group's query heads of the per-head bound. No page says
+   how heads combine; the max keeps the bound admissible for every head of the
+   group. Parity unpinned by the pages (pinned only to this reading).
+2. The budget counts the forced pages: a request with n pages keeps
+   min(budget, n) pages; top-k fills budget - |forced|. Parity unpinned by
+   the pages (pinned only to this reading).
+3. Ties between equal scores go to the lower logical page index; the page
+   list is emitted in ascending logical order.
+4. The bound is unscaled (a positive scale does not change the ranking).
+5. The sink logit is in the same natural-log units as scale*q.k, is not
+   multiplied by scale, and takes no part in page selection.
+6. Only valid tokens (t < seq_len) enter metadata and attention.
+
+Precision: every input is fp32 or bf16. bf16 is widened exactly (its bits
+are the high half of an fp32). Products fp32*bf16 (24+8 bits) and fp32*fp32
+(48 bits) are exact in fp64's 53-bit significand, so the only rounding here is
+fp64 summation, exp and log.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+#: Relative band around the k-th selected score inside which the choice
+#: between pages is reported as ambiguous instead of being required to match.
+AMBIGUITY_REL = 1e-6
+
+
+# ---------------------------------------------------------------------------
+# Storage
+
+
+def widen(a: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """Exact float64 value of stored K/V/meta elements.
+
+    bf16 arrives as its raw 16-bit patterns (uint16); its value is the fp32
+    whose high 16 bits are those bits and whose low 16 bits are zero.
+    """
+    if kv_dtype == BF16:
+        a = np.asarray(a)
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 data must be passed as uint16 bit patterns")
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if kv_dtype == F32:
+        a = np.asarray(a)
+        if a.dtype != np.float32:
+            raise TypeError("f32 data must be float32")
+        return a.astype(np.float64)
+    raise ValueError(f"unknown kv dtype {kv_dtype!r}")
+
+
+def num_pages(seq_len: int, page_size: int) -> int:
+    """Pages a context of seq_len tokens occupies: ceil(seq_len / page_size).
+
+    "Attention: Undivided & Uncompressed", section "Bytes": a paged cache
+    allocates ceil(n/B) pages, so at most one page per sequence is partial.
+    """
+    if seq_len < 0 or page_size <= 0:
+        raise ValueError("seq_len must be >= 0 and page_size > 0")
+    return -(-int(seq_len) // int(page_size))
+
+
+def page_token_count(seq_len: int, p: int, page_size: int) -> int:
+    """Valid tokens on logical page p: those t with p*P <= t < min((p+1)*P, len)."""
+    return max(0, min(page_size, int(seq_len) - p * page_size))
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: page metadata ("Don't read the haystack", "Part two: the skipping")
+
+
+def unit_page_meta(k_pool, kv_dtype, page_table, seq_lens, b, g, page_size):
+    """Elementwise max and min of the valid keys of each logical page.
+
+    Returns (kmax, kmin), each float64 [n_pages(b), D], for request b and KV
+    head g. Slots past the sequence end on the last page are ignored.
+    """
+    n = num_pages(int(seq_lens[b]), page_size)
+    d = k_pool.shape[-1]
+    kmax = np.empty((n, d), dtype=np.float64)
+    kmin = np.empty((n, d), dtype=np.float64)
+    for p in range(n):
+        phys = int(page_table[b, p])
+        cnt = page_token_count(int(seq_lens[b]), p, page_size)
+        keys = widen(k_pool[phys, g, :cnt, :], kv_dtype)  # [cnt, D]
+        kmax[p] = keys.max(axis=0)
+        kmin[p] = keys.min(axis=0)
+    return kmax, kmin
+
+
+def page_meta_pool(k_pool, kv_dtype, page_table, seq_lens, page_size, pages_of=None):
+    """Metadata for every mapped physical page, as {(phys, g): (kmax, kmin)}.
+
+    pages_of: optional {b: iterable of logical pages} restricting the build
+    (used for the incremental tail-page update). Physical pages no request
+    maps are absent from the result.
+    """
+    out = {}
+    hkv = k_pool.shape[1]
+    for b in range(page_table.shape[0]):
+        n = num_pages(int(seq_lens[b]), page_size)
+        pages = range(n) if pages_of is None else [p for p in pages_of[b] if 0 <= p < n]
+        for p in pages:
+            phys = int(page_table[b, p])
+            cnt = page_token_count(int(seq_lens[b]), p, page_size)
+            for g in range(hkv):
+                keys = widen(k_pool[phys, g, :cnt, :], kv_dtype)
+                out[(phys, g)] = (keys.max(axis=0), keys.min(axis=0))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: the page bound ("Don't read the haystack", "Part two: the skipping")
+
+
+def unit_scores(q_group: np.ndarray, kmax: np.ndarray, kmin: np.ndarray):
+    """Per-head bounds U[h, p] and the group score S[p] = max_h U[h, p].
+
+    U[h, p] = sum_d max(q[h,d]*kmin[p,d], q[h,d]*kmax[p,d]), the larger of the
+    two products for each coordinate, so U >= q.k for every key in the page.
+    q_group: float64 [G, D] (the query heads sharing this KV head).
+    """
+    q = np.asarray(q_group, dtype=np.float64)
+    prod_min = q[:, None, :] * kmin[None, :, :]  # [G, n, D]
+    prod_max = q[:, None, :] * kmax[None, :, :]
+    u = np.maximum(prod_min, prod_max).sum(axis=-1)  # [G, n]
+    return u, u.max(axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Stage 3: selection
+
+
+def _forced(n: int, n_sink: int, n_local: int):
+    return sorted(set(range(min(n_sink, n))) | set(range(max(0, n - n_local), n)))
+
+
+def select_pages(scores: np.ndarray, n: int, budget: int, n_sink: int, n_local: int):
+    """Logical pages kept for one (request, KV head), ascending.
+
+    If the budget covers all n pages every page is kept (the dense case).
+    Otherwise the first n_sink and last n_local pages are always kept and the
+    remaining budget - |forced| slots go to the other pages in order of
+    decreasing score, ties to the lower page index.
+    Returns (sel: int64 array ascending, forced: list, taken: list of the
+    scored pages in the order they were taken).
+    """
+    if budget >= n:
+        return np.arange(n, dtype=np.int64), list(range(n)), []
+    forced = _forced(n, n_sink, n_local)
+    r = budget - len(forced)
+    if r < 0:
+        raise ValueError("forced pages exceed the budget")
+    fset = set(forced)
+    cand = np.array([p for p in range(n) if p not in fset], dtype=np.int64)
+    s = np.asarray(scores, dtype=np.float64)[cand]
+    order = np.lexsort((cand, -s))  # primary: score descending; then index ascending
+    taken = [int(p) for p in cand[order[:r]]]
+    sel = np.array(sorted(fset | set(taken)), dtype=np.int64)
+    return sel, forced, taken
+
+
+def ambiguous_pages(scores, n, budget, n_sink, n_local, rel=AMBIGUITY_REL):
+    """Scored pages whose score lies within rel*|s_k| of the k-th taken score.
+
+    A page choice inside this set may legitimately differ between an fp32
+    device and this fp64 reference. Returns (set, s_k or None).
+    """
+    sel, forced, taken = select_pages(scores, n, budget, n_sink, n_local)
+    if not taken:
+        return set(), None
+    s = np.asarray(scores, dtype=np.float64)
+    s_k = float(s[taken[-1]])
+    fset = set(forced)
+    amb = {p for p in range(n) if p not in fset and abs(s[p] - s_k) <= rel * abs(s_k)}
+    return amb, s_k
+
+
+# ---------------------------------------------------------------------------
+# Stage 4: attention over the kept tokens
+
+
+def gather_tokens(pool, kv_dtype, page_table, seq_lens, b, g, pages, page_size):
+    """float64 rows [T, D] of the valid tokens on the given logical pages."""
+    rows = []
+    for p in pages:
+        phys = int(page_table[b, int(p)])
+        cnt = page_token_count(int(seq_lens[b]), int(p), page_size)
+        rows.append(widen(pool[phys, g, :cnt, :], kv_dtype))
+    if not rows:
+        return np.zeros((0, pool.shape[-1]), dtype=np.float64)
+    return np.concatenate(rows, axis=0)
+
+
+def attend(q_h, keys, values, scale, sink=None):
+    """Softmax attention of one query over given keys, with an optional sink.
+
+    x_t = scale * (q . k_t). The sink logit s joins only the normaliser, as a
+    key whose value vector is zero ("Training-free sparse attention for
+    long-context LLM decode", "Strongest signals", item 1):
+        M = max(max_t x_t, s);  Z = sum_t e^(x_t - M) + e^(s - M)
+        out = sum_t e^(x_t - M) v_t / Z;  lse = M + ln Z.
+    Plain two-pass evaluation, no online rescaling and no splits.
+    Returns (out float64 [D], lse float).
+    """
+    x = float(scale) * (keys @ np.asarray(q_h, dtype=np.float64))
+    s = -math.inf if sink is None else float(sink)
+    m = max(float(x.max()) if x.size else -math.inf, s)
+    if m == -math.inf:
+        return np.zeros(values.shape[-1]), -math.inf
+    w = np.exp(x - m)
+    z = float(w.sum()) + (math.exp(s - m) if s != -math.inf else 0.0)
+    return (w @ values) / z, m + math.log(z)
+
+
+def split_partial(q_h, keys, values, scale):
+    """Partial softmax state of one KV slice ("Part one": running max, normaliser,
+    unnormalised accumulator). An empty slice gives (-inf, 0, zeros)."""
+    if keys.shape[0] == 0:
+        return -math.inf, 0.0, np.zeros(values.shape[-1])
+    x = float(scale) * (keys @ np.asarray(q_h, dtype=np.float64))
+    m = float(x.max())
+    w = np.exp(x - m)
+    return m, float(w.sum()), w @ values
+
+
+def combine_partials(parts, sink=None):
+    """Log-sum-exp merge of split partials, with the sink as one more partial
+    (m = s, l = 1, acc = 0) ("Attention: Undivided & Uncompressed", "Traffic").
+
+    parts: iterable of (m, l, acc). Returns (out, lse).
+    """
+    parts = list(parts)
+    if sink is not None and float(sink) != -math.inf:
+        parts.append((float(sink), 1.0, np.zeros_like(parts[0][2])))
+    big_m = max(m for m, _, _ in parts)
+    if big_m == -math.inf:
+        return np.zeros_like(parts[0][2]), -math.inf
+    big_l = 0.0
+    acc = np.zeros_like(parts[0][2])
+    for m, l, a in parts:
+        if m == -math.inf:
+            continue
+        w = math.exp(m - big_m)
+        big_l += w * l
+        acc = acc + w * a
+    return acc / big_l, big_m + math.log(big_l)
+
+
+def sparse_split_slots(budget: int, n_splits: int):
+    """Slots [lo, hi) of the kept-page list that split s covers: chunks of
+    ceil(budget / n_splits) slots. Slots past the kept count are empty."""
+    c = -(-budget // n_splits)
+    return [(min(s * c, budget), min((s + 1) * c, budget)) for s in range(n_splits)]
+
+
+def dense_split_pages(n: int, n_splits: int):
+    """Logical pages [lo, hi) that split s of the dense decode covers:
+    chunks of ceil(n / n_splits) pages of this request."""
+    c = -(-n // n_splits)
+    return [(min(s * c, n), min((s + 1) * c, n)) for s in range(n_splits)]
+
+
+# ---------------------------------------------------------------------------
+# Whole step
+
+
+def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None):
+    """Score, select and attend for one (request b, KV head g).
+
+    inp: dict of host arrays with keys q [B,Hq,D] f32, k_pool, v_pool,
+    kv_dtype, page_table, seq_lens, page_size, scale (the fp32 value the
+    device uses), sink ([Hq] f32 or None).
+    sel_override: attend over this page list instead of the selected one.
+    Returns a dict with u, scores, sel, forced, taken, out [G,D], lse [G].
+    """
+    q = inp["q"]
+    hq, hkv = q.shape[1], inp["k_pool"].shape[1]
+    grp = hq // hkv
+    ps = inp["page_size"]
+    n = num_pages(int(inp["seq_lens"][b]), ps)
+    kmax, kmin = unit_page_meta(inp["k_pool"], inp["kv_dtype"], inp["page_table"],
+                                inp["seq_lens"], b, g, ps)
+    qg = q[b, g * grp:(g + 1) * grp].astype(np.float64)
+    u, s = unit_scores(qg, kmax, kmin)
+    sel, forced, taken = select_pages(s, n, budget, n_sink, n_local)
+    pages = sel if sel_override is None else np.asarray(sel_override, dtype=np.int64)
+    keys = gather_tokens(inp["k_pool"], inp["kv_dtype"], inp["page_table"], inp["seq_lens"],
+                         b, g, pages, ps)
+    vals = gather_tokens(inp["v_pool"], inp["kv_dtype"], inp["page_table"], inp["seq_lens"],
+                         b, g, pages, ps)
+    outs, lses = [], []
+    for i in range(grp):
+        h = g * grp + i
+        sk = None if inp.get("sink") is None else inp["sink"][h]
+        o, l = attend(qg[i], keys, vals, inp["scale"], sk)
+        outs.append(o)
+        lses.append(l)
+    return {"u": u, "scores": s, "sel": sel, "forced": forced, "taken": taken,
+            "out": np.stack(outs), "lse": np.array(lses), "n": n}
+
+
+def decode_step(inp, budget, n_sink, n_local, units=None):
+    """unit_step over every (b, g) (or the given list of units)."""
+    b_, hkv = inp["q"].shape[0], inp["k_pool"].shape[1]
+    units = [(b, g) for b in range(b_) for g in range(hkv)] if units is None else units
+    return {(b, g): unit_step(inp, b, g, budget, n_sink, n_local) for b, g in units}
+
+
+def full_decode(inp, b, h):
+    """Exact softmax attention of query head h of request b over every valid
+    token (the dense decode; with the sink folded in when present)."""
+    q = inp["q"]
+    hq, hkv = q.shape[1], inp["k_pool"].shape[1]
+    g = h // (hq // hkv)
+    n = num_pages(int(inp["seq_lens"][b]), inp["page_size"])
+    pages = range(n)
+    keys = gather_tokens(inp["k_pool"], inp["kv_dtype"], inp["page_table"], inp["seq_lens"],
+                         b, g, pages, inp["page_size"])
+    vals = gather_tokens(inp["v_pool"], inp["kv_dtype"], inp["page_table"], inp["seq_lens"],
+                         b, g, pages, inp["page_size"])
+    sk = None if inp.get("sink") is None else inp["sink"][h]
+    return attend(q[b, h].astype(np.float64), keys, vals, inp["scale"], sk)

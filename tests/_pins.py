@@ -1,0 +1,261 @@
+"""Pins of the fp64 oracle against facts it does not compute itself.
+
+Each check takes the oracle module, so the mutation tests can run the same
+check against an oracle with a planted mistake and see it fail.
+"""
+
+from __future__ import annotations
+
+import itertools
+import math
+
+import numpy as np
+import torch
+
+import workloads as wl
+
+
+def small_inputs(**kw):
+    base = dict(name="pin", batch=2, num_q_heads=6, num_kv_heads=2, head_dim=16,
+                ctx_range=(40, 150), budget_pages=4, n_local=1, needles=1, seed=7,
+                permuted_pool=True, max_pages=12)
+    base.update(kw)
+    w = wl.Workload(**base)
+    inp = wl.make_inputs(w, device="cpu")
+    return w, inp, wl.host_inputs(inp)
+
+
+def check_meta_bounds(ref, h):
+    """kmax/kmin bound every valid key, are attained by one, ignore the
+    sentinel slots, and a constant page gives kmax == kmin == the constant."""
+    ps = h["page_size"]
+    for b in range(h["page_table"].shape[0]):
+        for g in range(h["k_pool"].shape[1]):
+            kmax, kmin = ref.unit_page_meta(h["k_pool"], h["kv_dtype"], h["page_table"],
+                                            h["seq_lens"], b, g, ps)
+            n = ref.num_pages(int(h["seq_lens"][b]), ps)
+            assert kmax.shape[0] == n
+            for p in range(n):
+                cnt = ref.page_token_count(int(h["seq_lens"][b]), p, ps)
+                keys = ref.widen(h["k_pool"][int(h["page_table"][b, p]), g, :cnt], h["kv_dtype"])
+                assert np.all(keys <= kmax[p]) and np.all(keys >= kmin[p])
+                assert np.all(np.any(keys == kmax[p], axis=0))
+                assert np.all(np.any(keys == kmin[p], axis=0))
+                assert np.all(np.abs(kmax[p]) < wl.SENTINEL)
+    # constant page
+    kp = np.full((1, 1, ps, 8), 0.375, dtype=np.float32)
+    kmax, kmin = ref.unit_page_meta(kp, "f32", np.zeros((1, 1), np.int32),
+                                    np.array([ps], np.int32), 0, 0, ps)
+    assert np.all(kmax == 0.375) and np.all(kmin == 0.375)
+
+
+def check_score_admissible(ref, h):
+    """The per-page bound is >= every q.k in the page for every query head of
+    the group ("Don't read the haystack", "Part two: the skipping")."""
+    ps = h["page_size"]
+    hq, hkv = h["q"].shape[1], h["k_pool"].shape[1]
+    grp = hq // hkv
+    worst = np.inf
+    for b in range(h["page_table"].shape[0]):
+        for g in range(hkv):
+            kmax, kmin = ref.unit_page_meta(h["k_pool"], h["kv_dtype"], h["page_table"],
+                                            h["seq_lens"], b, g, ps)
+            qg = h["q"][b, g * grp:(g + 1) * grp].astype(np.float64)
+            u, s = ref.unit_scores(qg, kmax, kmin)
+            for p in range(kmax.shape[0]):
+                keys = ref.gather_tokens(h["k_pool"], h["kv_dtype"], h["page_table"],
+                                         h["seq_lens"], b, g, [p], ps)
+                dots = qg @ keys.T  # [G, cnt]
+                assert np.all(u[:, p] >= dots.max(axis=1) - 1e-12 * np.abs(dots).max())
+                assert s[p] >= dots.max() - 1e-12 * np.abs(dots).max()
+                worst = min(worst, float(s[p] - dots.max()))
+    return worst
+
+
+def check_score_closed_forms(ref):
+    """Tight cases and the centre/radius identity of the bound."""
+    rng = np.random.default_rng(3)
+    d = 32
+    q = rng.standard_normal((3, d)).astype(np.float32).astype(np.float64)
+    # one valid key (or a constant page): the bound is exactly q.k
+    k = rng.standard_normal((1, d)).astype(np.float32).astype(np.float64)
+    u, s = ref.unit_scores(q, k, k)
+    np.testing.assert_allclose(u[:, 0], q @ k[0], rtol=1e-13, atol=1e-13)
+    assert s[0] == u[:, 0].max()
+    # identity: max(q*kmin, q*kmax) summed == q.mid + |q|.half
+    kmax = rng.standard_normal((50, d))
+    kmin = kmax - np.abs(rng.standard_normal((50, d)))
+    u, _ = ref.unit_scores(q, kmax, kmin)
+    mid, half = 0.5 * (kmax + kmin), 0.5 * (kmax - kmin)
+    ident = q @ mid.T + np.abs(q) @ half.T
+    np.testing.assert_allclose(u, ident, rtol=1e-12, atol=1e-12)
+    # sign symmetry: U(-q; K) == U(q; -K), and -K swaps the roles of min and max
+    u_neg_q, _ = ref.unit_scores(-q, kmax, kmin)
+    u_neg_k, _ = ref.unit_scores(q, -kmin, -kmax)
+    np.testing.assert_allclose(u_neg_q, u_neg_k, rtol=1e-13, atol=1e-13)
+    # group aggregation: identical heads give the single head's bound; the
+    # group score is one of the heads' bounds and no smaller than any
+    u1, s1 = ref.unit_scores(q[:1], kmax, kmin)
+    _, s_rep = ref.unit_scores(np.repeat(q[:1], 4, axis=0), kmax, kmin)
+    np.testing.assert_array_equal(s_rep, s1)
+    u3, s3 = ref.unit_scores(q, kmax, kmin)
+    assert np.all(s3 >= u3.max(axis=0)) and np.all(np.any(u3 == s3, axis=0))
+
+
+def check_selection_rank_count(ref, scores, n, budget, n_sink, n_local):
+    """Selection re-derived by counting, independent of any sort: a scored
+    page is kept iff fewer than R scored pages beat it (higher score, or equal
+    score and lower index)."""
+    sel, forced, _ = ref.select_pages(scores, n, budget, n_sink, n_local)
+    if budget >= n:
+        assert list(sel) == list(range(n))
+        return
+    fset = set(range(min(n_sink, n))) | set(range(max(0, n - n_local), n))
+    assert set(forced) == fset
+    r = budget - len(fset)
+    cand = [p for p in range(n) if p not in fset]
+    expect = set(fset)
+    for p in cand:
+        beats = sum(1 for o in cand if scores[o] > scores[p] or (scores[o] == scores[p] and o < p))
+        if beats < r:
+            expect.add(p)
+    assert set(int(x) for x in sel) == expect
+    assert len(sel) == min(budget, n)
+    assert list(sel) == sorted(sel)
+
+
+def check_selection_bruteforce(ref, seed=0, trials=60):
+    """On tiny inputs with many ties: the kept scored pages are the
+    lexicographically first R-subset among those of maximum total score."""
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        n = int(rng.integers(2, 11))
+        budget = int(rng.integers(1, n + 2))
+        n_sink = int(rng.integers(0, 2))
+        n_local = int(rng.integers(0, 3))
+        if n_sink + n_local > budget:
+            n_sink, n_local = 0, 0
+        scores = rng.integers(-3, 4, size=n).astype(np.float64)
+        sel, forced, _ = ref.select_pages(scores, n, budget, n_sink, n_local)
+        if budget >= n:
+            assert list(sel) == list(range(n))
+            continue
+        fset = set(range(n_sink)) | set(range(n - n_local, n))
+        cand = [p for p in range(n) if p not in fset]
+        r = budget - len(fset)
+        best = None
+        for sub in itertools.combinations(cand, r):
+            key = (-sum(scores[list(sub)]), sub)
+            if best is None or key < best:
+                best = key
+        assert set(int(x) for x in sel) == fset | set(best[1])
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    qt = torch.from_numpy(np.asarray(q, np.float64)).view(1, 1, 1, -1)
+    kt = torch.from_numpy(np.asarray(k, np.float64)).view(1, 1, k.shape[0], -1)
+    vt = torch.from_numpy(np.asarray(v, np.float64)).view(1, 1, v.shape[0], -1)
+    m = None if mask is None else torch.from_numpy(mask).view(1, 1, 1, -1)
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=m,
+                                                            scale=scale).view(-1).numpy()
+
+
+def check_dense_is_exact_attention(ref, h):
+    """With a budget covering every page the method is exact softmax attention:
+    checked against torch's scaled_dot_product_attention in fp64 on the CPU."""
+    ps = h["page_size"]
+    hq, hkv = h["q"].shape[1], h["k_pool"].shape[1]
+    grp = hq // hkv
+    big = int(h["page_table"].shape[1]) + 1
+    for b in range(h["page_table"].shape[0]):
+        for g in range(hkv):
+            res = ref.unit_step(h, b, g, budget=big, n_sink=0, n_local=0)
+            keys = ref.gather_tokens(h["k_pool"], h["kv_dtype"], h["page_table"], h["seq_lens"],
+                                     b, g, range(res["n"]), ps)
+            vals = ref.gather_tokens(h["v_pool"], h["kv_dtype"], h["page_table"], h["seq_lens"],
+                                     b, g, range(res["n"]), ps)
+            assert keys.shape[0] == int(h["seq_lens"][b])
+            for i in range(grp):
+                o = _sdpa(h["q"][b, g * grp + i], keys, vals, h["scale"])
+                np.testing.assert_allclose(res["out"][i], o, rtol=1e-11, atol=1e-12)
+                o2, l2 = ref.full_decode(h, b, g * grp + i)
+                np.testing.assert_allclose(o2, o, rtol=1e-11, atol=1e-12)
+
+
+def check_restricted_reference(ref, h, budget, n_sink, n_local):
+    """The sparse output equals dense attention with -inf on every token
+    outside the kept pages, and differs from unmasked dense attention."""
+    ps = h["page_size"]
+    hq, hkv = h["q"].shape[1], h["k_pool"].shape[1]
+    grp = hq // hkv
+    differs = 0.0
+    for b in range(h["page_table"].shape[0]):
+        for g in range(hkv):
+            res = ref.unit_step(h, b, g, budget, n_sink, n_local)
+            n = res["n"]
+            keys = ref.gather_tokens(h["k_pool"], h["kv_dtype"], h["page_table"], h["seq_lens"],
+                                     b, g, range(n), ps)
+            vals = ref.gather_tokens(h["v_pool"], h["kv_dtype"], h["page_table"], h["seq_lens"],
+                                     b, g, range(n), ps)
+            tok_page = np.arange(keys.shape[0]) // ps
+            mask = np.where(np.isin(tok_page, res["sel"]), 0.0, -np.inf)
+            for i in range(grp):
+                o = _sdpa(h["q"][b, g * grp + i], keys, vals, h["scale"], mask)
+                np.testing.assert_allclose(res["out"][i], o, rtol=1e-11, atol=1e-12)
+                if budget < n:
+                    full = _sdpa(h["q"][b, g * grp + i], keys, vals, h["scale"])
+                    differs = max(differs, np.linalg.norm(o - full) / np.linalg.norm(full))
+    return differs
+
+
+def check_sink(ref):
+    """The sink is a zero-value virtual key: (a) closed form from the sink-free
+    result, (b) torch SDPA with one extra zero key whose logit is set to the
+    sink through an additive mask, (c) a sink of -inf changes nothing."""
+    rng = np.random.default_rng(11)
+    d, t = 24, 37
+    q = rng.standard_normal(d)
+    k = rng.standard_normal((t, d))
+    v = rng.standard_normal((t, d))
+    scale = 1.0 / math.sqrt(d)
+    o0, l0 = ref.attend(q, k, v, scale)
+    for s in (-3.0, 0.0, 0.7, 2.5, 9.0):
+        o, l = ref.attend(q, k, v, scale, s)
+        np.testing.assert_allclose(o, o0 * math.exp(l0) / (math.exp(l0) + math.exp(s)), rtol=1e-12)
+        np.testing.assert_allclose(l, math.log(math.exp(l0) + math.exp(s)), rtol=1e-13)
+        k2 = np.vstack([k, np.zeros((1, d))])
+        v2 = np.vstack([v, np.zeros((1, d))])
+        mask = np.concatenate([np.zeros(t), [s]])
+        np.testing.assert_allclose(o, _sdpa(q, k2, v2, scale, mask), rtol=1e-11, atol=1e-13)
+    o_inf, l_inf = ref.attend(q, k, v, scale, -math.inf)
+    assert np.array_equal(o_inf, o0) and l_inf == l0
+
+
+def check_split_invariance(ref):
+    """Merging split partials reproduces the unsplit softmax for any split
+    count, including splits with no tokens, with or without a sink."""
+    rng = np.random.default_rng(5)
+    d, t = 16, 53
+    q = rng.standard_normal(d)
+    k = 2.0 * rng.standard_normal((t, d))
+    v = rng.standard_normal((t, d))
+    scale = 0.3
+    for sink in (None, 1.5):
+        o_ref, l_ref = ref.attend(q, k, v, scale, sink)
+        for n_splits in (1, 2, 7, t, t + 5):
+            c = -(-t // n_splits)
+            parts = [ref.split_partial(q, k[s * c:(s + 1) * c], v[s * c:(s + 1) * c], scale)
+                     for s in range(n_splits)]
+            o, l = ref.combine_partials(parts, sink)
+            np.testing.assert_allclose(o, o_ref, rtol=1e-13, atol=1e-14)
+            assert abs(l - l_ref) <= 1e-13 * max(1.0, abs(l_ref))
+
+
+def check_split_ranges(ref):
+    """Split ranges tile [0, budget) and [0, n) exactly and in order."""
+    for total in (1, 5, 64, 127, 128):
+        for ns in (1, 2, 3, 8, 64, 200):
+            for ranges in (ref.sparse_split_slots(total, ns), ref.dense_split_pages(total, ns)):
+                assert len(ranges) == ns
+                covered = [i for lo, hi in ranges for i in range(lo, hi)]
+                assert covered == list(range(total))
