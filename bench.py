@@ -1,0 +1,440 @@
+"""Decode-step benchmark of page-selected sparse decode on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--sets R]
+
+One step = one decode step of the whole hot path over one batch: refresh of
+each request's tail-page metadata, page scores, selection, sparse split-KV
+decode and merge, captured as one HIP graph. R independent input batches are
+drawn and the timed steps cycle through them, so each step reads data that
+the previous steps evicted from the 256 MB memory-side cache (the working set
+of one step is about 204 MB at the b32/64k workload). Before timing, one
+step is checked against the fp64 oracle on sampled (request, KV head) units;
+no timing is printed if that check fails.
+
+Printed: one JSON line with the step time (us per decode step), effective
+HBM bandwidth on algorithmic bytes, the score kernel's roofline (the kernel
+that moves the most bytes), per-kernel times, the in-house dense decode's
+step time and the speedup over it, and the oracle timed on host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "µs/decode-step + effective HBM GB/s (fraction of peak) at batch 32, 64k ctx"
+PEAK_HBM_GBPS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="b32_64k_needles_local4")
+    ap.add_argument("--sets", type=int, default=4, help="independent input batches cycled")
+    ap.add_argument("--dense-steps", type=int, default=20)
+    ap.add_argument("--parity-units", type=int, default=6)
+    ap.add_argument("--cpu-units", type=int, default=16,
+                    help="(request, KV head) units of one step the oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-kernel", default=None,
+                    help="profiling aid: after setup, launch only this stage --steps times "
+                         "(score | step | copy: a 1 GiB device-to-device copy)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# setup
+
+
+def make_set(w, seed, torch, wl, ps):
+    inp = wl.make_inputs(w, device="cuda", seed=seed)
+    g = ps.Geometry.of(inp["q"], inp["k_pool"], inp["page_table"])
+    meta = ps.build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+    step = ps.DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
+                         inp["scale"])
+    tail = torch.tensor([int(n) - 1 for n in inp["n_pages_host"]], device="cuda",
+                        dtype=torch.int32)
+    return {"inp": inp, "g": g, "meta": meta, "step": step, "tail": tail}
+
+
+def run_sparse_step(s):
+    inp, step = s["inp"], s["step"]
+    step.refresh_tail_meta(inp["k_pool"], inp["page_table"], inp["seq_lens"], s["tail"],
+                           s["meta"])
+    return step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], s["meta"], inp["page_table"],
+                       inp["seq_lens"], inp["sink"])
+
+
+def run_dense_step(s):
+    inp, step = s["inp"], s["step"]
+    return step.dense(inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                      inp["seq_lens"], inp["sink"])
+
+
+def capture(fn, s, torch):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(2):
+            fn(s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fn(s)
+    torch.cuda.synchronize()
+    return graph
+
+
+# ---------------------------------------------------------------------------
+# oracle views (host copies of one (request, KV head) unit)
+
+
+def unit_host(inp, b, g, wl):
+    w = inp["workload"]
+    grp = w.group
+    n = int(inp["n_pages_host"][b])
+    phys = inp["page_table"][b, :n].long()
+    import numpy as np
+    sink = None if inp["sink"] is None else inp["sink"][g * grp:(g + 1) * grp].cpu().numpy()
+    return {
+        "q": inp["q"][b:b + 1, g * grp:(g + 1) * grp].cpu().numpy(),
+        "k_pool": wl.kv_bits_numpy(inp["k_pool"][phys, g:g + 1]),
+        "v_pool": wl.kv_bits_numpy(inp["v_pool"][phys, g:g + 1]),
+        "kv_dtype": w.kv_dtype,
+        "page_table": np.arange(n, dtype=np.int32)[None, :],
+        "seq_lens": inp["seq_lens"][b:b + 1].cpu().numpy(),
+        "page_size": w.page_size,
+        "scale": inp["scale"],
+        "sink": sink,
+    }
+
+
+def sample_units(w, k):
+    units = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
+    if k >= len(units):
+        return units
+    stride = len(units) / k
+    return [units[int(i * stride)] for i in range(k)]
+
+
+def parity_gate(s, w, units, wl):
+    """Selection identical to the oracle outside the ambiguity band; output
+    rel-L2 within the gate. Returns a summary dict; raises on failure."""
+    import numpy as np
+
+    import oracle as ref
+
+    gate = 2e-3 if w.kv_dtype == "bf16" else 1e-5
+    step, inp = s["step"], s["inp"]
+    sel = step.sel.cpu().numpy()
+    cnt = step.sel_count.cpu().numpy()
+    out = step.out.cpu().double().numpy()
+    worst, n_amb, n_diff = 0.0, 0, 0
+    for b, g in units:
+        hu = unit_host(inp, b, g, wl)
+        r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local)
+        k = min(w.budget_pages, r["n"])
+        if int(cnt[b, g]) != k:
+            raise AssertionError(f"parity: sel_count {cnt[b, g]} != {k} at unit {(b, g)}")
+        amb, _ = ref.ambiguous_pages(r["scores"], r["n"], w.budget_pages, w.n_sink, w.n_local)
+        got = set(int(x) for x in sel[b, g, :k])
+        want = set(int(x) for x in r["sel"])
+        if got - amb != want - amb:
+            raise AssertionError(f"parity: selection differs outside the band at {(b, g)}")
+        n_amb += len(amb)
+        if got != want:
+            n_diff += 1
+            r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local,
+                              sel_override=sel[b, g, :k])
+        for i in range(w.group):
+            o = out[b, g * w.group + i]
+            e = float(np.linalg.norm(o - r["out"][i]) / np.linalg.norm(r["out"][i]))
+            worst = max(worst, e)
+    if not worst <= gate:
+        raise AssertionError(f"parity: rel-L2 {worst} above {gate}")
+    return {"units_checked": len(units), "max_rel_l2": worst, "gate": gate,
+            "ambiguous_pages": n_amb, "units_differing_inside_band": n_diff}
+
+
+def cpu_baseline(s, w, units, wl):
+    """The fp64 oracle's decode step (score, select, attend; metadata given,
+    as on the device) timed on the host for a sample of units, scaled to the
+    whole step."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as ref
+
+    inp = s["inp"]
+    per_unit = []
+    with threadpool_limits(limits=1):
+        for b, g in units:
+            hu = unit_host(inp, b, g, wl)
+            kmax, kmin = ref.unit_page_meta(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
+                                            hu["seq_lens"], 0, 0, hu["page_size"])
+            t0 = time.perf_counter()
+            qg = hu["q"][0].astype(np.float64)
+            _, sc = ref.unit_scores(qg, kmax, kmin)
+            sel, _, _ = ref.select_pages(sc, kmax.shape[0], w.budget_pages, w.n_sink, w.n_local)
+            keys = ref.gather_tokens(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
+                                     hu["seq_lens"], 0, 0, sel, hu["page_size"])
+            vals = ref.gather_tokens(hu["v_pool"], hu["kv_dtype"], hu["page_table"],
+                                     hu["seq_lens"], 0, 0, sel, hu["page_size"])
+            for i in range(w.group):
+                sk = None if hu["sink"] is None else hu["sink"][i]
+                ref.attend(qg[i], keys, vals, hu["scale"], sk)
+            per_unit.append(time.perf_counter() - t0)
+    total_units = w.batch * w.num_kv_heads
+    us = float(np.mean(per_unit)) * total_units * 1e6
+    return {"value": us, "unit": "us/decode-step", "cores": 1, "kind": "oracle",
+            "sample": f"{len(units)} of {total_units} (request, KV head) units of one step, "
+                      f"single-threaded numpy fp64, scaled x{total_units}/{len(units)}; "
+                      "metadata precomputed as on the device"}
+
+
+# ---------------------------------------------------------------------------
+# measured HBM traffic (committed rocprofv3 counter summary)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("ps_score.hip", "ps_device.h"):
+        with open(os.path.join(ROOT, "sparse_long_context_page_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """Bytes per score-kernel dispatch from the committed counter summary,
+    or None when the summary is absent or was taken on other kernel source."""
+    path = os.path.join(PROFILE_DIR, f"score_pages_{workload}.pmc.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode step has no "
+                                   "cross-GPU work (see DESIGN.md for how it would shard)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    import sparse_long_context_page_amd as ps
+    from sparse_long_context_page_amd import _lib
+    from sparse_long_context_page_amd import accounting as acc
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    _lib.load()  # no fallback: fails loudly if the HIP library is missing
+    w = wl.WORKLOADS[args.workload]
+    print(f"# setup {w.name}: {args.sets} input sets", file=sys.stderr, flush=True)
+    sets = [make_set(w, w.seed + 17 * i, torch, wl, ps) for i in range(args.sets)]
+    torch.cuda.synchronize()
+
+    # -- parity gate on set 0 (eager) --------------------------------------
+    s0 = sets[0]
+    path = s0["step"].path_for(s0["inp"]["seq_lens_host"])
+    if path != "sparse":
+        raise SystemExit(f"workload {w.name} takes the {path} path; nothing sparse to time")
+    out_eager, _ = run_sparse_step(s0)
+    out_eager = out_eager.clone()
+    torch.cuda.synchronize()
+    print("# parity gate", file=sys.stderr, flush=True)
+    parity = parity_gate(s0, w, sample_units(w, args.parity_units), wl)
+
+    if args.only_kernel:
+        profile_only(args, sets, torch, ps)
+        return
+
+    # -- graph-captured step loop (the timed region) -----------------------
+    graphs = [capture(run_sparse_step, s, torch) for s in sets]
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    if not torch.equal(s0["step"].out, out_eager):
+        raise SystemExit("graph replay differs from the eager step")
+    for i in range(args.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    gpu_ms = e0.elapsed_time(e1)
+    ms_per_step = gpu_ms / args.steps
+    print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr,
+          flush=True)
+
+    # -- per-kernel times: HIP events around each launch, same order -------
+    stages = ["tail_meta", "score", "select", "sparse_decode", "combine"]
+    per = {k: [] for k in stages}
+    n_k = max(args.steps // 2, 20)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+           for _ in range(n_k)]
+    for i in range(n_k):
+        s = sets[i % len(sets)]
+        inp, step, ev = s["inp"], s["step"], evs[i]
+        g = s["g"]
+        acc_t, ml_t = step.partials(step.n_splits)
+        ev[0].record()
+        step.refresh_tail_meta(inp["k_pool"], inp["page_table"], inp["seq_lens"], s["tail"],
+                               s["meta"])
+        ev[1].record()
+        ps.ps_score_pages(g, inp["q"], s["meta"], inp["page_table"], inp["seq_lens"],
+                          step.scores)
+        ev[2].record()
+        ps.ps_select_topk(g, step.scores, inp["seq_lens"], step.budget, step.n_sink,
+                          step.n_local, step.sel, step.sel_count)
+        ev[3].record()
+        ps.ps_sparse_decode(g, inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                            inp["seq_lens"], step.sel, step.sel_count, step.budget, step.scale,
+                            step.n_splits, acc_t, ml_t)
+        ev[4].record()
+        ps.ps_combine(g, acc_t, ml_t, step.n_splits, inp["sink"], step.out, step.lse)
+        ev[5].record()
+    torch.cuda.synchronize()
+    for i in range(n_k):
+        for j, k in enumerate(stages):
+            per[k].append(evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3)
+    kern_us = {k: float(np.mean(v[2:])) for k, v in per.items()}
+
+    # -- dense baseline ----------------------------------------------------
+    dgraphs = [capture(run_dense_step, s, torch) for s in sets]
+    for i in range(3):
+        dgraphs[i % len(dgraphs)].replay()
+    torch.cuda.synchronize()
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for i in range(args.dense_steps):
+        dgraphs[i % len(dgraphs)].replay()
+    d1.record()
+    torch.cuda.synchronize()
+    dense_us = d0.elapsed_time(d1) / args.dense_steps * 1e3
+
+    # -- bytes ---------------------------------------------------------------
+    inp0 = s0["inp"]
+    lens = [int(x) for x in inp0["seq_lens_host"]]
+    elem = 2 if w.kv_dtype == "bf16" else 4
+    meta_b = acc.meta_bytes(lens, w.num_kv_heads, w.head_dim, elem, w.page_size)
+    run_sparse_step(s0)
+    torch.cuda.synchronize()
+    sel_h = s0["step"].sel.cpu().numpy()
+    lists = {(b, g): list(sel_h[b, g]) for b in range(w.batch) for g in range(w.num_kv_heads)}
+    kv_b = acc.selected_kv_bytes(lens, lists, w.head_dim, elem, w.page_size)
+    touched = meta_b + kv_b
+    dense_b = acc.dense_kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
+    step_us = ms_per_step * 1e3
+    eff_gbps = touched / (step_us * 1e-6) / 1e9
+    score_gbps = meta_b / (kern_us["score"] * 1e-6) / 1e9
+    decode_gbps = kv_b / (kern_us["sparse_decode"] * 1e-6) / 1e9
+
+    traffic = measured_traffic(w.name)
+    result = {
+        "metric": METRIC,
+        "value": round(step_us, 3),
+        "unit": "us/decode-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads,
+                   "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                   "context": w.context if w.context else list(w.ctx_range),
+                   "page_size": w.page_size, "budget_pages": w.budget_pages,
+                   "n_sink_pages": w.n_sink, "n_local_pages": w.n_local, "needles": w.needles,
+                   "kv_storage": w.kv_dtype, "n_splits": w.n_splits, "input_sets": len(sets),
+                   "path": path, "graph_captured": True},
+        "effective_hbm_gbps": round(eff_gbps, 1),
+        "hbm_frac_of_peak": round(eff_gbps / PEAK_HBM_GBPS, 4),
+        "touched_bytes": touched,
+        "touched_bytes_split": {"metadata": meta_b, "selected_kv": kv_b},
+        "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "selection_overhead_us": round(kern_us["select"], 3),
+        "score_plus_select_us": round(kern_us["score"] + kern_us["select"], 3),
+        "sparse_decode_gbps": round(decode_gbps, 1),
+        "dense_us_per_step": round(dense_us, 3),
+        "dense_bytes": dense_b,
+        "dense_hbm_gbps": round(dense_b / (dense_us * 1e-6) / 1e9, 1),
+        "speedup_vs_dense": round(dense_us / step_us, 3),
+        "timed_wall_ms": round(wall_ms, 3),
+        "parity": parity,
+        "roofline": {"kernel": "ps_score_pages", "bound": "hbm",
+                     "achieved": round(score_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": meta_b,
+                     "avg_launch_us": round(kern_us["score"], 3)},
+    }
+    if not args.no_cpu_baseline:
+        print("# cpu baseline", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(s0, w, sample_units(w, args.cpu_units), wl)
+    print(json.dumps(result), flush=True)
+
+
+def profile_only(args, sets, torch, ps):
+    """Launch one stage repeatedly (for rocprofv3 counter runs)."""
+    for i in range(args.steps):
+        s = sets[i % len(sets)]
+        inp, step, g = s["inp"], s["step"], s["g"]
+        if args.only_kernel == "score":
+            ps.ps_score_pages(g, inp["q"], s["meta"], inp["page_table"], inp["seq_lens"],
+                              step.scores)
+        elif args.only_kernel == "step":
+            run_sparse_step(s)
+        elif args.only_kernel == "copy":
+            # calibration for the HBM byte counters: a plain 1 GiB device copy
+            if i == 0:
+                src = torch.empty(1 << 28, device="cuda", dtype=torch.float32)
+                dst = torch.empty_like(src)
+            dst.copy_(src)
+        else:
+            raise SystemExit(f"unknown stage {args.only_kernel}")
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_only": args.only_kernel, "launches": args.steps}), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,63 @@
+// Host-side launchers of the pagesparse kernels. Arguments reaching these
+// functions have already been validated by the C ABI layer (ps_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ps {
+
+struct Shape {
+  int batch, hq, hkv, group, head_dim, max_pages;
+  int64_t num_phys_pages;
+  int kv_bf16;  // 1: bf16 pools, 0: fp32 pools
+};
+
+hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int32_t* page_table,
+                                  const int32_t* seq_lens, const int32_t* page_begin,
+                                  int n_pages, void* meta, hipStream_t st);
+
+hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
+                              const int32_t* page_table, const int32_t* seq_lens, float* scores,
+                              hipStream_t st);
+
+hipError_t launch_select_topk(const Shape& s, const float* scores, const int32_t* seq_lens,
+                              int budget, int n_sink, int n_local, int32_t* sel,
+                              int32_t* sel_count, hipStream_t st);
+
+hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void* k_pool,
+                         const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
+                         const int32_t* sel, const int32_t* sel_count, int budget, float scale,
+                         int n_splits, float* part_acc, float* part_ml, hipStream_t st);
+
+hipError_t launch_combine(const Shape& s, const float* part_acc, const float* part_ml,
+                          int n_splits, const float* sink, float* out, float* lse,
+                          hipStream_t st);
+
+}  // namespace ps
+
+// Instantiate BODY with a compile-time group size kG in [1, 8].
+#define PS_WITH_GROUP(G, ...)                  \
+  switch (G) {                                 \
+    case 1: { constexpr int kG = 1; __VA_ARGS__; } break; \
+    case 2: { constexpr int kG = 2; __VA_ARGS__; } break; \
+    case 3: { constexpr int kG = 3; __VA_ARGS__; } break; \
+    case 4: { constexpr int kG = 4; __VA_ARGS__; } break; \
+    case 5: { constexpr int kG = 5; __VA_ARGS__; } break; \
+    case 6: { constexpr int kG = 6; __VA_ARGS__; } break; \
+    case 7: { constexpr int kG = 7; __VA_ARGS__; } break; \
+    case 8: { constexpr int kG = 8; __VA_ARGS__; } break; \
+    default: return hipErrorInvalidValue;      \
+  }
+
+// Instantiate BODY with element type TElem and head dimension kD.
+#define PS_WITH_KV(BF16, D, ...)                                          \
+  if (BF16) {                                                             \
+    using TElem = ::ps::bf16_t;                                           \
+    if ((D) == 64) { constexpr int kD = 64; __VA_ARGS__; }                \
+    else { constexpr int kD = 128; __VA_ARGS__; }                         \
+  } else {                                                                \
+    using TElem = float;                                                  \
+    if ((D) == 64) { constexpr int kD = 64; __VA_ARGS__; }                \
+    else { constexpr int kD = 128; __VA_ARGS__; }                         \
+  }

@@ -1,0 +1,95 @@
+// Page metadata: elementwise max and min of the valid keys of each page.
+// ("Don't read the haystack", section "Part two: the skipping".)
+//
+// One wavefront per (request, logical page, KV head). The page's 16 key rows
+// are read with coalesced 16-byte loads (lane = (row group, column vector)),
+// max/min are folded over the lane's rows and then across row groups with
+// cross-lane shuffles, and two lane groups write the kmax and kmin rows.
+// Min/max select stored values, so the result is exact in either dtype.
+#include "ps_device.h"
+#include "ps_launch.h"
+
+namespace ps {
+
+constexpr int kMetaWaves = 4;
+
+template <typename T, int D>
+__global__ __launch_bounds__(kMetaWaves * kWave) void build_page_meta_kernel(
+    const T* __restrict__ k_pool, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_begin, int n_pages,
+    int batch, int hkv, int max_pages, int items_per_req, T* __restrict__ meta) {
+  using L = RowLayout<T, D>;
+  constexpr int V = L::kVec;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t flat = (int64_t)blockIdx.x * kMetaWaves + wave;
+  if (flat >= (int64_t)items_per_req * batch) return;  // tail of the last block
+  const int b = (int)(flat / items_per_req);
+  const int item = (int)(flat % items_per_req);
+
+  const int len = seq_lens[b];
+  const int np = ceil_div(len, kPage);
+  const int64_t begin = page_begin ? page_begin[b] : 0;
+  const int64_t end = begin + n_pages < np ? begin + n_pages : np;
+  const int64_t p = begin + item / hkv;
+  const int g = item % hkv;
+  if (p >= end) return;  // uniform per wavefront
+
+  const int phys = page_table[(int64_t)b * max_pages + p];
+  const int cnt = min(kPage, len - (int)p * kPage);
+  const int r0 = lane / L::kLanesPerRow;
+  const int c = lane % L::kLanesPerRow;
+  const T* src = k_pool + (((int64_t)phys * hkv + g) * kPage) * D + c * V;
+
+  float mx[V], mn[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    mx[j] = -INFINITY;
+    mn[j] = INFINITY;
+  }
+#pragma unroll
+  for (int i = 0; i < L::kLoadsPerPage; ++i) {
+    const int t = r0 + i * L::kRowsPerLoad;
+    if (t < cnt) {
+      float f[V];
+      unpack(ld16(src + (int64_t)t * D), f);
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        mx[j] = fmax_(mx[j], f[j]);
+        mn[j] = fmin_(mn[j], f[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int off = L::kLanesPerRow; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      mx[j] = fmax_(mx[j], __shfl_xor(mx[j], off));
+      mn[j] = fmin_(mn[j], __shfl_xor(mn[j], off));
+    }
+  }
+  if (r0 < 2) {
+    T* dst = meta + ((int64_t)phys * hkv + g) * 2 * D + r0 * D + c * V;
+    st16(dst, r0 == 0 ? pack(mx) : pack(mn));
+  }
+}
+
+hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int32_t* page_table,
+                                  const int32_t* seq_lens, const int32_t* page_begin,
+                                  int n_pages, void* meta, hipStream_t st) {
+  const int pages = n_pages < s.max_pages ? n_pages : s.max_pages;
+  const int items_per_req = pages * s.hkv;
+  const int64_t waves = (int64_t)items_per_req * s.batch;
+  const int64_t blocks = (waves + kMetaWaves - 1) / kMetaWaves;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  dim3 grid((unsigned)blocks), block(kMetaWaves * kWave);
+  PS_WITH_KV(s.kv_bf16, s.head_dim, {
+    hipLaunchKernelGGL((build_page_meta_kernel<TElem, kD>), grid, block, 0, st,
+                       static_cast<const TElem*>(k_pool), page_table, seq_lens, page_begin,
+                       pages, s.batch, s.hkv, s.max_pages, items_per_req,
+                       static_cast<TElem*>(meta));
+  });
+  return hipGetLastError();
+}
+
+}  // namespace ps

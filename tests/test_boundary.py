@@ -1,0 +1,157 @@
+"""The C ABI on the CPU: the library loads, exports exactly what the header
+declares, and rejects every invalid argument with its documented status
+before any HIP call (no call here reaches the GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from sparse_long_context_page_amd import _lib, ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pagesparse.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libpagesparse.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(ps_[a-z_0-9]+)\s*\(", text)
+
+
+def test_header_declares_the_bound_entry_points():
+    assert tuple(declared_functions()) == _lib.ENTRY_POINTS
+
+
+def test_library_exports_exactly_the_header():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    assert {e for e in exported if e.startswith("ps_")} == set(declared_functions())
+
+
+def test_abi_version_and_strerror():
+    assert ops.ps_abi_version() >> 16 == 1
+    for code in range(0, -7, -1):
+        assert ops.ps_strerror(code).startswith("PS_")
+    assert "unknown" in ops.ps_strerror(17)
+
+
+def geom(**kw):
+    base = dict(batch=2, num_q_heads=12, num_kv_heads=2, head_dim=128, page_size=16,
+                max_pages=64, num_phys_pages=128, kv_dtype=_lib.PS_BF16, reserved=0)
+    base.update(kw)
+    return _lib.PsGeom(**base)
+
+
+X = ctypes.c_void_p(4096)  # a non-NULL pointer that is never dereferenced
+
+
+def score(g):
+    return _lib.load().ps_score_pages(g, X, X, X, X, X, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(reserved=1), _lib.PS_ERR_SHAPE),
+    (dict(batch=-1), _lib.PS_ERR_SHAPE),
+    (dict(num_q_heads=0), _lib.PS_ERR_SHAPE),
+    (dict(num_q_heads=13), _lib.PS_ERR_SHAPE),
+    (dict(num_q_heads=32, num_kv_heads=2), _lib.PS_ERR_UNSUPPORTED),
+    (dict(head_dim=96), _lib.PS_ERR_UNSUPPORTED),
+    (dict(head_dim=0), _lib.PS_ERR_SHAPE),
+    (dict(page_size=32), _lib.PS_ERR_UNSUPPORTED),
+    (dict(page_size=0), _lib.PS_ERR_SHAPE),
+    (dict(kv_dtype=7), _lib.PS_ERR_UNSUPPORTED),
+    (dict(max_pages=0), _lib.PS_ERR_SHAPE),
+    (dict(num_phys_pages=0), _lib.PS_ERR_SHAPE),
+    (dict(num_phys_pages=1 << 60), _lib.PS_ERR_OVERFLOW),
+    (dict(num_phys_pages=1 << 31), _lib.PS_ERR_OVERFLOW),
+    (dict(max_pages=1 << 28), _lib.PS_ERR_OVERFLOW),
+    (dict(batch=(1 << 31) - 1, num_q_heads=16, num_kv_heads=16, max_pages=(1 << 27) - 1),
+     _lib.PS_ERR_OVERFLOW),
+    (dict(num_q_heads=16, num_kv_heads=16, max_pages=1 << 27), _lib.PS_ERR_OVERFLOW),
+])
+def test_geometry_validation(kw, code):
+    assert score(geom(**kw)) == code
+
+
+def test_null_geometry():
+    assert _lib.load().ps_score_pages(None, X, X, X, X, X, None) == _lib.PS_ERR_NULL
+
+
+def test_null_pointers():
+    lib = _lib.load()
+    g = geom()
+    assert lib.ps_build_page_meta(g, None, X, X, None, 4, X, None) == _lib.PS_ERR_NULL
+    assert lib.ps_build_page_meta(g, X, X, X, None, 4, None, None) == _lib.PS_ERR_NULL
+    assert lib.ps_score_pages(g, X, None, X, X, X, None) == _lib.PS_ERR_NULL
+    assert lib.ps_select_topk(g, X, X, 8, 0, 0, None, X, None) == _lib.PS_ERR_NULL
+    assert lib.ps_sparse_decode(g, X, X, X, X, X, X, None, 8, 0.1, 2, X, X, None) == \
+        _lib.PS_ERR_NULL
+    assert lib.ps_full_decode(g, X, X, None, X, X, 0.1, 2, X, X, None) == _lib.PS_ERR_NULL
+    assert lib.ps_combine(g, X, X, 2, None, None, None, None) == _lib.PS_ERR_NULL
+
+
+def test_budget_and_split_validation():
+    lib = _lib.load()
+    g = geom()
+    assert lib.ps_build_page_meta(g, X, X, X, None, 0, X, None) == _lib.PS_ERR_SHAPE
+    assert lib.ps_select_topk(g, X, X, 0, 0, 0, X, X, None) == _lib.PS_ERR_BUDGET
+    assert lib.ps_select_topk(g, X, X, 8, -1, 0, X, X, None) == _lib.PS_ERR_BUDGET
+    assert lib.ps_select_topk(g, X, X, 8, 0, -1, X, X, None) == _lib.PS_ERR_BUDGET
+    assert lib.ps_select_topk(g, X, X, 8, 5, 4, X, X, None) == _lib.PS_ERR_BUDGET
+    assert lib.ps_sparse_decode(g, X, X, X, X, X, X, X, 8, 0.1, 0, X, X, None) == \
+        _lib.PS_ERR_BUDGET
+    assert lib.ps_sparse_decode(g, X, X, X, X, X, X, X, 8, 0.1, 9, X, X, None) == \
+        _lib.PS_ERR_BUDGET
+    assert lib.ps_sparse_decode(g, X, X, X, X, X, X, X, 0, 0.1, 1, X, X, None) == \
+        _lib.PS_ERR_BUDGET
+    assert lib.ps_full_decode(g, X, X, X, X, X, 0.1, 65, X, X, None) == _lib.PS_ERR_BUDGET
+    assert lib.ps_full_decode(g, X, X, X, X, X, 0.1, 0, X, X, None) == _lib.PS_ERR_BUDGET
+    assert lib.ps_combine(g, X, X, 0, None, X, None, None) == _lib.PS_ERR_BUDGET
+    assert lib.ps_combine(g, X, X, 5000, None, X, None, None) == _lib.PS_ERR_BUDGET
+
+
+def test_partials_overflow():
+    lib = _lib.load()
+    g = geom(batch=1 << 20, num_q_heads=8, num_kv_heads=8, max_pages=4096)
+    assert lib.ps_combine(g, X, X, 4096, None, X, None, None) == _lib.PS_ERR_OVERFLOW
+
+
+def test_empty_batch_is_a_no_op():
+    # validated, nothing enqueued, no HIP call: the pointers are never touched
+    lib = _lib.load()
+    g = geom(batch=0)
+    assert lib.ps_build_page_meta(g, X, X, X, None, 4, X, None) == _lib.PS_OK
+    assert lib.ps_score_pages(g, X, X, X, X, X, None) == _lib.PS_OK
+    assert lib.ps_select_topk(g, X, X, 8, 1, 2, X, X, None) == _lib.PS_OK
+    assert lib.ps_sparse_decode(g, X, X, X, X, X, X, X, 8, 0.1, 2, X, X, None) == _lib.PS_OK
+    assert lib.ps_full_decode(g, X, X, X, X, X, 0.1, 2, X, X, None) == _lib.PS_OK
+    assert lib.ps_combine(g, X, X, 2, None, X, None, None) == _lib.PS_OK
+
+
+def test_binding_rejects_host_tensors():
+    g = ops.Geometry(1, 4, 1, 64, 4, 4, torch.float32)
+    q = torch.zeros(1, 4, 64)
+    meta = torch.zeros(4, 1, 2, 64)
+    pt = torch.zeros(1, 4, dtype=torch.int32)
+    sl = torch.ones(1, dtype=torch.int32)
+    sc = torch.zeros(1, 1, 4)
+    with pytest.raises(ValueError, match="device tensor"):
+        ops.ps_score_pages(g, q, meta, pt, sl, sc)
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libpagesparse.so")
+    with pytest.raises(_lib.NativeLibraryMissing):
+        _lib.load()

@@ -12,7 +12,8 @@ Recipe (the same for every workload, see each Workload for its sizes):
   seed gives different (but fixed) values on CPU and on the GPU; small draws
   (lengths, needle pages, the pool permutation, sink logits) come from numpy
   PCG64(seed) and are identical on every device.
-* Context lengths are fixed, or uniform integers in an inclusive range.
+* Context lengths are fixed, uniform integers in an inclusive range, or
+  listed explicitly (edge cases).
 * The page table maps logical page p of request b to a physical page. Pools
   are laid out request-major, or (``permuted_pool``) through a seeded random
   permutation of one shared pool. Table entries past a request's last page
@@ -47,6 +48,7 @@ class Workload:
     budget_pages: int
     context: Optional[int] = None          # fixed context length
     ctx_range: Optional[tuple] = None      # (lo, hi) inclusive, for ragged batches
+    lengths: Optional[tuple] = None        # explicit per-request lengths (edge cases)
     page_size: int = 16
     n_sink: int = 0
     n_local: int = 0
@@ -119,7 +121,11 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None):
     b_, hq, hkv, d, ps = w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.page_size
     if hq % hkv:
         raise ValueError("num_q_heads must be a multiple of num_kv_heads")
-    if w.context is not None:
+    if w.lengths is not None:
+        if len(w.lengths) != b_:
+            raise ValueError("lengths must give one length per request")
+        lens = np.array(w.lengths, dtype=np.int64)
+    elif w.context is not None:
         lens = np.full(b_, w.context, dtype=np.int64)
     else:
         lo, hi = w.ctx_range
