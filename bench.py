@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--parity-units", type=int, default=6)
     ap.add_argument("--cpu-units", type=int, default=16,
                     help="(request, KV head) units of one step the oracle is timed on")
+    ap.add_argument("--n-splits", type=int, default=None, help="override the sparse split count")
+    ap.add_argument("--dense-splits", type=int, default=None,
+                    help="override the dense split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-kernel", default=None,
                     help="profiling aid: after setup, launch only this stage --steps times "
@@ -260,6 +263,10 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     _lib.load()  # no fallback: fails loudly if the HIP library is missing
     w = wl.WORKLOADS[args.workload]
+    if args.n_splits:
+        w = w.replace(n_splits=args.n_splits)
+    if args.dense_splits:
+        w = w.replace(dense_splits=args.dense_splits)
     print(f"# setup {w.name}: {args.sets} input sets", file=sys.stderr, flush=True)
     sets = [make_set(w, w.seed + 17 * i, torch, wl, ps) for i in range(args.sets)]
     torch.cuda.synchronize()
@@ -301,6 +308,19 @@ def main():
     ms_per_step = gpu_ms / args.steps
     print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr,
           flush=True)
+
+    # -- the same steps launched eagerly (no graph), back to back -------------
+    for i in range(args.warmup):
+        run_sparse_step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record()
+    for i in range(args.steps):
+        run_sparse_step(sets[i % len(sets)])
+    g1.record()
+    torch.cuda.synchronize()
+    eager_us = g0.elapsed_time(g1) / args.steps * 1e3
 
     # -- per-kernel times: HIP events around each launch, same order -------
     stages = ["tail_meta", "score", "select", "sparse_decode", "combine"]
@@ -348,6 +368,21 @@ def main():
     d1.record()
     torch.cuda.synchronize()
     dense_us = d0.elapsed_time(d1) / args.dense_steps * 1e3
+
+    # -- achievable bandwidth: a plain 2 GiB device-to-device copy --------------
+    src = torch.empty(1 << 29, device="cuda", dtype=torch.float32)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst
 
     # -- bytes ---------------------------------------------------------------
     inp0 = s0["inp"]
@@ -399,7 +434,9 @@ def main():
         "dense_bytes": dense_b,
         "dense_hbm_gbps": round(dense_b / (dense_us * 1e-6) / 1e9, 1),
         "speedup_vs_dense": round(dense_us / step_us, 3),
+        "copy_gbps_read_plus_write": round(copy_gbps, 1),
         "timed_wall_ms": round(wall_ms, 3),
+        "eager_us_per_step": round(eager_us, 3),
         "parity": parity,
         "roofline": {"kernel": "ps_score_pages", "bound": "hbm",
                      "achieved": round(score_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

@@ -6,8 +6,9 @@
 // "Strongest signals", item 1.)
 //
 // One wavefront per (request, query head): lanes stride over the splits for
-// the max and the normaliser (wave reductions), then over the head dimension
-// for the weighted sum of accumulators, splits in order.
+// the max and the normaliser (wave reductions); each lane computes the weight
+// of one split, and the weighted sum of accumulators runs over the head
+// dimension with the weights broadcast by shuffles, splits in order.
 #include "ps_device.h"
 #include "ps_launch.h"
 
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(
     if (lse && lane == 0) lse[row] = -INFINITY;
     return;
   }
+  // Normaliser: lanes stride over the splits, then a wave sum.
   float l = 0.0f;
   for (int s = lane; s < n_splits; s += kWave) {
     const float ms = ml[2 * s];
@@ -56,13 +58,46 @@ __global__ __launch_bounds__(kCombineWaves * kWave) void combine_kernel(
   l = wave_sum(l);
   if (sig != -INFINITY) l += expf(sig - mx);
   const float inv = 1.0f / l;
-  for (int d = lane; d < d_; d += kWave) {
-    float a = 0.0f;
-    for (int s = 0; s < n_splits; ++s) {
-      const float ms = ml[2 * s];
-      if (ms != -INFINITY) a = __builtin_fmaf(expf(ms - mx), acc[(int64_t)s * d_ + d], a);
+
+  // Weighted sum of accumulators, splits in order; a chunk of up to 64 split
+  // weights is held one per lane and broadcast with shuffles, and the
+  // accumulator rows of 8 splits are loaded before they are used.
+  constexpr int kDPerLane = 2;  // head_dim <= 128
+  constexpr int kBatch = 8;
+  float a[kDPerLane] = {0.0f, 0.0f};
+  for (int s0 = 0; s0 < n_splits; s0 += kWave) {
+    const int sl = s0 + lane;
+    float w = 0.0f;
+    if (sl < n_splits) {
+      const float ms = ml[2 * sl];
+      w = ms == -INFINITY ? 0.0f : expf(ms - mx);
     }
-    o[d] = a * inv;
+    const int cnt = min(kWave, n_splits - s0);
+    for (int j0 = 0; j0 < cnt; j0 += kBatch) {
+      float v[kBatch][kDPerLane];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float* src = acc + (int64_t)(s0 + j0 + j) * d_;
+#pragma unroll
+        for (int k = 0; k < kDPerLane; ++k) {
+          const int d = lane + k * kWave;
+          v[j][k] = (j0 + j < cnt && d < d_) ? src[d] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const float wj = __shfl(w, (j0 + j) & (kWave - 1));
+        if (j0 + j < cnt) {
+#pragma unroll
+          for (int k = 0; k < kDPerLane; ++k) a[k] = __builtin_fmaf(wj, v[j][k], a[k]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kDPerLane; ++k) {
+    const int d = lane + k * kWave;
+    if (d < d_) o[d] = a[k] * inv;
   }
   if (lse && lane == 0) lse[row] = mx + logf(l);
 }

@@ -259,6 +259,295 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(
   }
 }
 
+// bf16 K/V: q.k on the matrix cores. A page (16 tokens) is one
+// v_mfma_f32_16x16x32_bf16 row block: A = K (row = token, the 8 contraction
+// coordinates of a lane are 8 consecutive d of one 16-byte load straight from
+// the pool), B = the group's queries scaled by scale*log2(e) (column = head,
+// padded to 16 with zeros), split exactly into hi + mid + lo bf16 terms in
+// LDS once per workgroup and read from there as each product is issued. Lane (token group, head) then holds 4 logits of one
+// head; the page max per head is a 3-step shuffle, the running max is uniform
+// per head and raised lazily (by more than 8 in log2 units), and p =
+// 2^(x - m) is handed to the V owners through LDS. P.V runs on the vector
+// ALUs with V in row layout (lane = (row group, 8 columns)), every lane
+// accumulating all G heads for its rows and columns. The queries are
+// requested first; each wavefront resolves its page ids (list entry, then
+// table entry) a block of 4 ahead, keeps the next page's K and V in flight
+// while the current page is attended, and leaves its accumulators unreduced
+// in LDS for the workgroup merge (no cross-row shuffles).
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// A page as the decode sees it: valid token count (0 = none) and its
+// physical page.
+struct PageRef {
+  int cnt;
+  int phys;
+};
+
+constexpr int kIdBlock = 4;  // page ids a wavefront resolves at a time
+
+template <int D, int G, bool SPARSE>
+__global__ __launch_bounds__(kDecWaves * kWave, 3) void decode_mfma_kernel(
+    const float* __restrict__ q, const bf16_t* __restrict__ k_pool,
+    const bf16_t* __restrict__ v_pool, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ sel_count, int budget, int hkv, int max_pages, int n_splits,
+    float qscale, float* __restrict__ part_acc, float* __restrict__ part_ml) {
+  using L = RowLayout<bf16_t, D>;  // V row layout
+  constexpr int KB = D / 32;
+  constexpr int LPR = L::kLanesPerRow;
+  constexpr int RPL = L::kRowsPerLoad;
+  constexpr int NT = L::kLoadsPerPage;  // V rows per lane per page
+  constexpr int NB = D / 16;            // 16-column blocks of the output
+  static_assert(G <= 8, "group size");
+  __shared__ __align__(16) uint16_t qsp[3][8][D];         // split scaled queries
+  __shared__ __align__(16) uint16_t vt[kDecWaves][16][D];  // V page of each wavefront
+  __shared__ float sm_m[kDecWaves][G], sm_mt[kDecWaves][G], sm_l[kDecWaves][G];
+  __shared__ float sm_acc[kDecWaves][G][D];
+
+  const int split = blockIdx.x % n_splits;
+  const int unit = blockIdx.x / n_splits;  // b * hkv + g
+  const int b = unit / hkv;
+  const int g = unit % hkv;
+  // Uniform per wavefront, so page ids below are scalar loads: they are
+  // counted apart from the vector loads of K and V and never make a wait for
+  // one page's K/V drain the loads of the pages behind it.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  const int col = lane % 16;   // token row of A / head column of B
+  const int kgrp = lane / 16;  // which 8 of each 32 coordinates; token group of D
+  const int rg = lane / LPR;   // V row group
+  const int vc = lane % LPR;   // V column vector
+
+  // The queries are requested first: their split is the first thing waited
+  // for, and vector loads complete in order.
+  const float* qg = q + ((int64_t)b * hkv * G + g * G) * D;
+  constexpr int kQPer = (G * D + kDecWaves * kWave - 1) / (kDecWaves * kWave);
+  float qv[kQPer];
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int e = threadIdx.x + i * kDecWaves * kWave;
+    qv[i] = e < G * D ? qg[e] : 0.0f;
+  }
+
+  const int32_t* list = SPARSE ? sel + (int64_t)unit * budget : nullptr;
+  const int32_t* row = page_table + (int64_t)b * max_pages;
+  const int len = seq_lens[b];
+  int first, hi;
+  if constexpr (SPARSE) {
+    const int per = ceil_div(budget, n_splits);
+    first = split * per;
+    hi = min(first + per, min(sel_count[unit], budget));
+  } else {
+    const int np = ceil_div(len, kPage);
+    const int per = ceil_div(np, n_splits);
+    first = min(split * per, np);
+    hi = min(split * per + per, np);
+  }
+  // Wavefront `wave` takes the split's items first + wave + kDecWaves*k.
+  const int n_items = hi > first + wave ? ceil_div(hi - first - wave, kDecWaves) : 0;
+
+  // Page ids of a block of kIdBlock items (list entry, then table entry).
+  // Every read is in bounds: list slots are clamped to the row, and items
+  // past the wavefront's last one read logical page 0 and get no tokens.
+  auto resolve_block = [&](int blk, PageRef (&refs)[kIdBlock]) {
+    int pg[kIdBlock];
+#pragma unroll
+    for (int j = 0; j < kIdBlock; ++j) {
+      const int item = first + wave + (blk * kIdBlock + j) * kDecWaves;
+      pg[j] = SPARSE ? list[min(item, budget - 1)] : item;
+    }
+#pragma unroll
+    for (int j = 0; j < kIdBlock; ++j) {
+      const bool ok = blk * kIdBlock + j < n_items;
+      const int pc = ok ? pg[j] : 0;
+      refs[j].phys = row[pc];
+      refs[j].cnt = ok ? min(kPage, len - pc * kPage) : 0;
+    }
+  };
+  // All 16 rows of a (page, KV head) block are read (they are in bounds);
+  // rows past the valid count are zeroed in V and masked in the logits.
+  auto load = [&](const PageRef& r, uint4 (&kf)[KB], uint4 (&vf)[NT]) {
+    const int64_t off = ((int64_t)r.phys * hkv + g) * kPage * D;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) kf[kb] = ld16(k_pool + off + col * D + kb * 32 + kgrp * 8);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) vf[i] = ld16(v_pool + off + (rg + i * RPL) * D + vc * 8);
+  };
+
+  PageRef ids[kIdBlock];
+  resolve_block(0, ids);
+
+  // Split of the scaled queries, once per workgroup (the table reads above
+  // are in flight meanwhile).
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int e = threadIdx.x + i * kDecWaves * kWave;
+    if (e < G * D) {
+      uint32_t hi_, mid_, lo_;
+      bf16_split3(qv[i] * qscale, hi_, mid_, lo_);
+      const int h = e / D, d = e % D;
+      qsp[0][h][d] = (uint16_t)hi_;
+      qsp[1][h][d] = (uint16_t)mid_;
+      qsp[2][h][d] = (uint16_t)lo_;
+    }
+  }
+
+  // Two pages in flight before the barrier.
+  uint4 ka[KB], va[NT], kb_[KB], vb[NT];
+  load(ids[0], ka, va);
+  load(ids[1], kb_, vb);
+  __syncthreads();
+  const bool live = col < G;  // lanes of real heads in the B operand
+
+  float m_run = -INFINITY, m_true = -INFINITY, l_part = 0.0f;  // head `col`
+  // P.V accumulators: acc[nb][i] = output of head 4*kgrp+i, column 16*nb+col.
+  f32x4_t acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const int trow = 4 * kgrp + (col >> 2);  // V row this lane hands to the transposed read
+  const int tcol = 4 * (col & 3);          // and its 4-column offset within a 16-column block
+
+  auto attend = [&](const PageRef& r, const uint4 (&kf)[KB], const uint4 (&vf)[NT]) {
+    f32x4_t s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 2; k >= 0; --k)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const uint4 bq = live ? *reinterpret_cast<const uint4*>(&qsp[k][col][kb * 32 + kgrp * 8])
+                              : make_uint4(0, 0, 0, 0);
+        s[kb] = mfma_bf16_16x16x32(kf[kb], bq, s[kb]);
+      }
+    float x[4];
+    {
+      f32x4_t t = s[0];
+#pragma unroll
+      for (int kb = 1; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t[i] += s[kb][i];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] = 4 * kgrp + i < r.cnt ? t[i] : -INFINITY;
+    }
+    float mp = fmax_(fmax_(x[0], x[1]), fmax_(x[2], x[3]));
+    mp = fmax_(mp, __shfl_xor(mp, 16));
+    mp = fmax_(mp, __shfl_xor(mp, 32));
+    m_true = fmax_(m_true, mp);
+    const bool resc = mp > m_run + kLazyRescale;
+    float alpha = 1.0f;
+    if (resc) {
+      alpha = exp2_(m_run - mp);
+      m_run = mp;
+      l_part *= alpha;
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pr[i] = x[i] == -INFINITY ? 0.0f : exp2_(x[i] - m_run);
+    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    // Weights as the A operand of P.V (row = head `col`, k = token 4*kgrp+i),
+    // split into hi + lo bf16 so the product keeps ~16 bits of each weight.
+    uint32_t whi[4], wlo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      whi[i] = bf16_rne_bits(pr[i]);
+      wlo[i] = bf16_rne_bits(pr[i] - bf16_bits_to_float(whi[i]));
+    }
+    const uint2 aph = make_uint2(whi[0] | (whi[1] << 16), whi[2] | (whi[3] << 16));
+    const uint2 apl = make_uint2(wlo[0] | (wlo[1] << 16), wlo[2] | (wlo[3] << 16));
+    if (__any(resc && live)) {
+      // accumulator rows are heads 4*kgrp+i; their factors live in lanes 4*kgrp+i
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = __shfl(alpha, 4 * kgrp + i);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[nb][i] *= ai;
+      }
+    }
+    // Stage V (rows past the valid count as zeros), then P.V per 16 columns
+    // with the B operand read transposed from LDS.
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int t = rg + i * RPL;
+      *reinterpret_cast<uint4*>(&vt[wave][t][vc * 8]) = t < r.cnt ? vf[i] : make_uint4(0, 0, 0, 0);
+    }
+    wave_sync_lds();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const uint2 bv = lds_read_tr16(&vt[wave][trow][nb * 16 + tcol]);
+      acc[nb] = mfma_bf16_16x16x16(apl, bv, acc[nb]);
+      acc[nb] = mfma_bf16_16x16x16(aph, bv, acc[nb]);
+    }
+    wave_sync_lds();  // V is read before the next page overwrites it
+  };
+
+  // Pipeline: the next page's loads are in flight while the current page is
+  // attended; the next block of page ids is resolved a block ahead.
+  PageRef nxt[kIdBlock];
+  for (int base = 0; base < n_items; base += kIdBlock) {
+    resolve_block(base / kIdBlock + 1, nxt);
+#pragma unroll
+    for (int j = 0; j < kIdBlock; j += 2) {
+      if (base + j >= n_items) break;  // uniform per wavefront
+      // ids of items base+j+2 and base+j+3 (possibly in the next block)
+      const PageRef r2 = j + 2 < kIdBlock ? ids[j + 2] : nxt[j + 2 - kIdBlock];
+      const PageRef r3 = j + 3 < kIdBlock ? ids[j + 3] : nxt[j + 3 - kIdBlock];
+      attend(ids[j], ka, va);
+      load(r2, ka, va);
+      if (base + j + 1 < n_items) attend(ids[j + 1], kb_, vb);
+      load(r3, kb_, vb);
+    }
+#pragma unroll
+    for (int j = 0; j < kIdBlock; ++j) ids[j] = nxt[j];
+  }
+
+  // Per wavefront: normaliser over token groups; each (head, column) of the
+  // accumulators is owned by one lane.
+  l_part += __shfl_xor(l_part, 16);
+  l_part += __shfl_xor(l_part, 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * kgrp + i;
+    if (h < G) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) sm_acc[wave][h][nb * 16 + col] = acc[nb][i];
+    }
+  }
+  if (kgrp == 0 && live) {
+    sm_m[wave][col] = m_run;
+    sm_mt[wave][col] = m_true;
+    sm_l[wave][col] = l_part;
+  }
+  __syncthreads();
+
+  // Merge against the split's true max; write the partials.
+  const int hq = hkv * G;
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecWaves * kWave) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float mo = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) mo = fmax_(mo, sm_mt[w][h]);
+    float a = 0.0f, lsum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = sm_m[w][h];
+      const float wt = mw == -INFINITY ? 0.0f : exp2_(mw - mo);
+      a = __builtin_fmaf(wt, sm_acc[w][h][d], a);
+      lsum = __builtin_fmaf(wt, sm_l[w][h], lsum);
+    }
+    const int64_t ph = ((int64_t)b * hq + g * G + h) * n_splits + split;
+    part_acc[ph * D + d] = a;
+    if (d == 0) {
+      part_ml[ph * 2 + 0] = mo == -INFINITY ? -INFINITY : mo * kLn2;
+      part_ml[ph * 2 + 1] = lsum;
+    }
+  }
+}
+
 hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void* k_pool,
                          const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
                          const int32_t* sel, const int32_t* sel_count, int budget, float scale,
@@ -267,7 +556,35 @@ hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(kDecWaves * kWave);
   const float qscale = scale * 1.44269504088896340736f;  // log2(e)
-  PS_WITH_KV(s.kv_bf16, s.head_dim, {
+  if (s.kv_bf16) {
+    PS_WITH_GROUP(s.group, {
+      if (s.head_dim == 64) {
+        if (sparse)
+          hipLaunchKernelGGL((decode_mfma_kernel<64, kG, true>), grid, block, 0, st, q,
+                             static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
+                             page_table, seq_lens, sel, sel_count, budget, s.hkv, s.max_pages,
+                             n_splits, qscale, part_acc, part_ml);
+        else
+          hipLaunchKernelGGL((decode_mfma_kernel<64, kG, false>), grid, block, 0, st, q,
+                             static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
+                             page_table, seq_lens, nullptr, nullptr, 0, s.hkv, s.max_pages,
+                             n_splits, qscale, part_acc, part_ml);
+      } else {
+        if (sparse)
+          hipLaunchKernelGGL((decode_mfma_kernel<128, kG, true>), grid, block, 0, st, q,
+                             static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
+                             page_table, seq_lens, sel, sel_count, budget, s.hkv, s.max_pages,
+                             n_splits, qscale, part_acc, part_ml);
+        else
+          hipLaunchKernelGGL((decode_mfma_kernel<128, kG, false>), grid, block, 0, st, q,
+                             static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
+                             page_table, seq_lens, nullptr, nullptr, 0, s.hkv, s.max_pages,
+                             n_splits, qscale, part_acc, part_ml);
+      }
+    });
+    return hipGetLastError();
+  }
+  PS_WITH_KV(false, s.head_dim, {
     PS_WITH_GROUP(s.group, {
       if (sparse) {
         hipLaunchKernelGGL((decode_kernel<TElem, kD, kG, true>), grid, block, 0, st, q,

@@ -117,4 +117,57 @@ __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// bf16 bits of a finite float, rounded to nearest even.
+__device__ __forceinline__ uint32_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Exact three-term bf16 split of a finite fp32 value: x == hi + mid + lo with
+// every term a bf16 (each residual is exact in fp32 and has at most 16, then
+// 8, significant bits), barring underflow below 2^-100.
+__device__ __forceinline__ void bf16_split3(float x, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  hi = bf16_rne_bits(x);
+  const float r1 = x - bf16_bits_to_float(hi);
+  mid = bf16_rne_bits(r1);
+  const float r2 = r1 - bf16_bits_to_float(mid);
+  lo = bf16_rne_bits(r2);
+}
+
+// Matrix-core fragments of v_mfma_f32_16x16x32_bf16: A and B are 8 bf16 per
+// lane (A: row = lane % 16; B: column = lane % 16; the same 8 contraction
+// indices for a given lane / 16), C and D 4 floats per lane
+// (row = 4 * (lane / 16) + i, column = lane % 16).
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x32(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x16_bf16: A and B are 4 bf16 per lane (A: row = lane % 16,
+// B: column = lane % 16; contraction indices 4 * (lane / 16) + i), C and D as
+// for the 16x16x32 form.
+typedef __attribute__((ext_vector_type(4))) short i16x4_t;
+
+__device__ __forceinline__ f32x4_t mfma_bf16_16x16x16(const uint2& a, const uint2& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                   __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane 4a+e receives
+// element e of the 4-element (8-byte) chunks addressed by lanes a, a+4, a+8
+// and a+12 of its group, in that order. With lane L of group k addressing
+// row 4k + L/4, columns c0 + 4(L%4) .. +3 of a row-major bf16 tile, lane
+// 16k + j receives rows 4k..4k+3 of column c0 + j: the B operand of
+// v_mfma_f32_16x16x16_bf16 with k = row and column = c0 + j.
+__device__ __forceinline__ uint2 lds_read_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
 }  // namespace ps

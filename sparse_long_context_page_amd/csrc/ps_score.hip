@@ -9,9 +9,10 @@
 // a fixed butterfly over the row's lanes. The order is fixed, so results are
 // bitwise reproducible.
 //
-// Work split: a workgroup of 4 wavefronts covers a chunk of consecutive
-// logical pages of one (request, KV head). Within a wavefront, lane =
-// (page slot, column vector): a page's kmax and kmin rows are read as
+// Two kernels: bf16 metadata goes to the matrix cores (below); fp32 metadata
+// uses the vector ALUs: a workgroup of 4 wavefronts covers a chunk of
+// consecutive logical pages of one (request, KV head); within a wavefront,
+// lane = (page slot, column vector); a page's kmax and kmin rows are read as
 // coalesced 16-byte vectors, several pages per wave-load, and all loads of a
 // wavefront's pages are issued before any arithmetic.
 #include "ps_device.h"
@@ -109,11 +110,150 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   }
 }
 
+// bf16 metadata: the contraction on the matrix cores. A 16-page tile is one
+// v_mfma_f32_16x16x32_bf16 column block: B = metadata (column = page, the
+// 8 contraction coordinates of a lane are 8 consecutive d of one 16-byte
+// load), A = the group's queries (row = head, padded to 16 with zeros). The
+// fp32 queries are split exactly into hi + mid + lo bf16 terms and the signs
+// separated (max(q,0) against kmax, min(q,0) against kmin), so every product
+// is exact; each (sign, 32-coordinate block) has its own accumulator (lo, mid,
+// then hi added), and the 2*D/32 accumulators are summed in a fixed tree. The
+// split of a workgroup's queries is computed once, cooperatively, into LDS.
+template <int N>
+__device__ __forceinline__ f32x4_t tree_sum(const f32x4_t (&a)[N]) {
+  if constexpr (N == 1) {
+    return a[0];
+  } else {
+    f32x4_t lo[N / 2], hi[N / 2];
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      lo[i] = a[i];
+      hi[i] = a[N / 2 + i];
+    }
+    const f32x4_t x = tree_sum<N / 2>(lo);
+    const f32x4_t y = tree_sum<N / 2>(hi);
+    f32x4_t r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = x[i] + y[i];
+    return r;
+  }
+}
+
+constexpr int kMfmaWaves = 4;
+constexpr int kMfmaPagesPerBlock = kMfmaWaves * 16;  // one 16-page tile per wavefront
+
+template <int D, int G>
+__global__ __launch_bounds__(kMfmaWaves * kWave) void score_pages_mfma_kernel(
+    const float* __restrict__ q, const bf16_t* __restrict__ meta,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
+    int max_pages, int chunks_per_unit, float* __restrict__ scores) {
+  constexpr int KB = D / 32;  // 32-coordinate blocks
+  static_assert(G <= 8, "group size");
+  // [sign][part][head][d] bf16 bits: sign 0 = max(q,0), 1 = min(q,0);
+  // part 0 = hi, 1 = mid, 2 = lo. Rows G..15 of the A operand are zero.
+  __shared__ __align__(16) uint16_t qsplit[2][3][8][D];
+
+  const int unit = blockIdx.x / chunks_per_unit;  // b * hkv + g
+  const int chunk = blockIdx.x % chunks_per_unit;
+  const int b = unit / hkv;
+  const int g = unit % hkv;
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int col = lane % 16;   // page of the tile (B column), head of A (row)
+  const int kgrp = lane / 16;  // which 8 of each 32 coordinates
+  const int block_p0 = chunk * kMfmaPagesPerBlock;
+  const int p = block_p0 + wave * 16 + col;
+  // The table entry is read together with the length (the row has max_pages
+  // entries, so the read is in bounds); it is used only if p < n_b.
+  const int phys = p < max_pages ? page_table[(int64_t)b * max_pages + p] : 0;
+  const int np = ceil_div(seq_lens[b], kPage);
+  if (block_p0 >= np) return;  // uniform per workgroup
+
+  // 1. this wavefront's tile of metadata
+  uint4 bx[KB], bn[KB];
+  if (p < np) {
+    const bf16_t* src = meta + ((int64_t)phys * hkv + g) * 2 * D + kgrp * 8;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bx[kb] = ld16(src + kb * 32);
+      bn[kb] = ld16(src + D + kb * 32);
+    }
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bx[kb] = make_uint4(0, 0, 0, 0);
+      bn[kb] = make_uint4(0, 0, 0, 0);
+    }
+  }
+
+  // 2. exact split of the group's queries, by sign, into LDS
+  const float* qg = q + ((int64_t)b * hkv * G + g * G) * D;
+  for (int e = threadIdx.x; e < G * D; e += kMfmaWaves * kWave) {
+    const int h = e / D;
+    const int d = e % D;
+    const float v = qg[e];
+    uint32_t part[3];
+    bf16_split3(v, part[0], part[1], part[2]);
+    const bool pos = v > 0.0f;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      qsplit[0][k][h][d] = (uint16_t)(pos ? part[k] : 0u);
+      qsplit[1][k][h][d] = (uint16_t)(pos ? 0u : part[k]);
+    }
+  }
+  __syncthreads();
+  if (block_p0 + wave * 16 >= np) return;  // uniform per wavefront, after the barrier
+
+  // 3. one accumulator per (sign, 32-coordinate block): lo, then mid, then
+  // hi; A fragments are read from LDS as they are needed
+  f32x4_t acc[2 * KB];
+#pragma unroll
+  for (int i = 0; i < 2 * KB; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  const bool live = col < G;
+#pragma unroll
+  for (int k = 2; k >= 0; --k) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      const int off = kb * 32 + kgrp * 8;
+      const uint4 ax = live ? *reinterpret_cast<const uint4*>(&qsplit[0][k][col][off])
+                            : make_uint4(0, 0, 0, 0);
+      const uint4 an = live ? *reinterpret_cast<const uint4*>(&qsplit[1][k][col][off])
+                            : make_uint4(0, 0, 0, 0);
+      acc[kb] = mfma_bf16_16x16x32(ax, bx[kb], acc[kb]);
+      acc[KB + kb] = mfma_bf16_16x16x32(an, bn[kb], acc[KB + kb]);
+    }
+  }
+  const f32x4_t u = tree_sum<2 * KB>(acc);  // u[i] = bound of head 4*kgrp+i on page col
+  float best = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) best = (4 * kgrp + i < G) ? fmax_(best, u[i]) : best;
+  best = fmax_(best, __shfl_xor(best, 16));  // heads 0-3 with 4-7
+  if (kgrp == 0 && p < np) scores[(int64_t)unit * max_pages + p] = best;
+}
+
 hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
                               const int32_t* page_table, const int32_t* seq_lens, float* scores,
                               hipStream_t st) {
   const dim3 block(kScoreWaves * kWave);
-  PS_WITH_KV(s.kv_bf16, s.head_dim, {
+  if (s.kv_bf16) {
+    const int chunks = (s.max_pages + kMfmaPagesPerBlock - 1) / kMfmaPagesPerBlock;
+    const int64_t blocks = (int64_t)chunks * s.batch * s.hkv;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const dim3 grid((unsigned)blocks);
+    PS_WITH_GROUP(s.group, {
+      if (s.head_dim == 64) {
+        hipLaunchKernelGGL((score_pages_mfma_kernel<64, kG>), grid, block, 0, st, q,
+                           static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,
+                           s.max_pages, chunks, scores);
+      } else {
+        hipLaunchKernelGGL((score_pages_mfma_kernel<128, kG>), grid, block, 0, st, q,
+                           static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,
+                           s.max_pages, chunks, scores);
+      }
+    });
+    return hipGetLastError();
+  }
+  PS_WITH_KV(false, s.head_dim, {
     const int per_block = ScoreCfg<TElem, kD>::kPagesPerBlock;
     const int chunks = (s.max_pages + per_block - 1) / per_block;
     const int64_t blocks = (int64_t)chunks * s.batch * s.hkv;
