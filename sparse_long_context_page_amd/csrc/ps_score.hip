@@ -15,6 +15,8 @@
 // lane = (page slot, column vector); a page's kmax and kmin rows are read as
 // coalesced 16-byte vectors, several pages per wave-load, and all loads of a
 // wavefront's pages are issued before any arithmetic.
+#include <algorithm>
+
 #include "ps_device.h"
 #include "ps_launch.h"
 
@@ -119,6 +121,9 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
 // is exact; each (sign, 32-coordinate block) has its own accumulator (lo, mid,
 // then hi added), and the 2*D/32 accumulators are summed in a fixed tree. The
 // split of a workgroup's queries is computed once, cooperatively, into LDS.
+// Each wavefront streams a run of tiles of one (request, KV head): its table
+// entries are read once up front, and the metadata of the next two tiles is
+// in flight while the current tile is scored.
 template <int N>
 __device__ __forceinline__ f32x4_t tree_sum(const f32x4_t (&a)[N]) {
   if constexpr (N == 1) {
@@ -139,14 +144,15 @@ __device__ __forceinline__ f32x4_t tree_sum(const f32x4_t (&a)[N]) {
   }
 }
 
+
 constexpr int kMfmaWaves = 4;
-constexpr int kMfmaPagesPerBlock = kMfmaWaves * 16;  // one 16-page tile per wavefront
+constexpr int kMaxTiles = 32;  // 16-page tiles one wavefront streams at most
 
 template <int D, int G>
-__global__ __launch_bounds__(kMfmaWaves * kWave) void score_pages_mfma_kernel(
+__global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel(
     const float* __restrict__ q, const bf16_t* __restrict__ meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
-    int max_pages, int chunks_per_unit, float* __restrict__ scores) {
+    int max_pages, int chunks_per_unit, int tiles_per_wave, float* __restrict__ scores) {
   constexpr int KB = D / 32;  // 32-coordinate blocks
   static_assert(G <= 8, "group size");
   // [sign][part][head][d] bf16 bits: sign 0 = max(q,0), 1 = min(q,0);
@@ -157,78 +163,116 @@ __global__ __launch_bounds__(kMfmaWaves * kWave) void score_pages_mfma_kernel(
   const int chunk = blockIdx.x % chunks_per_unit;
   const int b = unit / hkv;
   const int g = unit % hkv;
-  const int wave = threadIdx.x / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int lane = threadIdx.x % kWave;
   const int col = lane % 16;   // page of the tile (B column), head of A (row)
   const int kgrp = lane / 16;  // which 8 of each 32 coordinates
-  const int block_p0 = chunk * kMfmaPagesPerBlock;
-  const int p = block_p0 + wave * 16 + col;
-  // The table entry is read together with the length (the row has max_pages
-  // entries, so the read is in bounds); it is used only if p < n_b.
-  const int phys = p < max_pages ? page_table[(int64_t)b * max_pages + p] : 0;
   const int np = ceil_div(seq_lens[b], kPage);
+  const int block_p0 = chunk * kMfmaWaves * tiles_per_wave * 16;
   if (block_p0 >= np) return;  // uniform per workgroup
+  const int p0 = block_p0 + wave * tiles_per_wave * 16;
+  // tiles of this wavefront that hold pages of the request
+  const int n_tiles = p0 < np ? min(tiles_per_wave, ceil_div(np - p0, 16)) : 0;
 
-  // 1. this wavefront's tile of metadata
-  uint4 bx[KB], bn[KB];
-  if (p < np) {
-    const bf16_t* src = meta + ((int64_t)phys * hkv + g) * 2 * D + kgrp * 8;
+  // 1. the queries (needed first), then every table entry of the wavefront's
+  // tiles; pages past the request read its last entry and are not written.
+  const float* qg = q + ((int64_t)b * hkv * G + g * G) * D;
+  constexpr int kQPer = (G * D + kMfmaWaves * kWave - 1) / (kMfmaWaves * kWave);
+  float qv[kQPer];
+#pragma unroll
+  for (int i = 0; i < kQPer; ++i) {
+    const int e = threadIdx.x + i * kMfmaWaves * kWave;
+    qv[i] = e < G * D ? qg[e] : 0.0f;
+  }
+  const int32_t* row = page_table + (int64_t)b * max_pages;
+  int phys[kMaxTiles];
+#pragma unroll
+  for (int t = 0; t < kMaxTiles; ++t)
+    if (t < n_tiles) phys[t] = row[min(p0 + t * 16 + col, np - 1)];
+  auto load = [&](int t, uint4 (&bx)[KB], uint4 (&bn)[KB]) {
+    const bf16_t* src = meta + ((int64_t)phys[t] * hkv + g) * 2 * D + kgrp * 8;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       bx[kb] = ld16(src + kb * 32);
       bn[kb] = ld16(src + D + kb * 32);
     }
-  } else {
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bx[kb] = make_uint4(0, 0, 0, 0);
-      bn[kb] = make_uint4(0, 0, 0, 0);
-    }
-  }
+  };
 
-  // 2. exact split of the group's queries, by sign, into LDS
-  const float* qg = q + ((int64_t)b * hkv * G + g * G) * D;
-  for (int e = threadIdx.x; e < G * D; e += kMfmaWaves * kWave) {
-    const int h = e / D;
-    const int d = e % D;
-    const float v = qg[e];
-    uint32_t part[3];
-    bf16_split3(v, part[0], part[1], part[2]);
-    const bool pos = v > 0.0f;
+  // 2. exact split of the group's queries, by sign, into LDS; fragments to
+  // registers
 #pragma unroll
-    for (int k = 0; k < 3; ++k) {
-      qsplit[0][k][h][d] = (uint16_t)(pos ? part[k] : 0u);
-      qsplit[1][k][h][d] = (uint16_t)(pos ? 0u : part[k]);
+  for (int i = 0; i < kQPer; ++i) {
+    const int e = threadIdx.x + i * kMfmaWaves * kWave;
+    if (e < G * D) {
+      const int h = e / D;
+      const int d = e % D;
+      const float v = qv[i];
+      uint32_t part[3];
+      bf16_split3(v, part[0], part[1], part[2]);
+      const bool pos = v > 0.0f;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        qsplit[0][k][h][d] = (uint16_t)(pos ? part[k] : 0u);
+        qsplit[1][k][h][d] = (uint16_t)(pos ? 0u : part[k]);
+      }
     }
   }
+  uint4 xa[KB], na[KB], xb[KB], nb[KB];  // two tiles of metadata in flight
+  if (n_tiles > 0) load(0, xa, na);
+  if (n_tiles > 1) load(1, xb, nb);
   __syncthreads();
-  if (block_p0 + wave * 16 >= np) return;  // uniform per wavefront, after the barrier
-
-  // 3. one accumulator per (sign, 32-coordinate block): lo, then mid, then
-  // hi; A fragments are read from LDS as they are needed
-  f32x4_t acc[2 * KB];
-#pragma unroll
-  for (int i = 0; i < 2 * KB; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   const bool live = col < G;
+  uint4 a[2][3][KB];
 #pragma unroll
-  for (int k = 2; k >= 0; --k) {
+  for (int sg = 0; sg < 2; ++sg)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int off = kb * 32 + kgrp * 8;
-      const uint4 ax = live ? *reinterpret_cast<const uint4*>(&qsplit[0][k][col][off])
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        a[sg][k][kb] = live ? *reinterpret_cast<const uint4*>(&qsplit[sg][k][col][kb * 32 + kgrp * 8])
                             : make_uint4(0, 0, 0, 0);
-      const uint4 an = live ? *reinterpret_cast<const uint4*>(&qsplit[1][k][col][off])
-                            : make_uint4(0, 0, 0, 0);
-      acc[kb] = mfma_bf16_16x16x32(ax, bx[kb], acc[kb]);
-      acc[KB + kb] = mfma_bf16_16x16x32(an, bn[kb], acc[KB + kb]);
+
+  // 3. per tile: one accumulator per (sign, 32-coordinate block), lo then mid
+  // then hi, summed in a fixed tree; max over the group's heads
+  float* out = scores + (int64_t)unit * max_pages;
+  auto score_tile = [&](int t, const uint4 (&bx)[KB], const uint4 (&bn)[KB]) {
+    f32x4_t acc[2 * KB];
+#pragma unroll
+    for (int i = 0; i < 2 * KB; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int k = 2; k >= 0; --k) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        acc[kb] = mfma_bf16_16x16x32(a[0][k][kb], bx[kb], acc[kb]);
+        acc[KB + kb] = mfma_bf16_16x16x32(a[1][k][kb], bn[kb], acc[KB + kb]);
+      }
     }
-  }
-  const f32x4_t u = tree_sum<2 * KB>(acc);  // u[i] = bound of head 4*kgrp+i on page col
-  float best = -INFINITY;
+    const f32x4_t u = tree_sum<2 * KB>(acc);  // u[i] = bound of head 4*kgrp+i on page col
+    float best = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) best = (4 * kgrp + i < G) ? fmax_(best, u[i]) : best;
-  best = fmax_(best, __shfl_xor(best, 16));  // heads 0-3 with 4-7
-  if (kgrp == 0 && p < np) scores[(int64_t)unit * max_pages + p] = best;
+    for (int i = 0; i < 4; ++i) best = (4 * kgrp + i < G) ? fmax_(best, u[i]) : best;
+    best = fmax_(best, __shfl_xor(best, 16));  // heads 0-3 with 4-7
+    const int p = p0 + t * 16 + col;
+    if (kgrp == 0 && p < np) out[p] = best;
+  };
+  // Steady state: every iteration scores two tiles and requests the next two,
+  // so the number of loads in flight is the same on every path.
+  int t = 0;
+  for (; t + 3 < n_tiles; t += 2) {
+    score_tile(t, xa, na);
+    load(t + 2, xa, na);
+    score_tile(t + 1, xb, nb);
+    load(t + 3, xb, nb);
+  }
+  if (t + 2 < n_tiles) {  // three tiles left
+    score_tile(t, xa, na);
+    load(t + 2, xa, na);
+    score_tile(t + 1, xb, nb);
+    score_tile(t + 2, xa, na);
+  } else {
+    if (t < n_tiles) score_tile(t, xa, na);
+    if (t + 1 < n_tiles) score_tile(t + 1, xb, nb);
+  }
 }
 
 hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
@@ -236,7 +280,13 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
                               hipStream_t st) {
   const dim3 block(kScoreWaves * kWave);
   if (s.kv_bf16) {
-    const int chunks = (s.max_pages + kMfmaPagesPerBlock - 1) / kMfmaPagesPerBlock;
+    // Tiles per wavefront: enough wavefronts for about two per SIMD (1024
+    // SIMDs), each streaming as many 16-page tiles as that leaves.
+    const int tiles_per_unit = (s.max_pages + 15) / 16;
+    const int64_t tiles = (int64_t)tiles_per_unit * s.batch * s.hkv;
+    const int tpw = (int)std::min<int64_t>(kMaxTiles, std::max<int64_t>(1, tiles / 2048));
+    const int per_block = kMfmaWaves * tpw * 16;
+    const int chunks = (s.max_pages + per_block - 1) / per_block;
     const int64_t blocks = (int64_t)chunks * s.batch * s.hkv;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
@@ -244,11 +294,11 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
       if (s.head_dim == 64) {
         hipLaunchKernelGGL((score_pages_mfma_kernel<64, kG>), grid, block, 0, st, q,
                            static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,
-                           s.max_pages, chunks, scores);
+                           s.max_pages, chunks, tpw, scores);
       } else {
         hipLaunchKernelGGL((score_pages_mfma_kernel<128, kG>), grid, block, 0, st, q,
                            static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,
-                           s.max_pages, chunks, scores);
+                           s.max_pages, chunks, tpw, scores);
       }
     });
     return hipGetLastError();
