@@ -143,7 +143,8 @@ int ps_score_pages(const ps_geom* geom, const float* q, const void* meta,
  * sel[b,g,:] lists the kept logical pages in ascending order followed by -1
  * padding; sel_count[b,g] = min(budget_pages, n).
  * Host checks: budget_pages >= 1, n_sink_pages >= 0, n_local_pages >= 0,
- * n_sink_pages + n_local_pages <= budget_pages.
+ * n_sink_pages + n_local_pages <= budget_pages (else PS_ERR_BUDGET);
+ * max_pages <= 65536 (else PS_ERR_UNSUPPORTED).
  * Device precondition: scores are finite (no NaN). */
 int ps_select_topk(const ps_geom* geom, const float* scores, const int32_t* seq_lens,
                    int32_t budget_pages, int32_t n_sink_pages, int32_t n_local_pages,

@@ -109,6 +109,7 @@ PS_API int ps_select_topk(const ps_geom* geom, const float* scores, const int32_
   if (!scores || !seq_lens || !sel || !sel_count) return PS_ERR_NULL;
   if (budget_pages < 1 || n_sink_pages < 0 || n_local_pages < 0) return PS_ERR_BUDGET;
   if ((int64_t)n_sink_pages + n_local_pages > budget_pages) return PS_ERR_BUDGET;
+  if (s.max_pages > ps::kSelectMaxPages) return PS_ERR_UNSUPPORTED;
   int64_t t;
   if (!prod_ok({s.batch, s.hkv, budget_pages, 4}, &t)) return PS_ERR_OVERFLOW;
   if (s.batch == 0) return PS_OK;

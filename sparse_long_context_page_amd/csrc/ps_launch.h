@@ -21,6 +21,9 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
                               const int32_t* page_table, const int32_t* seq_lens, float* scores,
                               hipStream_t st);
 
+// Largest max_pages the selection kernel holds in registers (1M tokens).
+constexpr int kSelectMaxPages = 65536;
+
 hipError_t launch_select_topk(const Shape& s, const float* scores, const int32_t* seq_lens,
                               int budget, int n_sink, int n_local, int32_t* sel,
                               int32_t* sel_count, hipStream_t st);

@@ -119,10 +119,10 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
 // fp32 queries are split exactly into hi + mid + lo bf16 terms and the signs
 // separated (max(q,0) against kmax, min(q,0) against kmin), so every product
 // is exact; each (sign, 32-coordinate block) has its own accumulator (lo, mid,
-// then hi added), and the 2*D/32 accumulators are summed in a fixed tree. The
-// split of a workgroup's queries is computed once, cooperatively, into LDS.
-// Each wavefront streams a run of tiles of one (request, KV head): its table
-// entries are read once up front, and the metadata of the next two tiles is
+// then hi added), and the 2*D/32 accumulators are summed in a fixed tree.
+// Each wavefront streams a run of tiles of one (request, KV head): it splits
+// its own slice of the queries in registers (no LDS, no barrier), reads its
+// table entries once up front, and keeps the metadata of the next two tiles
 // in flight while the current tile is scored.
 template <int N>
 __device__ __forceinline__ f32x4_t tree_sum(const f32x4_t (&a)[N]) {
@@ -146,18 +146,16 @@ __device__ __forceinline__ f32x4_t tree_sum(const f32x4_t (&a)[N]) {
 
 
 constexpr int kMfmaWaves = 4;
-constexpr int kMaxTiles = 32;  // 16-page tiles one wavefront streams at most
+constexpr int kMaxTiles = 16;  // 16-page tiles one wavefront streams at most
 
 template <int D, int G>
 __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel(
     const float* __restrict__ q, const bf16_t* __restrict__ meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
-    int max_pages, int chunks_per_unit, int tiles_per_wave, float* __restrict__ scores) {
+    int max_pages, int last_phys, int chunks_per_unit, int tiles_per_wave,
+    float* __restrict__ scores) {
   constexpr int KB = D / 32;  // 32-coordinate blocks
   static_assert(G <= 8, "group size");
-  // [sign][part][head][d] bf16 bits: sign 0 = max(q,0), 1 = min(q,0);
-  // part 0 = hi, 1 = mid, 2 = lo. Rows G..15 of the A operand are zero.
-  __shared__ __align__(16) uint16_t qsplit[2][3][8][D];
 
   const int unit = blockIdx.x / chunks_per_unit;  // b * hkv + g
   const int chunk = blockIdx.x % chunks_per_unit;
@@ -167,28 +165,40 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   const int lane = threadIdx.x % kWave;
   const int col = lane % 16;   // page of the tile (B column), head of A (row)
   const int kgrp = lane / 16;  // which 8 of each 32 coordinates
-  const int np = ceil_div(seq_lens[b], kPage);
-  const int block_p0 = chunk * kMfmaWaves * tiles_per_wave * 16;
-  if (block_p0 >= np) return;  // uniform per workgroup
-  const int p0 = block_p0 + wave * tiles_per_wave * 16;
-  // tiles of this wavefront that hold pages of the request
-  const int n_tiles = p0 < np ? min(tiles_per_wave, ceil_div(np - p0, 16)) : 0;
+  const bool live = col < G;   // A rows G..15 are zero
+  const int p0 = (chunk * kMfmaWaves + wave) * tiles_per_wave * 16;
 
-  // 1. the queries (needed first), then every table entry of the wavefront's
-  // tiles; pages past the request read its last entry and are not written.
-  const float* qg = q + ((int64_t)b * hkv * G + g * G) * D;
-  constexpr int kQPer = (G * D + kMfmaWaves * kWave - 1) / (kMfmaWaves * kWave);
-  float qv[kQPer];
+  // 1. Everything that does not depend on the request length is requested at
+  // once: the length, the A-operand slice of the queries (8 consecutive
+  // coordinates per 32-block), and the table entries of the wavefront's tiles.
+  // Every load is unconditional and in bounds (padding lanes re-read head
+  // G-1, entries past the run re-read the row's last one): a conditional load
+  // makes later waits cover it, and an early exit lets the compiler sink the
+  // loads behind the length, a round trip more.
+  const int len = seq_lens[b];
+  __builtin_amdgcn_sched_barrier(0);
+  const float* qh = q + ((int64_t)b * hkv * G + g * G + min(col, G - 1)) * D + kgrp * 8;
+  float4 qv[KB][2];
 #pragma unroll
-  for (int i = 0; i < kQPer; ++i) {
-    const int e = threadIdx.x + i * kMfmaWaves * kWave;
-    qv[i] = e < G * D ? qg[e] : 0.0f;
+  for (int kb = 0; kb < KB; ++kb) {
+    qv[kb][0] = *reinterpret_cast<const float4*>(qh + kb * 32);
+    qv[kb][1] = *reinterpret_cast<const float4*>(qh + kb * 32 + 4);
   }
   const int32_t* row = page_table + (int64_t)b * max_pages;
   int phys[kMaxTiles];
 #pragma unroll
+  for (int t = 0; t < kMaxTiles; ++t) phys[t] = row[min(p0 + t * 16 + col, max_pages - 1)];
+  __builtin_amdgcn_sched_barrier(0);  // issue all of the above first
+
+  const int np = ceil_div(len, kPage);
+  // tiles of this wavefront that hold pages of the request
+  const int n_tiles = p0 < np ? min(tiles_per_wave, ceil_div(np - p0, 16)) : 0;
+  // A page past the request reads the metadata of physical page 0 (shared by
+  // all such lanes, so it stays in cache) and its score is not written; an
+  // entry of a live page is clamped into the pool.
+#pragma unroll
   for (int t = 0; t < kMaxTiles; ++t)
-    if (t < n_tiles) phys[t] = row[min(p0 + t * 16 + col, np - 1)];
+    phys[t] = p0 + t * 16 + col < np ? min(max(phys[t], 0), last_phys) : 0;
   auto load = [&](int t, uint4 (&bx)[KB], uint4 (&bn)[KB]) {
     const bf16_t* src = meta + ((int64_t)phys[t] * hkv + g) * 2 * D + kgrp * 8;
 #pragma unroll
@@ -197,40 +207,39 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
       bn[kb] = ld16(src + D + kb * 32);
     }
   };
+  // Two tiles of metadata in flight, requested whatever the run's length.
+  uint4 xa[KB], na[KB], xb[KB], nb[KB];
+  load(0, xa, na);
+  load(1, xb, nb);
+  __builtin_amdgcn_sched_barrier(0);  // the split below overlaps these loads
 
-  // 2. exact split of the group's queries, by sign, into LDS; fragments to
-  // registers
-#pragma unroll
-  for (int i = 0; i < kQPer; ++i) {
-    const int e = threadIdx.x + i * kMfmaWaves * kWave;
-    if (e < G * D) {
-      const int h = e / D;
-      const int d = e % D;
-      const float v = qv[i];
-      uint32_t part[3];
-      bf16_split3(v, part[0], part[1], part[2]);
-      const bool pos = v > 0.0f;
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        qsplit[0][k][h][d] = (uint16_t)(pos ? part[k] : 0u);
-        qsplit[1][k][h][d] = (uint16_t)(pos ? 0u : part[k]);
-      }
-    }
-  }
-  uint4 xa[KB], na[KB], xb[KB], nb[KB];  // two tiles of metadata in flight
-  if (n_tiles > 0) load(0, xa, na);
-  if (n_tiles > 1) load(1, xb, nb);
-  __syncthreads();
-  const bool live = col < G;
+  // 2. exact split of the queries, by sign, straight into A fragments:
+  // a[sign][part][kb], sign 0 = max(q,0), 1 = min(q,0); part 0 = hi, 1 = mid,
+  // 2 = lo; 8 bf16 per lane
   uint4 a[2][3][KB];
 #pragma unroll
-  for (int sg = 0; sg < 2; ++sg)
+  for (int kb = 0; kb < KB; ++kb) {
+    float v[8] = {qv[kb][0].x, qv[kb][0].y, qv[kb][0].z, qv[kb][0].w,
+                  qv[kb][1].x, qv[kb][1].y, qv[kb][1].z, qv[kb][1].w};
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
+    for (int j = 0; j < 8; ++j) v[j] = live ? v[j] : 0.0f;
+    uint32_t part[3][8];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-        a[sg][k][kb] = live ? *reinterpret_cast<const uint4*>(&qsplit[sg][k][col][kb * 32 + kgrp * 8])
-                            : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 8; ++j) bf16_split3(v[j], part[0][j], part[1][j], part[2][j]);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      uint32_t pw[4], nw[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = part[k][2 * j], hi = part[k][2 * j + 1];
+        const bool plo = v[2 * j] > 0.0f, phi = v[2 * j + 1] > 0.0f;
+        pw[j] = (plo ? lo : 0u) | ((phi ? hi : 0u) << 16);
+        nw[j] = (plo ? 0u : lo) | ((phi ? 0u : hi) << 16);
+      }
+      a[0][k][kb] = make_uint4(pw[0], pw[1], pw[2], pw[3]);
+      a[1][k][kb] = make_uint4(nw[0], nw[1], nw[2], nw[3]);
+    }
+  }
 
   // 3. per tile: one accumulator per (sign, 32-coordinate block), lo then mid
   // then hi, summed in a fixed tree; max over the group's heads
@@ -290,15 +299,16 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
     const int64_t blocks = (int64_t)chunks * s.batch * s.hkv;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
+    const int last_phys = (int)std::min<int64_t>(s.num_phys_pages - 1, 0x7fffffff);
     PS_WITH_GROUP(s.group, {
       if (s.head_dim == 64) {
         hipLaunchKernelGGL((score_pages_mfma_kernel<64, kG>), grid, block, 0, st, q,
                            static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,
-                           s.max_pages, chunks, tpw, scores);
+                           s.max_pages, last_phys, chunks, tpw, scores);
       } else {
         hipLaunchKernelGGL((score_pages_mfma_kernel<128, kG>), grid, block, 0, st, q,
                            static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,
-                           s.max_pages, chunks, tpw, scores);
+                           s.max_pages, last_phys, chunks, tpw, scores);
       }
     });
     return hipGetLastError();

@@ -109,6 +109,9 @@ def test_budget_and_split_validation():
     assert lib.ps_select_topk(g, X, X, 8, -1, 0, X, X, None) == _lib.PS_ERR_BUDGET
     assert lib.ps_select_topk(g, X, X, 8, 0, -1, X, X, None) == _lib.PS_ERR_BUDGET
     assert lib.ps_select_topk(g, X, X, 8, 5, 4, X, X, None) == _lib.PS_ERR_BUDGET
+    # the selection holds a request's scores in registers: at most 65536 pages
+    assert lib.ps_select_topk(geom(max_pages=65537), X, X, 8, 0, 0, X, X, None) == \
+        _lib.PS_ERR_UNSUPPORTED
     assert lib.ps_sparse_decode(g, X, X, X, X, X, X, X, 8, 0.1, 0, X, X, None) == \
         _lib.PS_ERR_BUDGET
     assert lib.ps_sparse_decode(g, X, X, X, X, X, X, X, 8, 0.1, 9, X, X, None) == \

@@ -287,3 +287,33 @@ def test_select_large_candidate_count():
     k = int(res["sel_count"][0, 0])
     check_unit_outputs(res, hu, 0, 0, w, w.budget_pages, w.n_sink, w.n_local,
                        sel_dev=res["sel"][0, 0, :k])
+
+
+@pytest.mark.parametrize("max_pages", [1, 512, 513, 4096, 4097, 32768, 65536])
+def test_select_register_tiles(max_pages):
+    """Selection on given scores at the edges of the per-lane register tiles
+    (512 pages per workgroup per step of the tile), with lengths that leave
+    partial wavefront segments, against the oracle's selection."""
+    from sparse_long_context_page_amd.ops import Geometry
+    gen = torch.Generator(device="cpu").manual_seed(max_pages)
+    lengths = sorted({1, max(1, max_pages // 3), max(1, max_pages - 1), max_pages})
+    batch = len(lengths)
+    g = Geometry(batch, 2, 1, 64, max_pages, 1)
+    seq = torch.tensor([n * 16 - 5 if n > 1 else 3 for n in lengths], dtype=torch.int32)
+    for kind in ("normal", "ties"):
+        if kind == "ties":
+            sc = torch.randint(-3, 4, (batch, 1, max_pages), generator=gen).float()
+        else:
+            sc = torch.randn((batch, 1, max_pages), generator=gen) * 30 + 100
+        for budget, ns, nl in ((128, 1, 4), (64, 0, 0), (2, 1, 1)):
+            sel = torch.empty((batch, 1, budget), device="cuda", dtype=torch.int32)
+            cnt = torch.empty((batch, 1), device="cuda", dtype=torch.int32)
+            ops.ps_select_topk(g, sc.cuda(), seq.cuda(), budget, ns, nl, sel, cnt)
+            torch.cuda.synchronize()
+            sel_h, cnt_h = sel.cpu().numpy(), cnt.cpu().numpy()
+            for b, n in enumerate(lengths):
+                want, _, _ = ref.select_pages(sc[b, 0, :n].double().numpy(), n, budget, ns, nl)
+                k = min(budget, n)
+                assert int(cnt_h[b, 0]) == k
+                assert list(sel_h[b, 0, :k]) == list(want), (kind, budget, n)
+                assert all(sel_h[b, 0, k:] == -1)
