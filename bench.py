@@ -73,11 +73,11 @@ def make_set(w, seed, torch, wl, ps):
 
 
 def run_sparse_step(s):
+    """One decode step after a token append: the last pages' metadata are
+    refreshed, then score, select, sparse decode and merge."""
     inp, step = s["inp"], s["step"]
-    step.refresh_tail_meta(inp["k_pool"], inp["page_table"], inp["seq_lens"], s["tail"],
-                           s["meta"])
     return step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], s["meta"], inp["page_table"],
-                       inp["seq_lens"], inp["sink"])
+                       inp["seq_lens"], inp["sink"], refresh_tail=True, tail_begin=s["tail"])
 
 
 def run_dense_step(s):

@@ -131,6 +131,20 @@ int ps_score_pages(const ps_geom* geom, const float* q, const void* meta,
                    const int32_t* page_table, const int32_t* seq_lens, float* scores,
                    void* stream);
 
+/* 1+2. The last page's metadata refreshed inside the page score: one launch
+ * does the work of ps_build_page_meta with page_begin[b] = n_b - 1 and
+ * n_pages = 1, followed by ps_score_pages, with bitwise the same metadata and
+ * scores. ("Don't read the haystack", section "Part two: the skipping": the
+ * page summaries are maintained incrementally as tokens append; a decode step
+ * appends to each request's last page only.) meta is read for every page and
+ * written for page n_b - 1 of every request.
+ * Host checks: those of ps_score_pages; bf16 K (else PS_ERR_UNSUPPORTED).
+ * Device preconditions: as ps_build_page_meta and ps_score_pages; no two
+ * requests share their last physical page. */
+int ps_refresh_score_pages(const ps_geom* geom, const float* q, const void* k_pool, void* meta,
+                           const int32_t* page_table, const int32_t* seq_lens, float* scores,
+                           void* stream);
+
 /* 3. Selection. ("Don't read the haystack", section "Part two: the
  * skipping": keep the top pages by bound plus the sink page and the last
  * local pages; "perf(core): fused sparse-attention decode via page
@@ -169,6 +183,27 @@ int ps_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool, co
                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* sel,
                      const int32_t* sel_count, int32_t budget_pages, float scale,
                      int32_t n_splits, float* part_acc, float* part_ml, void* stream);
+
+/* 3+4a. Selection fused into the sparse decode: one launch does the work of
+ * ps_select_topk followed by ps_sparse_decode, with bitwise the same page
+ * list and partials. ("Training-free sparse attention for long-context LLM
+ * decode", section "Reusable code": a fused single-launch variant of the
+ * sparse decode; "Don't read the haystack", section "Part one: hitting the
+ * wall on purpose": a decode step of small kernels is bound by launches.)
+ * Every split's workgroup selects the (b, g) page list from scores itself
+ * and attends the list slots of its split, so no page list is read back.
+ * sel and sel_count, when not NULL, receive what ps_select_topk writes.
+ * Host checks: those of ps_select_topk and ps_sparse_decode (same codes);
+ * sel and sel_count both NULL or both set (else PS_ERR_NULL); bf16 K/V,
+ * max_pages <= 8192 and ceil(budget_pages / n_splits) <= 512 (else
+ * PS_ERR_UNSUPPORTED).
+ * Device precondition: scores are finite (no NaN). */
+int ps_select_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool,
+                            const void* v_pool, const int32_t* page_table,
+                            const int32_t* seq_lens, const float* scores, int32_t budget_pages,
+                            int32_t n_sink_pages, int32_t n_local_pages, float scale,
+                            int32_t n_splits, int32_t* sel, int32_t* sel_count, float* part_acc,
+                            float* part_ml, void* stream);
 
 /* 4b. Dense split-KV decode: ps_sparse_decode over every page. Split s of a
  * request covers logical pages [s*c_b, min((s+1)*c_b, n_b)) with

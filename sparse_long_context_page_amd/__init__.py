@@ -12,7 +12,9 @@ from .ops import (  # noqa: F401
     ps_build_page_meta,
     ps_combine,
     ps_full_decode,
+    ps_refresh_score_pages,
     ps_score_pages,
+    ps_select_sparse_decode,
     ps_select_topk,
     ps_sparse_decode,
     ps_strerror,

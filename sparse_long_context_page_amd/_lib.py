@@ -25,8 +25,10 @@ PS_BF16 = 1
 ENTRY_POINTS = (
     "ps_build_page_meta",
     "ps_score_pages",
+    "ps_refresh_score_pages",
     "ps_select_topk",
     "ps_sparse_decode",
+    "ps_select_sparse_decode",
     "ps_full_decode",
     "ps_combine",
     "ps_strerror",
@@ -67,8 +69,11 @@ _G = ctypes.POINTER(PsGeom)
 _SIGS = {
     "ps_build_page_meta": [_G, _P, _P, _P, _P, _I, _P, _P],
     "ps_score_pages": [_G, _P, _P, _P, _P, _P, _P],
+    "ps_refresh_score_pages": [_G, _P, _P, _P, _P, _P, _P, _P],
     "ps_select_topk": [_G, _P, _P, _I, _I, _I, _P, _P, _P],
     "ps_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _P, _I, _F, _I, _P, _P, _P],
+    "ps_select_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P, _P, _P,
+                                _P, _P],
     "ps_full_decode": [_G, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P],
     "ps_combine": [_G, _P, _P, _I, _P, _P, _P, _P],
     "ps_strerror": [ctypes.c_int],

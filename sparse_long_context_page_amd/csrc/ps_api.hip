@@ -97,7 +97,21 @@ PS_API int ps_score_pages(const ps_geom* geom, const float* q, const void* meta,
   if (!q || !meta || !page_table || !seq_lens || !scores) return PS_ERR_NULL;
   if (s.batch == 0) return PS_OK;
   return hip_status(
-      ps::launch_score_pages(s, q, meta, page_table, seq_lens, scores, (hipStream_t)stream));
+      ps::launch_score_pages(s, q, meta, page_table, seq_lens, scores, nullptr, nullptr,
+                             (hipStream_t)stream));
+}
+
+PS_API int ps_refresh_score_pages(const ps_geom* geom, const float* q, const void* k_pool,
+                                  void* meta, const int32_t* page_table,
+                                  const int32_t* seq_lens, float* scores, void* stream) {
+  ps::Shape s;
+  int rc = check_geom(geom, &s);
+  if (rc) return rc;
+  if (!q || !k_pool || !meta || !page_table || !seq_lens || !scores) return PS_ERR_NULL;
+  if (!s.kv_bf16) return PS_ERR_UNSUPPORTED;
+  if (s.batch == 0) return PS_OK;
+  return hip_status(ps::launch_score_pages(s, q, meta, page_table, seq_lens, scores, k_pool, meta,
+                                           (hipStream_t)stream));
 }
 
 PS_API int ps_select_topk(const ps_geom* geom, const float* scores, const int32_t* seq_lens,
@@ -138,6 +152,36 @@ PS_API int ps_sparse_decode(const ps_geom* geom, const float* q, const void* k_p
   return hip_status(ps::launch_decode(s, true, q, k_pool, v_pool, page_table, seq_lens, sel,
                                       sel_count, budget_pages, scale, n_splits, part_acc,
                                       part_ml, (hipStream_t)stream));
+}
+
+PS_API int ps_select_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool,
+                                   const void* v_pool, const int32_t* page_table,
+                                   const int32_t* seq_lens, const float* scores,
+                                   int32_t budget_pages, int32_t n_sink_pages,
+                                   int32_t n_local_pages, float scale, int32_t n_splits,
+                                   int32_t* sel, int32_t* sel_count, float* part_acc,
+                                   float* part_ml, void* stream) {
+  ps::Shape s;
+  int rc = check_geom(geom, &s);
+  if (rc) return rc;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !scores || !part_acc || !part_ml)
+    return PS_ERR_NULL;
+  if ((sel == nullptr) != (sel_count == nullptr)) return PS_ERR_NULL;
+  if (budget_pages < 1 || n_sink_pages < 0 || n_local_pages < 0) return PS_ERR_BUDGET;
+  if ((int64_t)n_sink_pages + n_local_pages > budget_pages) return PS_ERR_BUDGET;
+  if (n_splits < 1 || n_splits > budget_pages || n_splits > kMaxSplits) return PS_ERR_BUDGET;
+  if (!s.kv_bf16 || s.max_pages > ps::kSelectDecodeMaxPages ||
+      (budget_pages + n_splits - 1) / n_splits > ps::kMaxSplitPages)
+    return PS_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!prod_ok({s.batch, s.hkv, budget_pages, 4}, &t)) return PS_ERR_OVERFLOW;
+  rc = check_partials(s, n_splits);
+  if (rc) return rc;
+  if (s.batch == 0) return PS_OK;
+  return hip_status(ps::launch_select_decode(s, q, k_pool, v_pool, page_table, seq_lens, scores,
+                                             budget_pages, n_sink_pages, n_local_pages, scale,
+                                             n_splits, sel, sel_count, part_acc, part_ml,
+                                             (hipStream_t)stream));
 }
 
 PS_API int ps_full_decode(const ps_geom* geom, const float* q, const void* k_pool,
@@ -185,4 +229,4 @@ PS_API const char* ps_strerror(int status) {
   }
 }
 
-PS_API int ps_abi_version(void) { return (1 << 16) | 0; }
+PS_API int ps_abi_version(void) { return (1 << 16) | 1; }  // 1.1: fused select + decode

@@ -19,6 +19,7 @@
 // written as fp32 partials (max in natural-log units).
 #include "ps_device.h"
 #include "ps_launch.h"
+#include "ps_select.h"
 
 namespace ps {
 
@@ -289,13 +290,29 @@ struct PageRef {
 
 constexpr int kIdBlock = 4;  // page ids a wavefront resolves at a time
 
-template <int D, int G, bool SPARSE>
-__global__ __launch_bounds__(kDecWaves * kWave, 3) void decode_mfma_kernel(
+// Where a workgroup's pages come from: every page of the request (dense), a
+// page list (sparse), or a selection the workgroup makes itself from the page
+// scores (sparse, fused with the selection: every split of a (request, KV
+// head) runs the same selection and keeps its share of the list).
+enum DecodeMode : int { kDense = 0, kList = 1, kSelect = 2 };
+
+// Selection inputs and outputs of the kSelect mode.
+struct SelectArgs {
+  const float* scores;  // [B, Hkv, max_pages]
+  int n_sink, n_local;
+  int32_t* sel;        // [B, Hkv, budget] or null
+  int32_t* sel_count;  // [B, Hkv] or null
+};
+
+template <int D, int G, int MODE, int C>
+__global__ __launch_bounds__(kDecWaves * kWave, (MODE == kSelect && D == 128) ? 2 : 3)
+void decode_mfma_kernel(
     const float* __restrict__ q, const bf16_t* __restrict__ k_pool,
     const bf16_t* __restrict__ v_pool, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
     const int32_t* __restrict__ sel_count, int budget, int hkv, int max_pages, int n_splits,
-    float qscale, float* __restrict__ part_acc, float* __restrict__ part_ml) {
+    float qscale, float* __restrict__ part_acc, float* __restrict__ part_ml, SelectArgs sa) {
+  constexpr bool SPARSE = MODE != kDense;
   using L = RowLayout<bf16_t, D>;  // V row layout
   constexpr int KB = D / 32;
   constexpr int LPR = L::kLanesPerRow;
@@ -307,6 +324,9 @@ __global__ __launch_bounds__(kDecWaves * kWave, 3) void decode_mfma_kernel(
   __shared__ __align__(16) uint16_t vt[kDecWaves][16][D];  // V page of each wavefront
   __shared__ float sm_m[kDecWaves][G], sm_mt[kDecWaves][G], sm_l[kDecWaves][G];
   __shared__ float sm_acc[kDecWaves][G][D];
+  // kSelect: the selection's workspace and this split's share of the list
+  __shared__ SelectLds<MODE == kSelect ? kDecWaves : 1> ssel;
+  __shared__ int spages[MODE == kSelect ? kMaxSplitPages : 1];
 
   const int split = blockIdx.x % n_splits;
   const int unit = blockIdx.x / n_splits;  // b * hkv + g
@@ -323,7 +343,7 @@ __global__ __launch_bounds__(kDecWaves * kWave, 3) void decode_mfma_kernel(
   const int vc = lane % LPR;   // V column vector
 
   // The queries are requested first: their split is the first thing waited
-  // for, and vector loads complete in order.
+  // for after the page ids, and vector loads complete in order.
   const float* qg = q + ((int64_t)b * hkv * G + g * G) * D;
   constexpr int kQPer = (G * D + kDecWaves * kWave - 1) / (kDecWaves * kWave);
   float qv[kQPer];
@@ -333,11 +353,33 @@ __global__ __launch_bounds__(kDecWaves * kWave, 3) void decode_mfma_kernel(
     qv[i] = e < G * D ? qg[e] : 0.0f;
   }
 
-  const int32_t* list = SPARSE ? sel + (int64_t)unit * budget : nullptr;
+  const int32_t* list = MODE == kList ? sel + (int64_t)unit * budget : nullptr;
   const int32_t* row = page_table + (int64_t)b * max_pages;
   const int len = seq_lens[b];
   int first, hi;
-  if constexpr (SPARSE) {
+  if constexpr (MODE == kSelect) {
+    // The whole workgroup selects the unit's pages; this split keeps list
+    // slots [first, first + per) in LDS and writes them (and the padding
+    // among them) to the page list output.
+    const int per = ceil_div(budget, n_splits);
+    first = split * per;
+    int32_t* dst = sa.sel ? sa.sel + (int64_t)unit * budget : nullptr;
+    const int kept = select_unit<kDecWaves, C>(
+        sa.scores + (int64_t)unit * max_pages, ceil_div(len, kPage), budget, sa.n_sink,
+        sa.n_local, ssel, [&](int o, int p) {
+          if (o >= first && o < first + per) {
+            spages[o - first] = p;
+            if (dst) dst[o] = p;
+          }
+        });
+    __syncthreads();  // spages complete
+    if (dst)
+      for (int o = max(kept, first) + (int)threadIdx.x; o < min(first + per, budget);
+           o += kDecWaves * kWave)
+        dst[o] = -1;
+    if (sa.sel_count && split == 0 && threadIdx.x == 0) sa.sel_count[unit] = kept;
+    hi = min(first + per, kept);
+  } else if constexpr (MODE == kList) {
     const int per = ceil_div(budget, n_splits);
     first = split * per;
     hi = min(first + per, min(sel_count[unit], budget));
@@ -350,6 +392,7 @@ __global__ __launch_bounds__(kDecWaves * kWave, 3) void decode_mfma_kernel(
   // Wavefront `wave` takes the split's items first + wave + kDecWaves*k.
   const int n_items = hi > first + wave ? ceil_div(hi - first - wave, kDecWaves) : 0;
 
+
   // Page ids of a block of kIdBlock items (list entry, then table entry).
   // Every read is in bounds: list slots are clamped to the row, and items
   // past the wavefront's last one read logical page 0 and get no tokens.
@@ -358,7 +401,10 @@ __global__ __launch_bounds__(kDecWaves * kWave, 3) void decode_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < kIdBlock; ++j) {
       const int item = first + wave + (blk * kIdBlock + j) * kDecWaves;
-      pg[j] = SPARSE ? list[min(item, budget - 1)] : item;
+      if constexpr (MODE == kSelect)
+        pg[j] = spages[min(item - first, kMaxSplitPages - 1)];
+      else
+        pg[j] = MODE == kList ? list[min(item, budget - 1)] : item;
     }
 #pragma unroll
     for (int j = 0; j < kIdBlock; ++j) {
@@ -557,29 +603,30 @@ hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void
   const dim3 grid((unsigned)blocks), block(kDecWaves * kWave);
   const float qscale = scale * 1.44269504088896340736f;  // log2(e)
   if (s.kv_bf16) {
+    const SelectArgs none{nullptr, 0, 0, nullptr, nullptr};
     PS_WITH_GROUP(s.group, {
       if (s.head_dim == 64) {
         if (sparse)
-          hipLaunchKernelGGL((decode_mfma_kernel<64, kG, true>), grid, block, 0, st, q,
+          hipLaunchKernelGGL((decode_mfma_kernel<64, kG, kList, 1>), grid, block, 0, st, q,
                              static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
                              page_table, seq_lens, sel, sel_count, budget, s.hkv, s.max_pages,
-                             n_splits, qscale, part_acc, part_ml);
+                             n_splits, qscale, part_acc, part_ml, none);
         else
-          hipLaunchKernelGGL((decode_mfma_kernel<64, kG, false>), grid, block, 0, st, q,
+          hipLaunchKernelGGL((decode_mfma_kernel<64, kG, kDense, 1>), grid, block, 0, st, q,
                              static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
                              page_table, seq_lens, nullptr, nullptr, 0, s.hkv, s.max_pages,
-                             n_splits, qscale, part_acc, part_ml);
+                             n_splits, qscale, part_acc, part_ml, none);
       } else {
         if (sparse)
-          hipLaunchKernelGGL((decode_mfma_kernel<128, kG, true>), grid, block, 0, st, q,
+          hipLaunchKernelGGL((decode_mfma_kernel<128, kG, kList, 1>), grid, block, 0, st, q,
                              static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
                              page_table, seq_lens, sel, sel_count, budget, s.hkv, s.max_pages,
-                             n_splits, qscale, part_acc, part_ml);
+                             n_splits, qscale, part_acc, part_ml, none);
         else
-          hipLaunchKernelGGL((decode_mfma_kernel<128, kG, false>), grid, block, 0, st, q,
+          hipLaunchKernelGGL((decode_mfma_kernel<128, kG, kDense, 1>), grid, block, 0, st, q,
                              static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
                              page_table, seq_lens, nullptr, nullptr, 0, s.hkv, s.max_pages,
-                             n_splits, qscale, part_acc, part_ml);
+                             n_splits, qscale, part_acc, part_ml, none);
       }
     });
     return hipGetLastError();
@@ -599,6 +646,42 @@ hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void
       }
     });
   });
+  return hipGetLastError();
+}
+
+hipError_t launch_select_decode(const Shape& s, const float* q, const void* k_pool,
+                                const void* v_pool, const int32_t* page_table,
+                                const int32_t* seq_lens, const float* scores, int budget,
+                                int n_sink, int n_local, float scale, int n_splits, int32_t* sel,
+                                int32_t* sel_count, float* part_acc, float* part_ml,
+                                hipStream_t st) {
+  const int64_t blocks = (int64_t)s.batch * s.hkv * n_splits;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (!s.kv_bf16 || s.max_pages > kSelectDecodeMaxPages ||
+      (budget + n_splits - 1) / n_splits > kMaxSplitPages)
+    return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(kDecWaves * kWave);
+  const float qscale = scale * 1.44269504088896340736f;  // log2(e)
+  const SelectArgs sa{scores, n_sink, n_local, sel, sel_count};
+  const int per_lane = (s.max_pages + kDecWaves * kWave - 1) / (kDecWaves * kWave);
+#define PS_SELECT_DECODE(DD, CC)                                                              \
+  hipLaunchKernelGGL((decode_mfma_kernel<DD, kG, kSelect, CC>), grid, block, 0, st, q,        \
+                     static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),  \
+                     page_table, seq_lens, nullptr, nullptr, budget, s.hkv, s.max_pages,      \
+                     n_splits, qscale, part_acc, part_ml, sa)
+#define PS_SELECT_DECODE_C(DD)                    \
+  do {                                            \
+    if (per_lane <= 16) PS_SELECT_DECODE(DD, 16); \
+    else PS_SELECT_DECODE(DD, 32);                \
+  } while (0)
+  PS_WITH_GROUP(s.group, {
+    if (s.head_dim == 64)
+      PS_SELECT_DECODE_C(64);
+    else
+      PS_SELECT_DECODE_C(128);
+  });
+#undef PS_SELECT_DECODE_C
+#undef PS_SELECT_DECODE
   return hipGetLastError();
 }
 

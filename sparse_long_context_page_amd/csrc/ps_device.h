@@ -109,6 +109,59 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Whole-wavefront reductions and scans on DPP lane moves (a few cycles each,
+// against an LDS round trip per step for __shfl). Results are uniform.
+enum : int {
+  kDppRowShr1 = 0x111,
+  kDppRowShr2 = 0x112,
+  kDppRowShr4 = 0x114,
+  kDppRowShr8 = 0x118,
+  kDppRowBcast15 = 0x142,  // lane 15 of each row to the next row
+  kDppRowBcast31 = 0x143,  // lane 31 to the rows above it
+};
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dppu(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dppu<kDppXor1>(v));
+  v = min(v, dppu<kDppXor2>(v));
+  v = min(v, dppu<kDppHalfMirror>(v));
+  v = min(v, dppu<kDppMirror>(v));  // every lane of a row holds the row's min
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return min(min(a, b), min(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dppu<kDppXor1>(v));
+  v = max(v, dppu<kDppXor2>(v));
+  v = max(v, dppu<kDppHalfMirror>(v));
+  v = max(v, dppu<kDppMirror>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order: shifts of 1, 2, 4
+// and 8 within each 16-lane row (lanes shifted in from outside the row add
+// 0), then each row adds the total of the rows below it.
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xF, 0xF, false);
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xA, 0xF, false);  // rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xC, 0xF, false);  // rows 2, 3
+  return v;
+}
+
 __device__ __forceinline__ float fmax_(float a, float b) { return a > b ? a : b; }
 __device__ __forceinline__ float fmin_(float a, float b) { return a < b ? a : b; }
 

@@ -17,16 +17,30 @@ hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int3
                                   const int32_t* seq_lens, const int32_t* page_begin,
                                   int n_pages, void* meta, hipStream_t st);
 
+// k_pool and meta_out non-null: also rebuild each request's last page's
+// metadata from k_pool into meta_out before scoring it (bf16 only).
 hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
                               const int32_t* page_table, const int32_t* seq_lens, float* scores,
-                              hipStream_t st);
+                              const void* k_pool, void* meta_out, hipStream_t st);
 
 // Largest max_pages the selection kernel holds in registers (1M tokens).
 constexpr int kSelectMaxPages = 65536;
+// Largest max_pages, and list slots per split, of the decode that makes its
+// own selection (a workgroup of 256 threads holds the scores in registers,
+// 32 per lane: 128k tokens).
+constexpr int kSelectDecodeMaxPages = 8192;
+constexpr int kMaxSplitPages = 512;
 
 hipError_t launch_select_topk(const Shape& s, const float* scores, const int32_t* seq_lens,
                               int budget, int n_sink, int n_local, int32_t* sel,
                               int32_t* sel_count, hipStream_t st);
+
+hipError_t launch_select_decode(const Shape& s, const float* q, const void* k_pool,
+                                const void* v_pool, const int32_t* page_table,
+                                const int32_t* seq_lens, const float* scores, int budget,
+                                int n_sink, int n_local, float scale, int n_splits, int32_t* sel,
+                                int32_t* sel_count, float* part_acc, float* part_ml,
+                                hipStream_t st);
 
 hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void* k_pool,
                          const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,

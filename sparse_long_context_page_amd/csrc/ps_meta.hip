@@ -1,13 +1,10 @@
 // Page metadata: elementwise max and min of the valid keys of each page.
 // ("Don't read the haystack", section "Part two: the skipping".)
 //
-// One wavefront per (request, logical page, KV head). The page's 16 key rows
-// are read with coalesced 16-byte loads (lane = (row group, column vector)),
-// max/min are folded over the lane's rows and then across row groups with
-// cross-lane shuffles, and two lane groups write the kmax and kmin rows.
-// Min/max select stored values, so the result is exact in either dtype.
-#include "ps_device.h"
+// One wavefront per (request, logical page, KV head) folds the page
+// (PageFold), and two lane groups write the kmax and kmin rows.
 #include "ps_launch.h"
+#include "ps_meta.h"
 
 namespace ps {
 
@@ -39,35 +36,10 @@ __global__ __launch_bounds__(kMetaWaves * kWave) void build_page_meta_kernel(
   const int cnt = min(kPage, len - (int)p * kPage);
   const int r0 = lane / L::kLanesPerRow;
   const int c = lane % L::kLanesPerRow;
-  const T* src = k_pool + (((int64_t)phys * hkv + g) * kPage) * D + c * V;
-
+  PageFold<T, D> pf;
+  pf.load(k_pool + ((int64_t)phys * hkv + g) * kPage * D, lane);
   float mx[V], mn[V];
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    mx[j] = -INFINITY;
-    mn[j] = INFINITY;
-  }
-#pragma unroll
-  for (int i = 0; i < L::kLoadsPerPage; ++i) {
-    const int t = r0 + i * L::kRowsPerLoad;
-    if (t < cnt) {
-      float f[V];
-      unpack(ld16(src + (int64_t)t * D), f);
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        mx[j] = fmax_(mx[j], f[j]);
-        mn[j] = fmin_(mn[j], f[j]);
-      }
-    }
-  }
-#pragma unroll
-  for (int off = L::kLanesPerRow; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int j = 0; j < V; ++j) {
-      mx[j] = fmax_(mx[j], __shfl_xor(mx[j], off));
-      mn[j] = fmin_(mn[j], __shfl_xor(mn[j], off));
-    }
-  }
+  pf.fold(cnt, lane, mx, mn);
   if (r0 < 2) {
     T* dst = meta + ((int64_t)phys * hkv + g) * 2 * D + r0 * D + c * V;
     st16(dst, r0 == 0 ? pack(mx) : pack(mn));

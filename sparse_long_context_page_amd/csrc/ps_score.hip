@@ -19,6 +19,7 @@
 
 #include "ps_device.h"
 #include "ps_launch.h"
+#include "ps_meta.h"
 
 namespace ps {
 
@@ -148,14 +149,20 @@ __device__ __forceinline__ f32x4_t tree_sum(const f32x4_t (&a)[N]) {
 constexpr int kMfmaWaves = 4;
 constexpr int kMaxTiles = 16;  // 16-page tiles one wavefront streams at most
 
-template <int D, int G>
+// REFRESH: the wavefront holding a request's last page first rebuilds that
+// page's metadata from its keys (the page a decode step appends to), writes
+// it to meta_out and scores the page with it.
+template <int D, int G, bool REFRESH>
 __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel(
     const float* __restrict__ q, const bf16_t* __restrict__ meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
     int max_pages, int last_phys, int chunks_per_unit, int tiles_per_wave,
-    float* __restrict__ scores) {
+    float* __restrict__ scores, const bf16_t* __restrict__ k_pool, bf16_t* meta_out) {
   constexpr int KB = D / 32;  // 32-coordinate blocks
   static_assert(G <= 8, "group size");
+  // the refreshed last page: kmax, kmin (one wavefront of a workgroup at most
+  // holds a request's last page)
+  __shared__ __align__(16) uint16_t tail_lds[2][REFRESH ? D : 8];
 
   const int unit = blockIdx.x / chunks_per_unit;  // b * hkv + g
   const int chunk = blockIdx.x % chunks_per_unit;
@@ -207,6 +214,20 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
       bn[kb] = ld16(src + D + kb * 32);
     }
   };
+  // The last page's keys, when this wavefront holds it (other wavefronts
+  // read page 0 instead, so that no load is conditional).
+  const int tail = np - 1;
+  const bool has_tail = REFRESH && n_tiles > 0 && tail < p0 + n_tiles * 16;
+  const int col_tail = tail % 16;
+  PageFold<bf16_t, D> tail_keys;
+  int phys_tail = 0;
+  if constexpr (REFRESH) {
+    int pt = phys[0];
+#pragma unroll
+    for (int t = 1; t < kMaxTiles; ++t) pt = t == (tail - p0) / 16 ? phys[t] : pt;
+    phys_tail = has_tail ? __builtin_amdgcn_readlane(pt, col_tail) : 0;
+    tail_keys.load(k_pool + ((int64_t)phys_tail * hkv + g) * kPage * D, lane);
+  }
   // Two tiles of metadata in flight, requested whatever the run's length.
   uint4 xa[KB], na[KB], xb[KB], nb[KB];
   load(0, xa, na);
@@ -241,10 +262,41 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
     }
   }
 
+  // The last page's metadata: folded from its keys, written out, and kept in
+  // LDS for the last tile.
+  if (has_tail) {
+    using LP = RowLayout<bf16_t, D>;
+    float mx[8], mn[8];
+    tail_keys.fold(len - tail * kPage, lane, mx, mn);
+    const int r0 = lane / LP::kLanesPerRow;
+    const int c = lane % LP::kLanesPerRow;
+    if (r0 < 2) {
+      const uint4 v = r0 == 0 ? pack(mx) : pack(mn);
+      st16(meta_out + ((int64_t)phys_tail * hkv + g) * 2 * D + r0 * D + c * 8, v);
+      *reinterpret_cast<uint4*>(&tail_lds[r0][c * 8]) = v;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+
   // 3. per tile: one accumulator per (sign, 32-coordinate block), lo then mid
   // then hi, summed in a fixed tree; max over the group's heads
   float* out = scores + (int64_t)unit * max_pages;
-  auto score_tile = [&](int t, const uint4 (&bx)[KB], const uint4 (&bn)[KB]) {
+  auto score_tile = [&](int t, const uint4 (&bx_in)[KB], const uint4 (&bn_in)[KB], bool last) {
+    uint4 bx[KB], bn[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      bx[kb] = bx_in[kb];
+      bn[kb] = bn_in[kb];
+    }
+    if (REFRESH && last && has_tail && col == col_tail) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        bx[kb] = *reinterpret_cast<const uint4*>(&tail_lds[0][kb * 32 + kgrp * 8]);
+        bn[kb] = *reinterpret_cast<const uint4*>(&tail_lds[1][kb * 32 + kgrp * 8]);
+      }
+    }
     f32x4_t acc[2 * KB];
 #pragma unroll
     for (int i = 0; i < 2 * KB; ++i) acc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -266,31 +318,34 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   };
   // Steady state: every iteration scores two tiles and requests the next two,
   // so the number of loads in flight is the same on every path.
+  // The main loop never scores the run's last tile (the one that can hold
+  // the request's last page).
   int t = 0;
   for (; t + 3 < n_tiles; t += 2) {
-    score_tile(t, xa, na);
+    score_tile(t, xa, na, false);
     load(t + 2, xa, na);
-    score_tile(t + 1, xb, nb);
+    score_tile(t + 1, xb, nb, false);
     load(t + 3, xb, nb);
   }
   if (t + 2 < n_tiles) {  // three tiles left
-    score_tile(t, xa, na);
+    score_tile(t, xa, na, false);
     load(t + 2, xa, na);
-    score_tile(t + 1, xb, nb);
-    score_tile(t + 2, xa, na);
+    score_tile(t + 1, xb, nb, false);
+    score_tile(t + 2, xa, na, true);
   } else {
-    if (t < n_tiles) score_tile(t, xa, na);
-    if (t + 1 < n_tiles) score_tile(t + 1, xb, nb);
+    if (t < n_tiles) score_tile(t, xa, na, t + 1 == n_tiles);
+    if (t + 1 < n_tiles) score_tile(t + 1, xb, nb, true);
   }
 }
 
 hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
                               const int32_t* page_table, const int32_t* seq_lens, float* scores,
-                              hipStream_t st) {
+                              const void* k_pool, void* meta_out, hipStream_t st) {
   const dim3 block(kScoreWaves * kWave);
   if (s.kv_bf16) {
-    // Tiles per wavefront: enough wavefronts for about two per SIMD (1024
-    // SIMDs), each streaming as many 16-page tiles as that leaves.
+    // Tiles per wavefront: about two wavefronts per SIMD (1024 SIMDs), each
+    // streaming the tiles that leaves (runs of 4 to 8 16-page tiles measured
+    // best at 32 x 4096 pages, 2 and 16 worse).
     const int tiles_per_unit = (s.max_pages + 15) / 16;
     const int64_t tiles = (int64_t)tiles_per_unit * s.batch * s.hkv;
     const int tpw = (int)std::min<int64_t>(kMaxTiles, std::max<int64_t>(1, tiles / 2048));
@@ -300,19 +355,25 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
     const int last_phys = (int)std::min<int64_t>(s.num_phys_pages - 1, 0x7fffffff);
+    const bf16_t* kp = static_cast<const bf16_t*>(k_pool);
+    bf16_t* mo = static_cast<bf16_t*>(meta_out);
+#define PS_SCORE_MFMA(DD, RR)                                                                 \
+  hipLaunchKernelGGL((score_pages_mfma_kernel<DD, kG, RR>), grid, block, 0, st, q,            \
+                     static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,          \
+                     s.max_pages, last_phys, chunks, tpw, scores, kp, mo)
     PS_WITH_GROUP(s.group, {
       if (s.head_dim == 64) {
-        hipLaunchKernelGGL((score_pages_mfma_kernel<64, kG>), grid, block, 0, st, q,
-                           static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,
-                           s.max_pages, last_phys, chunks, tpw, scores);
+        if (kp) PS_SCORE_MFMA(64, true);
+        else PS_SCORE_MFMA(64, false);
       } else {
-        hipLaunchKernelGGL((score_pages_mfma_kernel<128, kG>), grid, block, 0, st, q,
-                           static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,
-                           s.max_pages, last_phys, chunks, tpw, scores);
+        if (kp) PS_SCORE_MFMA(128, true);
+        else PS_SCORE_MFMA(128, false);
       }
     });
+#undef PS_SCORE_MFMA
     return hipGetLastError();
   }
+  if (k_pool) return hipErrorInvalidValue;  // the refresh is bf16 only
   PS_WITH_KV(false, s.head_dim, {
     const int per_block = ScoreCfg<TElem, kD>::kPagesPerBlock;
     const int chunks = (s.max_pages + per_block - 1) / per_block;

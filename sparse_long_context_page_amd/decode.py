@@ -3,8 +3,10 @@
 DecodeStep owns the intermediate buffers of a fixed geometry (scores, page
 lists, split partials, output), so a step allocates nothing and can be
 captured into a HIP graph. The path taken is reported by name: "sparse"
-(score -> select -> sparse decode -> combine) or "dense" (full decode ->
-combine), chosen on the host from the host-known context lengths: when the
+(score -> select -> sparse decode -> combine, with select and sparse decode
+in one launch where the fused entry point supports the geometry) or "dense"
+(full decode -> combine), chosen on the host from the host-known context
+lengths: when the
 budget covers every page of every request, the dense decode is the same
 computation with less work ("Don't read the haystack", section "Part two:
 the skipping").
@@ -23,7 +25,7 @@ from .ops import Geometry
 class DecodeStep:
     def __init__(self, geom: Geometry, budget_pages: int, n_sink: int = 0, n_local: int = 0,
                  n_splits: int = 8, dense_splits: int = 32, scale: Optional[float] = None,
-                 device="cuda"):
+                 device="cuda", fused: bool = True):
         self.g = geom
         self.budget = int(budget_pages)
         self.n_sink = int(n_sink)
@@ -31,6 +33,9 @@ class DecodeStep:
         self.n_splits = int(min(n_splits, self.budget))
         self.dense_splits = int(min(dense_splits, geom.max_pages))
         self.scale = ops.default_scale(geom.head_dim) if scale is None else float(scale)
+        # selection fused into the sparse decode (one launch) when supported
+        self.fused = bool(fused) and ops.select_decode_supported(geom, self.budget,
+                                                                 self.n_splits)
         b, hq, hkv, d = geom.batch, geom.num_q_heads, geom.num_kv_heads, geom.head_dim
         f32 = dict(device=device, dtype=torch.float32)
         self.scores = torch.empty((b, hkv, geom.max_pages), **f32)
@@ -57,14 +62,33 @@ class DecodeStep:
         step appends to); tail_begin[b] = n_b - 1."""
         ops.ps_build_page_meta(self.g, k_pool, page_table, seq_lens, tail_begin, 1, meta, stream)
 
-    def sparse(self, q, k_pool, v_pool, meta, page_table, seq_lens, sink=None, stream=None):
+    def sparse(self, q, k_pool, v_pool, meta, page_table, seq_lens, sink=None, stream=None,
+               refresh_tail=False, tail_begin=None):
+        """Score, select, decode and merge. With refresh_tail the metadata of
+        each request's last page is rebuilt first: inside the score launch on
+        the fused path, else by ps_build_page_meta from tail_begin[b] = n_b - 1
+        (a device int32 tensor the caller provides)."""
         g = self.g
-        ops.ps_score_pages(g, q, meta, page_table, seq_lens, self.scores, stream)
-        ops.ps_select_topk(g, self.scores, seq_lens, self.budget, self.n_sink, self.n_local,
-                           self.sel, self.sel_count, stream)
+        if refresh_tail and self.fused:
+            ops.ps_refresh_score_pages(g, q, k_pool, meta, page_table, seq_lens, self.scores,
+                                       stream)
+        else:
+            if refresh_tail:
+                if tail_begin is None:
+                    raise ValueError("the unfused tail refresh needs tail_begin (n_b - 1)")
+                self.refresh_tail_meta(k_pool, page_table, seq_lens, tail_begin, meta, stream)
+            ops.ps_score_pages(g, q, meta, page_table, seq_lens, self.scores, stream)
         acc, ml = self.partials(self.n_splits)
-        ops.ps_sparse_decode(g, q, k_pool, v_pool, page_table, seq_lens, self.sel, self.sel_count,
-                             self.budget, self.scale, self.n_splits, acc, ml, stream)
+        if self.fused:
+            ops.ps_select_sparse_decode(g, q, k_pool, v_pool, page_table, seq_lens, self.scores,
+                                        self.budget, self.n_sink, self.n_local, self.scale,
+                                        self.n_splits, self.sel, self.sel_count, acc, ml, stream)
+        else:
+            ops.ps_select_topk(g, self.scores, seq_lens, self.budget, self.n_sink, self.n_local,
+                               self.sel, self.sel_count, stream)
+            ops.ps_sparse_decode(g, q, k_pool, v_pool, page_table, seq_lens, self.sel,
+                                 self.sel_count, self.budget, self.scale, self.n_splits, acc, ml,
+                                 stream)
         ops.ps_combine(g, acc, ml, self.n_splits, sink, self.out, self.lse, stream)
         return self.out, self.lse
 

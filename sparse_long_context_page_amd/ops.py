@@ -107,6 +107,22 @@ def ps_score_pages(g: Geometry, q, meta, page_table, seq_lens, scores, stream=No
     _lib.check("ps_score_pages", rc)
 
 
+def ps_refresh_score_pages(g: Geometry, q, k_pool, meta, page_table, seq_lens, scores,
+                           stream=None) -> None:
+    """ps_build_page_meta of each request's last page, then ps_score_pages,
+    in one launch (bf16 pools)."""
+    lib = _lib.load()
+    rc = lib.ps_refresh_score_pages(
+        g.c(), _ptr(q, "q", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
+        _ptr(k_pool, "k_pool", g.kv_dtype, _pool_shape(g)),
+        _ptr(meta, "meta", g.kv_dtype, _meta_shape(g)),
+        _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
+        _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
+        _ptr(scores, "scores", torch.float32, (g.batch, g.num_kv_heads, g.max_pages)),
+        _stream(stream))
+    _lib.check("ps_refresh_score_pages", rc)
+
+
 def ps_select_topk(g: Geometry, scores, seq_lens, budget_pages: int, n_sink_pages: int,
                    n_local_pages: int, sel, sel_count, stream=None) -> None:
     lib = _lib.load()
@@ -136,6 +152,41 @@ def ps_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens, sel, 
         _ptr(part_ml, "part_ml", torch.float32, (g.batch, g.num_q_heads, n_splits, 2)),
         _stream(stream))
     _lib.check("ps_sparse_decode", rc)
+
+
+# Limits of the fused selection + decode (the unfused entry points have none
+# of these): bf16 pools, at most 8192 pages per request and 512 list slots
+# per split.
+SELECT_DECODE_MAX_PAGES = 8192
+SELECT_DECODE_MAX_SPLIT_PAGES = 512
+
+
+def select_decode_supported(g: Geometry, budget_pages: int, n_splits: int) -> bool:
+    return (g.kv_dtype == torch.bfloat16 and g.max_pages <= SELECT_DECODE_MAX_PAGES
+            and -(-budget_pages // n_splits) <= SELECT_DECODE_MAX_SPLIT_PAGES)
+
+
+def ps_select_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens, scores,
+                            budget_pages: int, n_sink: int, n_local: int, scale: float,
+                            n_splits: int, sel, sel_count, part_acc, part_ml,
+                            stream=None) -> None:
+    """ps_select_topk and ps_sparse_decode in one launch (sel and sel_count
+    may both be None)."""
+    lib = _lib.load()
+    rc = lib.ps_select_sparse_decode(
+        g.c(), _ptr(q, "q", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
+        _ptr(k_pool, "k_pool", g.kv_dtype, _pool_shape(g)),
+        _ptr(v_pool, "v_pool", g.kv_dtype, _pool_shape(g)),
+        _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
+        _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
+        _ptr(scores, "scores", torch.float32, (g.batch, g.num_kv_heads, g.max_pages)),
+        int(budget_pages), int(n_sink), int(n_local), float(scale), int(n_splits),
+        _ptr(sel, "sel", torch.int32, (g.batch, g.num_kv_heads, budget_pages), optional=True),
+        _ptr(sel_count, "sel_count", torch.int32, (g.batch, g.num_kv_heads), optional=True),
+        _ptr(part_acc, "part_acc", torch.float32, (g.batch, g.num_q_heads, n_splits, g.head_dim)),
+        _ptr(part_ml, "part_ml", torch.float32, (g.batch, g.num_q_heads, n_splits, 2)),
+        _stream(stream))
+    _lib.check("ps_select_sparse_decode", rc)
 
 
 def ps_full_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens, scale: float,

@@ -124,6 +124,36 @@ def test_budget_and_split_validation():
     assert lib.ps_combine(g, X, X, 5000, None, X, None, None) == _lib.PS_ERR_BUDGET
 
 
+def test_refresh_score_validation():
+    lib = _lib.load()
+    g = geom()
+    assert lib.ps_refresh_score_pages(g, X, None, X, X, X, X, None) == _lib.PS_ERR_NULL
+    assert lib.ps_refresh_score_pages(g, X, X, None, X, X, X, None) == _lib.PS_ERR_NULL
+    assert lib.ps_refresh_score_pages(geom(kv_dtype=_lib.PS_F32), X, X, X, X, X, X, None) == \
+        _lib.PS_ERR_UNSUPPORTED
+    assert lib.ps_refresh_score_pages(geom(batch=0), X, X, X, X, X, X, None) == _lib.PS_OK
+
+
+def test_fused_select_decode_validation():
+    lib = _lib.load()
+    g = geom()
+
+    def call(g=g, sel=X, cnt=X, budget=8, ns=1, nl=2, splits=2, scores=X):
+        return lib.ps_select_sparse_decode(g, X, X, X, X, X, scores, budget, ns, nl, 0.1, splits,
+                                           sel, cnt, X, X, None)
+    assert call(scores=None) == _lib.PS_ERR_NULL
+    assert call(sel=None) == _lib.PS_ERR_NULL           # one of the pair
+    assert call(cnt=None) == _lib.PS_ERR_NULL
+    assert call(budget=0) == _lib.PS_ERR_BUDGET
+    assert call(ns=5, nl=4) == _lib.PS_ERR_BUDGET
+    assert call(splits=9) == _lib.PS_ERR_BUDGET
+    assert call(splits=0) == _lib.PS_ERR_BUDGET
+    assert call(g=geom(kv_dtype=_lib.PS_F32)) == _lib.PS_ERR_UNSUPPORTED
+    assert call(g=geom(max_pages=8193)) == _lib.PS_ERR_UNSUPPORTED
+    assert call(budget=1026, ns=0, nl=0, splits=2) == _lib.PS_ERR_UNSUPPORTED  # 513 per split
+    assert call(g=geom(batch=0), sel=None, cnt=None) == _lib.PS_OK
+
+
 def test_partials_overflow():
     lib = _lib.load()
     g = geom(batch=1 << 20, num_q_heads=8, num_kv_heads=8, max_pages=4096)

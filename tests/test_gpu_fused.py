@@ -1,0 +1,116 @@
+"""The fused selection + sparse decode (ps_select_sparse_decode) against the
+two launches it replaces (ps_select_topk then ps_sparse_decode): the page
+list, the counts, the split partials and the merged outputs are bitwise
+identical, on the small bf16 workloads (several splits, ragged tails, sink and
+local pages, budgets that cover every page of short requests) and on the
+32 x 64k workload in the benchmark's launch configuration."""
+
+import pytest
+import torch
+
+import workloads as wl
+from _gpu_helpers import geometry
+from sparse_long_context_page_amd import DecodeStep, build_meta, ops
+from test_gpu_parity import SMALL
+
+pytestmark = pytest.mark.gpu
+
+BF16 = [w for w in SMALL if w.kv_dtype == "bf16"] + [wl.HEADLINE]
+
+
+def _both(inp, budget=None, n_sink=None, n_local=None, n_splits=None):
+    w = inp["workload"]
+    g = geometry(inp)
+    budget = w.budget_pages if budget is None else budget
+    kw = dict(n_sink=w.n_sink if n_sink is None else n_sink,
+              n_local=w.n_local if n_local is None else n_local,
+              n_splits=w.n_splits if n_splits is None else n_splits,
+              dense_splits=w.dense_splits, scale=inp["scale"])
+    meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+    res = []
+    for fused in (False, True):
+        step = DecodeStep(g, budget, fused=fused, **kw)
+        assert step.fused == fused
+        step.sel.fill_(-7)
+        step.sel_count.fill_(-7)
+        out, lse = step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
+                               inp["seq_lens"], inp["sink"])
+        acc, ml = step.partials(step.n_splits)
+        torch.cuda.synchronize()
+        res.append({k: v.clone() for k, v in dict(sel=step.sel, cnt=step.sel_count, acc=acc,
+                                                  ml=ml, out=out, lse=lse).items()})
+    return res
+
+
+@pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])
+def test_fused_equals_unfused_bitwise(w):
+    inp = wl.make_inputs(w, device="cuda")
+    configs = [dict()]
+    if w.batch * w.num_kv_heads <= 16:  # more budgets and splits on the small ones
+        configs += [dict(budget=3, n_sink=1, n_local=1, n_splits=2),
+                    dict(budget=1, n_sink=0, n_local=0, n_splits=1),
+                    dict(budget=64, n_sink=2, n_local=3, n_splits=7)]
+    for cfg in configs:
+        a, b = _both(inp, **cfg)
+        for k in a:
+            assert torch.equal(a[k], b[k]), (w.name, cfg, k)
+
+
+def test_fused_without_page_list_output():
+    w = SMALL[2]
+    inp = wl.make_inputs(w, device="cuda")
+    g = geometry(inp)
+    a, _ = _both(inp)
+    meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+    step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
+                      inp["scale"])
+    ops.ps_score_pages(g, inp["q"], meta, inp["page_table"], inp["seq_lens"], step.scores)
+    acc, ml = step.partials(step.n_splits)
+    ops.ps_select_sparse_decode(g, inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                                inp["seq_lens"], step.scores, w.budget_pages, w.n_sink,
+                                w.n_local, inp["scale"], step.n_splits, None, None, acc, ml)
+    torch.cuda.synchronize()
+    assert torch.equal(acc, a["acc"]) and torch.equal(ml, a["ml"])
+
+
+@pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])
+def test_refresh_score_equals_meta_then_score_bitwise(w):
+    """ps_refresh_score_pages on metadata whose last pages are stale equals
+    the full metadata build followed by ps_score_pages, bit for bit (the
+    refreshed last pages included)."""
+    inp = wl.make_inputs(w, device="cuda")
+    g = geometry(inp)
+    full = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+    want = torch.empty((g.batch, g.num_kv_heads, g.max_pages), device="cuda")
+    ops.ps_score_pages(g, inp["q"], full, inp["page_table"], inp["seq_lens"], want)
+    stale = full.clone()
+    tails = [int(inp["page_table"][b, int(n) - 1]) for b, n in enumerate(inp["n_pages_host"])]
+    stale[tails] = 3.0  # what the pages held before the last token was appended
+    got = torch.full_like(want, float("nan"))
+    ops.ps_refresh_score_pages(g, inp["q"], inp["k_pool"], stale, inp["page_table"],
+                               inp["seq_lens"], got)
+    torch.cuda.synchronize()
+    assert torch.equal(stale, full)
+    for b, n in enumerate(inp["n_pages_host"]):
+        assert torch.equal(got[b, :, :int(n)], want[b, :, :int(n)]), (w.name, b)
+
+
+def test_step_with_tail_refresh_fused_equals_unfused():
+    w = SMALL[4]  # sink page, local pages, permuted pool, lengths from 1 token
+    inp = wl.make_inputs(w, device="cuda")
+    g = geometry(inp)
+    tail = torch.tensor([int(n) - 1 for n in inp["n_pages_host"]], device="cuda",
+                        dtype=torch.int32)
+    outs = []
+    for fused in (False, True):
+        meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+        meta[[int(inp["page_table"][b, int(n) - 1]) for b, n in
+              enumerate(inp["n_pages_host"])]] = -2.0
+        step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
+                          inp["scale"], fused=fused)
+        out, lse = step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
+                               inp["seq_lens"], inp["sink"], refresh_tail=True, tail_begin=tail)
+        torch.cuda.synchronize()
+        outs.append((meta.clone(), step.sel.clone(), out.clone(), lse.clone()))
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
