@@ -4,12 +4,15 @@
 
 One step = one decode step of the whole hot path over one batch: refresh of
 each request's tail-page metadata, page scores, selection, sparse split-KV
-decode and merge, captured as one HIP graph. R independent input batches are
-drawn and the timed steps cycle through them, so each step reads data that
-the previous steps evicted from the 256 MB memory-side cache (the working set
-of one step is about 204 MB at the b32/64k workload). Before timing, one
-step is checked against the fp64 oracle on sampled (request, KV head) units;
-no timing is printed if that check fails.
+decode and merge (three launches: refresh+score, select+decode, merge). R
+independent input batches are drawn and the timed steps cycle through them,
+so each step reads data that the previous steps evicted from the 256 MB
+memory-side cache (the working set of one step is about 204 MB at the
+b32/64k workload). The timed steps are replays of one HIP graph holding one
+step per input set; one-graph-per-step and eager (uncaptured) step times are
+reported beside it. Before timing, one step is checked against the fp64
+oracle on sampled (request, KV head) units; no timing is printed if that
+check fails.
 
 Printed: one JSON line with the step time (us per decode step), effective
 HBM bandwidth on algorithmic bytes, the score kernel's roofline (the kernel
@@ -214,7 +217,7 @@ def cpu_baseline(s, w, units, wl):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("ps_score.hip", "ps_device.h"):
+    for f in ("ps_score.hip", "ps_device.h", "ps_meta.h"):
         with open(os.path.join(ROOT, "sparse_long_context_page_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -287,20 +290,31 @@ def main():
         return
 
     # -- graph-captured step loop (the timed region) -----------------------
+    # One graph holds one decode step per input set, in order (R steps), as a
+    # step sits inside a captured model forward; K steps are K // R replays
+    # of it plus K % R one-step graphs. Every step is the whole hot path.
     graphs = [capture(run_sparse_step, s, torch) for s in sets]
     graphs[0].replay()
     torch.cuda.synchronize()
     if not torch.equal(s0["step"].out, out_eager):
         raise SystemExit("graph replay differs from the eager step")
+
+    def all_sets(_):
+        for s in sets:
+            run_sparse_step(s)
+    multi = capture(all_sets, None, torch)
     for i in range(args.warmup):
         graphs[i % len(graphs)].replay()
+    multi.replay()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for i in range(args.steps):
-        graphs[i % len(graphs)].replay()
+    for _ in range(args.steps // len(sets)):
+        multi.replay()
+    for i in range(args.steps % len(sets)):
+        graphs[i].replay()
     e1.record()
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
@@ -308,6 +322,14 @@ def main():
     ms_per_step = gpu_ms / args.steps
     print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr,
           flush=True)
+
+    # -- the same steps, one graph per step ---------------------------------
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    one_graph_us = e0.elapsed_time(e1) / args.steps * 1e3
 
     # -- the same steps launched eagerly (no graph), back to back -------------
     for i in range(args.warmup):
@@ -322,38 +344,82 @@ def main():
     torch.cuda.synchronize()
     eager_us = g0.elapsed_time(g1) / args.steps * 1e3
 
-    # -- per-kernel times: HIP events around each launch, same order -------
-    stages = ["tail_meta", "score", "select", "sparse_decode", "combine"]
-    per = {k: [] for k in stages}
-    n_k = max(args.steps // 2, 20)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
-           for _ in range(n_k)]
-    for i in range(n_k):
-        s = sets[i % len(sets)]
-        inp, step, ev = s["inp"], s["step"], evs[i]
-        g = s["g"]
+    # -- per-kernel times: each launch of the step repeated back to back over
+    # the input sets, captured as one graph of n_k launches (so host launch
+    # cost cannot starve the small kernels) and replayed between two HIP
+    # events on torch's current stream ---------------------------------------
+    n_k, n_rep = 40, max(args.steps // 40, 3)
+
+    def time_launches(fn):
+        def batch(_):
+            for i in range(n_k):
+                fn(sets[i % len(sets)])
+        gk = capture(batch, None, torch)
+        gk.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(n_rep):
+            gk.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (n_rep * n_k) * 1e3
+
+    def k_refresh_score(s):
+        inp, step = s["inp"], s["step"]
+        ps.ps_refresh_score_pages(s["g"], inp["q"], inp["k_pool"], s["meta"], inp["page_table"],
+                                  inp["seq_lens"], step.scores)
+
+    def k_select_decode(s):
+        inp, step = s["inp"], s["step"]
         acc_t, ml_t = step.partials(step.n_splits)
-        ev[0].record()
+        ps.ps_select_sparse_decode(s["g"], inp["q"], inp["k_pool"], inp["v_pool"],
+                                   inp["page_table"], inp["seq_lens"], step.scores, step.budget,
+                                   step.n_sink, step.n_local, step.scale, step.n_splits,
+                                   step.sel, step.sel_count, acc_t, ml_t)
+
+    def k_combine(s):
+        inp, step = s["inp"], s["step"]
+        acc_t, ml_t = step.partials(step.n_splits)
+        ps.ps_combine(s["g"], acc_t, ml_t, step.n_splits, inp["sink"], step.out, step.lse)
+
+    def k_tail_meta(s):
+        inp, step = s["inp"], s["step"]
         step.refresh_tail_meta(inp["k_pool"], inp["page_table"], inp["seq_lens"], s["tail"],
                                s["meta"])
-        ev[1].record()
-        ps.ps_score_pages(g, inp["q"], s["meta"], inp["page_table"], inp["seq_lens"],
+
+    def k_score(s):
+        inp, step = s["inp"], s["step"]
+        ps.ps_score_pages(s["g"], inp["q"], s["meta"], inp["page_table"], inp["seq_lens"],
                           step.scores)
-        ev[2].record()
-        ps.ps_select_topk(g, step.scores, inp["seq_lens"], step.budget, step.n_sink,
+
+    def k_select(s):
+        inp, step = s["inp"], s["step"]
+        ps.ps_select_topk(s["g"], step.scores, inp["seq_lens"], step.budget, step.n_sink,
                           step.n_local, step.sel, step.sel_count)
-        ev[3].record()
-        ps.ps_sparse_decode(g, inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
+
+    def k_sparse_decode(s):
+        inp, step = s["inp"], s["step"]
+        acc_t, ml_t = step.partials(step.n_splits)
+        ps.ps_sparse_decode(s["g"], inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
                             inp["seq_lens"], step.sel, step.sel_count, step.budget, step.scale,
                             step.n_splits, acc_t, ml_t)
-        ev[4].record()
-        ps.ps_combine(g, acc_t, ml_t, step.n_splits, inp["sink"], step.out, step.lse)
-        ev[5].record()
+
+    fused = s0["step"].fused
+    kern_us = {}
+    if fused:  # the step's own launches
+        kern_us["refresh_score"] = time_launches(k_refresh_score)
+        kern_us["select_decode"] = time_launches(k_select_decode)
+    kern_us["combine"] = time_launches(k_combine)
+    # the unfused entry points, one stage each
+    kern_us["tail_meta"] = time_launches(k_tail_meta)
+    kern_us["score"] = time_launches(k_score)
+    kern_us["select"] = time_launches(k_select)
+    kern_us["sparse_decode"] = time_launches(k_sparse_decode)
+    for s in sets:  # leave every set as one whole step leaves it
+        run_sparse_step(s)
     torch.cuda.synchronize()
-    for i in range(n_k):
-        for j, k in enumerate(stages):
-            per[k].append(evs[i][j].elapsed_time(evs[i][j + 1]) * 1e3)
-    kern_us = {k: float(np.mean(v[2:])) for k, v in per.items()}
 
     # -- dense baseline ----------------------------------------------------
     dgraphs = [capture(run_dense_step, s, torch) for s in sets]
@@ -398,8 +464,18 @@ def main():
     dense_b = acc.dense_kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
     step_us = ms_per_step * 1e3
     eff_gbps = touched / (step_us * 1e-6) / 1e9
-    score_gbps = meta_b / (kern_us["score"] * 1e-6) / 1e9
-    decode_gbps = kv_b / (kern_us["sparse_decode"] * 1e-6) / 1e9
+    # the dominant kernel: the step's score launch (with the last-page
+    # refresh when fused): metadata of every page read, one fp32 score per
+    # page written, and per (request, KV head) the last page's 16 key rows
+    # read and its metadata written
+    units = w.batch * w.num_kv_heads
+    scores_b = sum(-(-n // w.page_size) for n in lens) * w.num_kv_heads * 4
+    tail_b = units * (w.page_size + 2) * w.head_dim * elem if fused else 0
+    dom_key = "refresh_score" if fused else "score"
+    dom_b = meta_b + scores_b + tail_b
+    score_gbps = dom_b / (kern_us[dom_key] * 1e-6) / 1e9
+    dec_key = "select_decode" if fused else "sparse_decode"
+    decode_gbps = kv_b / (kern_us[dec_key] * 1e-6) / 1e9
 
     traffic = measured_traffic(w.name)
     result = {
@@ -421,13 +497,19 @@ def main():
                    "page_size": w.page_size, "budget_pages": w.budget_pages,
                    "n_sink_pages": w.n_sink, "n_local_pages": w.n_local, "needles": w.needles,
                    "kv_storage": w.kv_dtype, "n_splits": w.n_splits, "input_sets": len(sets),
-                   "path": path, "graph_captured": True},
+                   "path": path,
+                   "graph_captured": f"{len(sets)} steps (one per input set) per graph"},
         "effective_hbm_gbps": round(eff_gbps, 1),
         "hbm_frac_of_peak": round(eff_gbps / PEAK_HBM_GBPS, 4),
         "touched_bytes": touched,
         "touched_bytes_split": {"metadata": meta_b, "selected_kv": kv_b},
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
+        "step_launches": (["ps_refresh_score_pages", "ps_select_sparse_decode", "ps_combine"]
+                          if fused else ["ps_build_page_meta", "ps_score_pages",
+                                         "ps_select_topk", "ps_sparse_decode", "ps_combine"]),
         "selection_overhead_us": round(kern_us["select"], 3),
+        "selection_in_decode_us": (round(kern_us["select_decode"] - kern_us["sparse_decode"], 3)
+                                   if fused else None),
         "score_plus_select_us": round(kern_us["score"] + kern_us["select"], 3),
         "sparse_decode_gbps": round(decode_gbps, 1),
         "dense_us_per_step": round(dense_us, 3),
@@ -437,13 +519,15 @@ def main():
         "copy_gbps_read_plus_write": round(copy_gbps, 1),
         "timed_wall_ms": round(wall_ms, 3),
         "eager_us_per_step": round(eager_us, 3),
+        "one_step_per_graph_us_per_step": round(one_graph_us, 3),
         "parity": parity,
-        "roofline": {"kernel": "ps_score_pages", "bound": "hbm",
+        "roofline": {"kernel": "ps_refresh_score_pages" if fused else "ps_score_pages",
+                     "bound": "hbm",
                      "achieved": round(score_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
-                     "algorithmic_bytes_per_launch": meta_b,
-                     "avg_launch_us": round(kern_us["score"], 3)},
+                     "algorithmic_bytes_per_launch": dom_b,
+                     "avg_launch_us": round(kern_us[dom_key], 3)},
     }
     if not args.no_cpu_baseline:
         print("# cpu baseline", file=sys.stderr, flush=True)
@@ -457,8 +541,12 @@ def profile_only(args, sets, torch, ps):
         s = sets[i % len(sets)]
         inp, step, g = s["inp"], s["step"], s["g"]
         if args.only_kernel == "score":
-            ps.ps_score_pages(g, inp["q"], s["meta"], inp["page_table"], inp["seq_lens"],
-                              step.scores)
+            if step.fused:
+                ps.ps_refresh_score_pages(g, inp["q"], inp["k_pool"], s["meta"],
+                                          inp["page_table"], inp["seq_lens"], step.scores)
+            else:
+                ps.ps_score_pages(g, inp["q"], s["meta"], inp["page_table"], inp["seq_lens"],
+                                  step.scores)
         elif args.only_kernel == "step":
             run_sparse_step(s)
         elif args.only_kernel == "copy":
