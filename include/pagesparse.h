@@ -124,7 +124,9 @@ int ps_build_page_meta(const ps_geom* geom, const void* k_pool, const int32_t* p
  * with (kmax, kmin) = meta[page_table[b,p], g]. Unscaled; the max over the
  * group makes one page list per KV head admissible for all its heads.
  * Computed in fp32 as sum_d (max(q,0)*kmax_d + min(q,0)*kmin_d) with exact
- * products and a fixed summation order; entries at p >= n_b are not written.
+ * products and a fixed summation order (bf16 metadata: on the matrix cores,
+ * q split exactly into three bf16 terms; fp32 metadata: fma), so results are
+ * bitwise reproducible; entries at p >= n_b are not written.
  * Device preconditions: as ps_build_page_meta, with meta built for every
  * page read. */
 int ps_score_pages(const ps_geom* geom, const float* q, const void* meta,
