@@ -149,6 +149,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(a, b), max(c, d));
 }
 
+// Sum over the 64 lanes (uniform result).
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  v += (int)dppu<kDppXor1>((uint32_t)v);
+  v += (int)dppu<kDppXor2>((uint32_t)v);
+  v += (int)dppu<kDppHalfMirror>((uint32_t)v);
+  v += (int)dppu<kDppMirror>((uint32_t)v);  // every lane of a row holds the row's sum
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
 // Inclusive prefix sum over the 64 lanes in lane order: shifts of 1, 2, 4
 // and 8 within each 16-lane row (lanes shifted in from outside the row add
 // 0), then each row adds the total of the rows below it.

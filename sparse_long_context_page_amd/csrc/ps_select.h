@@ -25,12 +25,15 @@ namespace ps {
 
 constexpr int kSelDigitBits = 8;
 constexpr int kSelBins = 1 << kSelDigitBits;
+constexpr int kSelRankMax = kWave;  // threshold bins up to this size are ranked directly
 
 template <int WAVES>
 struct SelectLds {
   int hist[3][kSelBins];
   uint32_t wave_min[WAVES], wave_max[WAVES];
-  int wave_cnt[2][WAVES];
+  int wave_cnt[WAVES];
+  uint64_t bin_val[kSelRankMax];  // the threshold bin as (key, ~page) values
+  uint64_t cut;  // kept: every candidate at or above this value
 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -50,6 +53,12 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // emit(slot, page) once per kept page, slots 0..kept-1 in ascending page
 // order, and returns kept = min(budget, n). Ends with the workgroup's LDS
 // free for reuse only after a barrier of the caller.
+//
+// The kept candidates are the r best in the order (key descending, page
+// ascending). Radix passes narrow the r-th key's bits; once its bin holds at
+// most 64 keys, those are gathered and wavefront 0 ranks them directly, which
+// fixes the cut exactly as (key, page); when every bit is decided first, the
+// bin's keys are equal and the cut is the remaining-th lowest page among them.
 template <int WAVES, int C, typename Emit>
 __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n, int budget,
                                            int n_sink, int n_local, SelectLds<WAVES>& sh,
@@ -107,7 +116,7 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
   int in_bin = hi - lo;
   int pass = 0;
 #pragma unroll 1
-  while (remaining > 0 && in_bin > remaining && top > 0) {
+  while (remaining > 0 && in_bin > remaining && in_bin > kSelRankMax && top > 0) {
     const int width = top < kSelDigitBits ? top : kSelDigitBits;
     const int shift = top - width;
     int* h = sh.hist[pass % 3];
@@ -148,49 +157,111 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
     ++pass;
   }
 
-  // Class of a page: 2 = kept, 1 = tie on the threshold key (the lowest
-  // `remaining` of them are kept), 0 = dropped or past the request.
-  auto page_class = [&](int j) -> int {
-    const int p = page(j);
-    if (p >= n) return 0;
-    if (!is_cand(p)) return 2;
-    if (remaining == 0) return 0;
-    const uint32_t km = key[j] & pmask;
-    return km > prefix ? 2 : (km == prefix ? 1 : 0);
+  // The cut. Default: every candidate above the bin is kept and the bin's
+  // lowest `remaining` pages (all of it when it holds exactly that many;
+  // equal keys when every bit is decided). Candidates compare as one 64-bit
+  // value, key high and complemented page low, so (key descending, page
+  // ascending) order is plain unsigned order.
+  auto order64 = [](uint32_t k, int p) {
+    return ((uint64_t)k << 32) | (uint64_t)(0xffffffffu - (uint32_t)p);
   };
+  bool ranked = false;
+  uint64_t cut = 0;
+  if (remaining > 0 && in_bin > remaining && top > 0) {
+    // 64 or fewer keys in the bin: gather them (slots from per-wavefront
+    // ballot counts); wavefront 0 ranks them in vector registers, reading
+    // the gathered values as LDS broadcasts
+    auto in_bin_key = [&](int j) { return is_cand(page(j)) && (key[j] & pmask) == prefix; };
+    int mine_cnt = 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) mine_cnt += __popcll(__ballot(in_bin_key(j)));
+    if (lane == 0) sh.wave_cnt[wave] = mine_cnt;
+    __syncthreads();
+    int slot = 0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) slot += w < wave ? sh.wave_cnt[w] : 0;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const bool on = in_bin_key(j);
+      const uint64_t m = __ballot(on);
+      if (on) sh.bin_val[slot + lanes_below(m)] = order64(key[j], page(j));
+      slot += __popcll(m);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint64_t v = lane < in_bin ? sh.bin_val[lane] : 0;
+      int rank = 0;  // bin values above this one
+#pragma unroll
+      for (int j0 = 0; j0 < kSelRankMax; j0 += 8) {
+        if (j0 >= in_bin) break;  // uniform
+        uint64_t w[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = sh.bin_val[j0 + i];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rank += (j0 + i < in_bin && w[i] > v) ? 1 : 0;
+      }
+      if (lane < in_bin && rank == remaining - 1) sh.cut = v;
+    }
+    __syncthreads();
+    ranked = true;
+    cut = sh.cut;
+  }
+
+  // Class of each page, 2 bits per page: 2 = kept, 1 = tie in the bin (the
+  // lowest `remaining` of them are kept), 0 = dropped or past the request.
+  uint32_t cls[(C + 15) / 16];
+#pragma unroll
+  for (int i = 0; i < (C + 15) / 16; ++i) cls[i] = 0;
   int cnt_keep = 0, cnt_tie = 0;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
-    const int c = page_class(j);
-    cnt_keep += __popcll(__ballot(c == 2));
-    cnt_tie += __popcll(__ballot(c == 1));
+    const int p = page(j);
+    const uint32_t k = key[j];
+    const uint32_t km = k & pmask;
+    const bool above = ranked ? order64(k, p) >= cut : km > prefix;
+    const bool tie = !ranked && km == prefix;
+    const int cc = above ? 2 : (tie ? 1 : 0);
+    const int c = p >= n ? 0 : (!is_cand(p) ? 2 : (remaining == 0 ? 0 : cc));
+    cls[j / 16] |= (uint32_t)c << (2 * (j % 16));
+    cnt_keep += c == 2 ? 1 : 0;
+    cnt_tie += c == 1 ? 1 : 0;
   }
-  if (lane == 0) {
-    sh.wave_cnt[0][wave] = cnt_keep;
-    sh.wave_cnt[1][wave] = cnt_tie;
-  }
+  const int wave_counts = wave_sum_i32((cnt_keep << 16) | cnt_tie);
+  if (lane == 0) sh.wave_cnt[wave] = wave_counts;
   __syncthreads();
   int keep_before = 0, tie_before = 0, keep_all = 0, tie_all = 0;
 #pragma unroll
   for (int w = 0; w < WAVES; ++w) {
-    keep_before += w < wave ? sh.wave_cnt[0][w] : 0;
-    tie_before += w < wave ? sh.wave_cnt[1][w] : 0;
-    keep_all += sh.wave_cnt[0][w];
-    tie_all += sh.wave_cnt[1][w];
+    const int kc = sh.wave_cnt[w] >> 16, tc = sh.wave_cnt[w] & 0xffff;
+    keep_before += w < wave ? kc : 0;
+    tie_before += w < wave ? tc : 0;
+    keep_all += kc;
+    tie_all += tc;
   }
   const int kept_total = keep_all + min(tie_all, remaining);
   int slot = keep_before + min(tie_before, remaining);
-  int tie_rank = tie_before;
+  if (tie_all <= remaining) {  // every tie is kept (the usual case)
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    const int c = page_class(j);
-    const uint64_t tm = __ballot(c == 1);
-    const bool keep = c == 2 || (c == 1 && tie_rank + lanes_below(tm) < remaining);
-    const uint64_t km = __ballot(keep);
-    const int o = slot + lanes_below(km);
-    if (keep && o < budget) emit(o, page(j));
-    slot += __popcll(km);
-    tie_rank += __popcll(tm);
+    for (int j = 0; j < C; ++j) {
+      const bool keep = ((cls[j / 16] >> (2 * (j % 16))) & 3) != 0;
+      const uint64_t km = __ballot(keep);
+      const int o = slot + lanes_below(km);
+      if (keep && o < budget) emit(o, page(j));
+      slot += __popcll(km);
+    }
+  } else {  // equal keys: the lowest `remaining` tied pages are kept
+    int tie_rank = tie_before;
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const int c = (cls[j / 16] >> (2 * (j % 16))) & 3;
+      const uint64_t tm = __ballot(c == 1);
+      const bool keep = c == 2 || (c == 1 && tie_rank + lanes_below(tm) < remaining);
+      const uint64_t km = __ballot(keep);
+      const int o = slot + lanes_below(km);
+      if (keep && o < budget) emit(o, page(j));
+      slot += __popcll(km);
+      tie_rank += __popcll(tm);
+    }
   }
   return kept_total < budget ? kept_total : budget;
 }
