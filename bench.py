@@ -374,10 +374,17 @@ def main():
     def k_select_decode(s):
         inp, step = s["inp"], s["step"]
         acc_t, ml_t = step.partials(step.n_splits)
-        ps.ps_select_sparse_decode(s["g"], inp["q"], inp["k_pool"], inp["v_pool"],
-                                   inp["page_table"], inp["seq_lens"], step.scores, step.budget,
-                                   step.n_sink, step.n_local, step.scale, step.n_splits,
-                                   step.sel, step.sel_count, acc_t, ml_t)
+        if step.n_splits == 1:  # the merge is in the same launch
+            ps.ps_select_sparse_decode(s["g"], inp["q"], inp["k_pool"], inp["v_pool"],
+                                       inp["page_table"], inp["seq_lens"], step.scores,
+                                       step.budget, step.n_sink, step.n_local, step.scale, 1,
+                                       step.sel, step.sel_count, None, None, inp["sink"],
+                                       step.out, step.lse)
+        else:
+            ps.ps_select_sparse_decode(s["g"], inp["q"], inp["k_pool"], inp["v_pool"],
+                                       inp["page_table"], inp["seq_lens"], step.scores,
+                                       step.budget, step.n_sink, step.n_local, step.scale,
+                                       step.n_splits, step.sel, step.sel_count, acc_t, ml_t)
 
     def k_combine(s):
         inp, step = s["inp"], s["step"]
@@ -504,7 +511,8 @@ def main():
         "touched_bytes": touched,
         "touched_bytes_split": {"metadata": meta_b, "selected_kv": kv_b},
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "step_launches": (["ps_refresh_score_pages", "ps_select_sparse_decode", "ps_combine"]
+        "step_launches": ((["ps_refresh_score_pages", "ps_select_sparse_decode"] +
+                           ([] if s0["step"].n_splits == 1 else ["ps_combine"]))
                           if fused else ["ps_build_page_meta", "ps_score_pages",
                                          "ps_select_topk", "ps_sparse_decode", "ps_combine"]),
         "selection_overhead_us": round(kern_us["select"], 3),

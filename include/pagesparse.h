@@ -195,17 +195,24 @@ int ps_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool, co
  * Every split's workgroup selects the (b, g) page list from scores itself
  * and attends the list slots of its split, so no page list is read back.
  * sel and sel_count, when not NULL, receive what ps_select_topk writes.
+ * With out != NULL (one split only) the single partial is merged in the same
+ * launch: out and lse (when not NULL) receive what ps_combine writes for
+ * n_splits = 1 with the given sink (NULL = none), bitwise; part_acc and
+ * part_ml are then not used (may be NULL). Otherwise the partials are
+ * written as by ps_sparse_decode and sink and lse must be NULL.
  * Host checks: those of ps_select_topk and ps_sparse_decode (same codes);
- * sel and sel_count both NULL or both set (else PS_ERR_NULL); bf16 K/V,
- * max_pages <= 8192 and ceil(budget_pages / n_splits) <= 512 (else
- * PS_ERR_UNSUPPORTED).
+ * sel and sel_count both NULL or both set, and the partials set when out is
+ * NULL (else PS_ERR_NULL); out != NULL with n_splits != 1, or sink or lse
+ * set without out (PS_ERR_BUDGET); bf16 K/V, max_pages <= 8192 and
+ * ceil(budget_pages / n_splits) <= 512 (else PS_ERR_UNSUPPORTED).
  * Device precondition: scores are finite (no NaN). */
 int ps_select_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool,
                             const void* v_pool, const int32_t* page_table,
                             const int32_t* seq_lens, const float* scores, int32_t budget_pages,
                             int32_t n_sink_pages, int32_t n_local_pages, float scale,
                             int32_t n_splits, int32_t* sel, int32_t* sel_count, float* part_acc,
-                            float* part_ml, void* stream);
+                            float* part_ml, const float* sink, float* out, float* lse,
+                            void* stream);
 
 /* 4b. Dense split-KV decode: ps_sparse_decode over every page. Split s of a
  * request covers logical pages [s*c_b, min((s+1)*c_b, n_b)) with

@@ -160,16 +160,18 @@ PS_API int ps_select_sparse_decode(const ps_geom* geom, const float* q, const vo
                                    int32_t budget_pages, int32_t n_sink_pages,
                                    int32_t n_local_pages, float scale, int32_t n_splits,
                                    int32_t* sel, int32_t* sel_count, float* part_acc,
-                                   float* part_ml, void* stream) {
+                                   float* part_ml, const float* sink, float* out, float* lse,
+                                   void* stream) {
   ps::Shape s;
   int rc = check_geom(geom, &s);
   if (rc) return rc;
-  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !scores || !part_acc || !part_ml)
-    return PS_ERR_NULL;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !scores) return PS_ERR_NULL;
   if ((sel == nullptr) != (sel_count == nullptr)) return PS_ERR_NULL;
+  if (!out && (!part_acc || !part_ml)) return PS_ERR_NULL;
   if (budget_pages < 1 || n_sink_pages < 0 || n_local_pages < 0) return PS_ERR_BUDGET;
   if ((int64_t)n_sink_pages + n_local_pages > budget_pages) return PS_ERR_BUDGET;
   if (n_splits < 1 || n_splits > budget_pages || n_splits > kMaxSplits) return PS_ERR_BUDGET;
+  if (out ? n_splits != 1 : (sink || lse)) return PS_ERR_BUDGET;
   if (!s.kv_bf16 || s.max_pages > ps::kSelectDecodeMaxPages ||
       (budget_pages + n_splits - 1) / n_splits > ps::kMaxSplitPages)
     return PS_ERR_UNSUPPORTED;
@@ -180,8 +182,8 @@ PS_API int ps_select_sparse_decode(const ps_geom* geom, const float* q, const vo
   if (s.batch == 0) return PS_OK;
   return hip_status(ps::launch_select_decode(s, q, k_pool, v_pool, page_table, seq_lens, scores,
                                              budget_pages, n_sink_pages, n_local_pages, scale,
-                                             n_splits, sel, sel_count, part_acc, part_ml,
-                                             (hipStream_t)stream));
+                                             n_splits, sel, sel_count, part_acc, part_ml, sink,
+                                             out, lse, (hipStream_t)stream));
 }
 
 PS_API int ps_full_decode(const ps_geom* geom, const float* q, const void* k_pool,
@@ -229,4 +231,4 @@ PS_API const char* ps_strerror(int status) {
   }
 }
 
-PS_API int ps_abi_version(void) { return (1 << 16) | 1; }  // 1.1: fused select + decode
+PS_API int ps_abi_version(void) { return (1 << 16) | 2; }  // 1.2: fused entry points

@@ -288,7 +288,6 @@ struct PageRef {
   int phys;
 };
 
-constexpr int kIdBlock = 4;  // page ids a wavefront resolves at a time
 
 // Where a workgroup's pages come from: every page of the request (dense), a
 // page list (sparse), or a selection the workgroup makes itself from the page
@@ -296,16 +295,25 @@ constexpr int kIdBlock = 4;  // page ids a wavefront resolves at a time
 // head) runs the same selection and keeps its share of the list).
 enum DecodeMode : int { kDense = 0, kList = 1, kSelect = 2 };
 
-// Selection inputs and outputs of the kSelect mode.
+// Selection inputs and outputs of the kSelect mode, and the merged output of
+// a launch with one split.
 struct SelectArgs {
   const float* scores;  // [B, Hkv, max_pages]
   int n_sink, n_local;
   int32_t* sel;        // [B, Hkv, budget] or null
   int32_t* sel_count;  // [B, Hkv] or null
+  const float* sink;   // [Hq] or null; with out
+  float* out;          // [B, Hq, D] or null: one split, merged output written
+  float* lse;          // [B, Hq] or null
 };
 
-template <int D, int G, int MODE, int C>
-__global__ __launch_bounds__(kDecWaves * kWave, (MODE == kSelect && D == 128) ? 2 : 3)
+// Wavefronts per workgroup: 8 when the launch has at most one workgroup per
+// compute unit (256), else 4.
+inline int decode_waves(int64_t blocks) { return blocks <= 256 ? 8 : 4; }
+
+// P: pages in flight per wavefront (its K and V rows held in registers).
+template <int D, int G, int MODE, int C, int W, int P>
+__global__ __launch_bounds__(W * kWave, W == 8 ? 1 : ((MODE == kSelect && D == 128) ? 2 : 3))
 void decode_mfma_kernel(
     const float* __restrict__ q, const bf16_t* __restrict__ k_pool,
     const bf16_t* __restrict__ v_pool, const int32_t* __restrict__ page_table,
@@ -321,11 +329,11 @@ void decode_mfma_kernel(
   constexpr int NB = D / 16;            // 16-column blocks of the output
   static_assert(G <= 8, "group size");
   __shared__ __align__(16) uint16_t qsp[3][8][D];         // split scaled queries
-  __shared__ __align__(16) uint16_t vt[kDecWaves][16][D];  // V page of each wavefront
-  __shared__ float sm_m[kDecWaves][G], sm_mt[kDecWaves][G], sm_l[kDecWaves][G];
-  __shared__ float sm_acc[kDecWaves][G][D];
+  __shared__ __align__(16) uint16_t vt[W][16][D];  // V page of each wavefront
+  __shared__ float sm_m[W][G], sm_mt[W][G], sm_l[W][G];
+  __shared__ float sm_acc[W][G][D];
   // kSelect: the selection's workspace and this split's share of the list
-  __shared__ SelectLds<MODE == kSelect ? kDecWaves : 1> ssel;
+  __shared__ SelectLds<MODE == kSelect ? W : 1> ssel;
   __shared__ int spages[MODE == kSelect ? kMaxSplitPages : 1];
 
   const int split = blockIdx.x % n_splits;
@@ -345,11 +353,11 @@ void decode_mfma_kernel(
   // The queries are requested first: their split is the first thing waited
   // for after the page ids, and vector loads complete in order.
   const float* qg = q + ((int64_t)b * hkv * G + g * G) * D;
-  constexpr int kQPer = (G * D + kDecWaves * kWave - 1) / (kDecWaves * kWave);
+  constexpr int kQPer = (G * D + W * kWave - 1) / (W * kWave);
   float qv[kQPer];
 #pragma unroll
   for (int i = 0; i < kQPer; ++i) {
-    const int e = threadIdx.x + i * kDecWaves * kWave;
+    const int e = threadIdx.x + i * W * kWave;
     qv[i] = e < G * D ? qg[e] : 0.0f;
   }
 
@@ -364,7 +372,7 @@ void decode_mfma_kernel(
     const int per = ceil_div(budget, n_splits);
     first = split * per;
     int32_t* dst = sa.sel ? sa.sel + (int64_t)unit * budget : nullptr;
-    const int kept = select_unit<kDecWaves, C>(
+    const int kept = select_unit<W, C>(
         sa.scores + (int64_t)unit * max_pages, ceil_div(len, kPage), budget, sa.n_sink,
         sa.n_local, ssel, [&](int o, int p) {
           if (o >= first && o < first + per) {
@@ -375,7 +383,7 @@ void decode_mfma_kernel(
     __syncthreads();  // spages complete
     if (dst)
       for (int o = max(kept, first) + (int)threadIdx.x; o < min(first + per, budget);
-           o += kDecWaves * kWave)
+           o += W * kWave)
         dst[o] = -1;
     if (sa.sel_count && split == 0 && threadIdx.x == 0) sa.sel_count[unit] = kept;
     hi = min(first + per, kept);
@@ -389,26 +397,26 @@ void decode_mfma_kernel(
     first = min(split * per, np);
     hi = min(split * per + per, np);
   }
-  // Wavefront `wave` takes the split's items first + wave + kDecWaves*k.
-  const int n_items = hi > first + wave ? ceil_div(hi - first - wave, kDecWaves) : 0;
+  // Wavefront `wave` takes the split's items first + wave + W*k.
+  const int n_items = hi > first + wave ? ceil_div(hi - first - wave, W) : 0;
 
 
-  // Page ids of a block of kIdBlock items (list entry, then table entry).
-  // Every read is in bounds: list slots are clamped to the row, and items
-  // past the wavefront's last one read logical page 0 and get no tokens.
-  auto resolve_block = [&](int blk, PageRef (&refs)[kIdBlock]) {
-    int pg[kIdBlock];
+  // Page ids of a block of P items (list entry, then table entry). Every
+  // read is in bounds: list slots are clamped to the row, and items past the
+  // wavefront's last one read logical page 0 and get no tokens.
+  auto resolve_block = [&](int blk, PageRef (&refs)[P]) {
+    int pg[P];
 #pragma unroll
-    for (int j = 0; j < kIdBlock; ++j) {
-      const int item = first + wave + (blk * kIdBlock + j) * kDecWaves;
+    for (int j = 0; j < P; ++j) {
+      const int item = first + wave + (blk * P + j) * W;
       if constexpr (MODE == kSelect)
         pg[j] = spages[min(item - first, kMaxSplitPages - 1)];
       else
         pg[j] = MODE == kList ? list[min(item, budget - 1)] : item;
     }
 #pragma unroll
-    for (int j = 0; j < kIdBlock; ++j) {
-      const bool ok = blk * kIdBlock + j < n_items;
+    for (int j = 0; j < P; ++j) {
+      const bool ok = blk * P + j < n_items;
       const int pc = ok ? pg[j] : 0;
       refs[j].phys = row[pc];
       refs[j].cnt = ok ? min(kPage, len - pc * kPage) : 0;
@@ -424,14 +432,16 @@ void decode_mfma_kernel(
     for (int i = 0; i < NT; ++i) vf[i] = ld16(v_pool + off + (rg + i * RPL) * D + vc * 8);
   };
 
-  PageRef ids[kIdBlock];
+  // Page ids are resolved two blocks of P ahead of their use.
+  PageRef ids[P], nxt[P];
   resolve_block(0, ids);
+  resolve_block(1, nxt);
 
   // Split of the scaled queries, once per workgroup (the table reads above
   // are in flight meanwhile).
 #pragma unroll
   for (int i = 0; i < kQPer; ++i) {
-    const int e = threadIdx.x + i * kDecWaves * kWave;
+    const int e = threadIdx.x + i * W * kWave;
     if (e < G * D) {
       uint32_t hi_, mid_, lo_;
       bf16_split3(qv[i] * qscale, hi_, mid_, lo_);
@@ -442,10 +452,10 @@ void decode_mfma_kernel(
     }
   }
 
-  // Two pages in flight before the barrier.
-  uint4 ka[KB], va[NT], kb_[KB], vb[NT];
-  load(ids[0], ka, va);
-  load(ids[1], kb_, vb);
+  // P pages in flight before the barrier.
+  uint4 kbuf[P][KB], vbuf[P][NT];
+#pragma unroll
+  for (int j = 0; j < P; ++j) load(ids[j], kbuf[j], vbuf[j]);
   __syncthreads();
   const bool live = col < G;  // lanes of real heads in the B operand
 
@@ -530,25 +540,29 @@ void decode_mfma_kernel(
     wave_sync_lds();  // V is read before the next page overwrites it
   };
 
-  // Pipeline: the next page's loads are in flight while the current page is
-  // attended; the next block of page ids is resolved a block ahead.
-  PageRef nxt[kIdBlock];
-  for (int base = 0; base < n_items; base += kIdBlock) {
-    resolve_block(base / kIdBlock + 1, nxt);
+  // Pipeline: while page j of a block is attended, the loads of the pages of
+  // the next block are in flight; each buffer is refilled as soon as its
+  // page is attended (every load in the loop unconditional, so the number in
+  // flight is the same on every path). The last block is attended after the
+  // loop and requests nothing more.
+  int base = 0;
+  for (; base + P < n_items; base += P) {
+    PageRef nn[P];
+    resolve_block(base / P + 2, nn);
 #pragma unroll
-    for (int j = 0; j < kIdBlock; j += 2) {
-      if (base + j >= n_items) break;  // uniform per wavefront
-      // ids of items base+j+2 and base+j+3 (possibly in the next block)
-      const PageRef r2 = j + 2 < kIdBlock ? ids[j + 2] : nxt[j + 2 - kIdBlock];
-      const PageRef r3 = j + 3 < kIdBlock ? ids[j + 3] : nxt[j + 3 - kIdBlock];
-      attend(ids[j], ka, va);
-      load(r2, ka, va);
-      if (base + j + 1 < n_items) attend(ids[j + 1], kb_, vb);
-      load(r3, kb_, vb);
+    for (int j = 0; j < P; ++j) {
+      attend(ids[j], kbuf[j], vbuf[j]);
+      load(nxt[j], kbuf[j], vbuf[j]);
     }
 #pragma unroll
-    for (int j = 0; j < kIdBlock; ++j) ids[j] = nxt[j];
+    for (int j = 0; j < P; ++j) {
+      ids[j] = nxt[j];
+      nxt[j] = nn[j];
+    }
   }
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if (base + j < n_items) attend(ids[j], kbuf[j], vbuf[j]);  // uniform per wavefront
 
   // Per wavefront: normaliser over token groups; each (head, column) of the
   // accumulators is owned by one lane.
@@ -571,24 +585,44 @@ void decode_mfma_kernel(
 
   // Merge against the split's true max; write the partials.
   const int hq = hkv * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecWaves * kWave) {
+  for (int idx = threadIdx.x; idx < G * D; idx += W * kWave) {
     const int h = idx / D;
     const int d = idx % D;
     float mo = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) mo = fmax_(mo, sm_mt[w][h]);
+    for (int w = 0; w < W; ++w) mo = fmax_(mo, sm_mt[w][h]);
     float a = 0.0f, lsum = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
       const float mw = sm_m[w][h];
       const float wt = mw == -INFINITY ? 0.0f : exp2_(mw - mo);
       a = __builtin_fmaf(wt, sm_acc[w][h][d], a);
       lsum = __builtin_fmaf(wt, sm_l[w][h], lsum);
     }
+    const float m_nat = mo == -INFINITY ? -INFINITY : mo * kLn2;
+    if (sa.out) {
+      // One split: the merge of ps_combine over that single partial, with
+      // the same operations (sink in the denominator only).
+      const int64_t row = (int64_t)b * hq + g * G + h;
+      const float sig = sa.sink ? sa.sink[g * G + h] : -INFINITY;
+      const float mx = fmax_(m_nat, sig);
+      if (mx == -INFINITY) {
+        sa.out[row * D + d] = 0.0f;
+        if (sa.lse && d == 0) sa.lse[row] = -INFINITY;
+        continue;
+      }
+      float l = m_nat != -INFINITY ? __builtin_fmaf(expf(m_nat - mx), lsum, 0.0f) : 0.0f;
+      if (sig != -INFINITY) l += expf(sig - mx);
+      const float inv = 1.0f / l;
+      const float wgt = m_nat == -INFINITY ? 0.0f : expf(m_nat - mx);
+      sa.out[row * D + d] = __builtin_fmaf(wgt, a, 0.0f) * inv;
+      if (sa.lse && d == 0) sa.lse[row] = mx + logf(l);
+      continue;
+    }
     const int64_t ph = ((int64_t)b * hq + g * G + h) * n_splits + split;
     part_acc[ph * D + d] = a;
     if (d == 0) {
-      part_ml[ph * 2 + 0] = mo == -INFINITY ? -INFINITY : mo * kLn2;
+      part_ml[ph * 2 + 0] = m_nat;
       part_ml[ph * 2 + 1] = lsum;
     }
   }
@@ -603,32 +637,30 @@ hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void
   const dim3 grid((unsigned)blocks), block(kDecWaves * kWave);
   const float qscale = scale * 1.44269504088896340736f;  // log2(e)
   if (s.kv_bf16) {
-    const SelectArgs none{nullptr, 0, 0, nullptr, nullptr};
+    const SelectArgs none{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+    const int waves = decode_waves(blocks);
+    const dim3 wblock(waves * kWave);
+#define PS_DECODE_MFMA(DD, MM, WW)                                                             \
+  hipLaunchKernelGGL((decode_mfma_kernel<DD, kG, MM, 1, WW, 2>), grid, wblock, 0, st, q,       \
+                     static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),   \
+                     page_table, seq_lens, sel, sel_count, sparse ? budget : 0, s.hkv,          \
+                     s.max_pages, n_splits, qscale, part_acc, part_ml, none)
+#define PS_DECODE_MFMA_W(DD, MM)                      \
+  do {                                                \
+    if (waves == 8) PS_DECODE_MFMA(DD, MM, 8);        \
+    else PS_DECODE_MFMA(DD, MM, 4);                   \
+  } while (0)
     PS_WITH_GROUP(s.group, {
       if (s.head_dim == 64) {
-        if (sparse)
-          hipLaunchKernelGGL((decode_mfma_kernel<64, kG, kList, 1>), grid, block, 0, st, q,
-                             static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
-                             page_table, seq_lens, sel, sel_count, budget, s.hkv, s.max_pages,
-                             n_splits, qscale, part_acc, part_ml, none);
-        else
-          hipLaunchKernelGGL((decode_mfma_kernel<64, kG, kDense, 1>), grid, block, 0, st, q,
-                             static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
-                             page_table, seq_lens, nullptr, nullptr, 0, s.hkv, s.max_pages,
-                             n_splits, qscale, part_acc, part_ml, none);
+        if (sparse) PS_DECODE_MFMA_W(64, kList);
+        else PS_DECODE_MFMA_W(64, kDense);
       } else {
-        if (sparse)
-          hipLaunchKernelGGL((decode_mfma_kernel<128, kG, kList, 1>), grid, block, 0, st, q,
-                             static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
-                             page_table, seq_lens, sel, sel_count, budget, s.hkv, s.max_pages,
-                             n_splits, qscale, part_acc, part_ml, none);
-        else
-          hipLaunchKernelGGL((decode_mfma_kernel<128, kG, kDense, 1>), grid, block, 0, st, q,
-                             static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),
-                             page_table, seq_lens, nullptr, nullptr, 0, s.hkv, s.max_pages,
-                             n_splits, qscale, part_acc, part_ml, none);
+        if (sparse) PS_DECODE_MFMA_W(128, kList);
+        else PS_DECODE_MFMA_W(128, kDense);
       }
     });
+#undef PS_DECODE_MFMA_W
+#undef PS_DECODE_MFMA
     return hipGetLastError();
   }
   PS_WITH_KV(false, s.head_dim, {
@@ -654,25 +686,32 @@ hipError_t launch_select_decode(const Shape& s, const float* q, const void* k_po
                                 const int32_t* seq_lens, const float* scores, int budget,
                                 int n_sink, int n_local, float scale, int n_splits, int32_t* sel,
                                 int32_t* sel_count, float* part_acc, float* part_ml,
-                                hipStream_t st) {
+                                const float* sink, float* out, float* lse, hipStream_t st) {
   const int64_t blocks = (int64_t)s.batch * s.hkv * n_splits;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (!s.kv_bf16 || s.max_pages > kSelectDecodeMaxPages ||
-      (budget + n_splits - 1) / n_splits > kMaxSplitPages)
+      (budget + n_splits - 1) / n_splits > kMaxSplitPages || (out && n_splits != 1))
     return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(kDecWaves * kWave);
+  const int waves = decode_waves(blocks);
+  const dim3 grid((unsigned)blocks), block(waves * kWave);
   const float qscale = scale * 1.44269504088896340736f;  // log2(e)
-  const SelectArgs sa{scores, n_sink, n_local, sel, sel_count};
-  const int per_lane = (s.max_pages + kDecWaves * kWave - 1) / (kDecWaves * kWave);
-#define PS_SELECT_DECODE(DD, CC)                                                              \
-  hipLaunchKernelGGL((decode_mfma_kernel<DD, kG, kSelect, CC>), grid, block, 0, st, q,        \
+  const SelectArgs sa{scores, n_sink, n_local, sel, sel_count, sink, out, lse};
+  const int per_lane = (s.max_pages + waves * kWave - 1) / (waves * kWave);
+#define PS_SELECT_DECODE(DD, CC, WW)                                                          \
+  hipLaunchKernelGGL((decode_mfma_kernel<DD, kG, kSelect, CC, WW, 2>), grid,                   \
+                     block, 0, st, q,                                                         \
                      static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),  \
                      page_table, seq_lens, nullptr, nullptr, budget, s.hkv, s.max_pages,      \
                      n_splits, qscale, part_acc, part_ml, sa)
-#define PS_SELECT_DECODE_C(DD)                    \
-  do {                                            \
-    if (per_lane <= 16) PS_SELECT_DECODE(DD, 16); \
-    else PS_SELECT_DECODE(DD, 32);                \
+#define PS_SELECT_DECODE_C(DD)                                                   \
+  do {                                                                           \
+    if (waves == 8) {                                                            \
+      if (per_lane <= 8) PS_SELECT_DECODE(DD, 8, 8);                             \
+      else PS_SELECT_DECODE(DD, 16, 8);                                          \
+    } else {                                                                     \
+      if (per_lane <= 16) PS_SELECT_DECODE(DD, 16, 4);                           \
+      else PS_SELECT_DECODE(DD, 32, 4);                                          \
+    }                                                                            \
   } while (0)
   PS_WITH_GROUP(s.group, {
     if (s.head_dim == 64)

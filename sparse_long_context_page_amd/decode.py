@@ -79,10 +79,17 @@ class DecodeStep:
                 self.refresh_tail_meta(k_pool, page_table, seq_lens, tail_begin, meta, stream)
             ops.ps_score_pages(g, q, meta, page_table, seq_lens, self.scores, stream)
         acc, ml = self.partials(self.n_splits)
+        if self.fused and self.n_splits == 1:  # select, decode and merge in one launch
+            ops.ps_select_sparse_decode(g, q, k_pool, v_pool, page_table, seq_lens, self.scores,
+                                        self.budget, self.n_sink, self.n_local, self.scale, 1,
+                                        self.sel, self.sel_count, None, None, sink, self.out,
+                                        self.lse, stream)
+            return self.out, self.lse
         if self.fused:
             ops.ps_select_sparse_decode(g, q, k_pool, v_pool, page_table, seq_lens, self.scores,
                                         self.budget, self.n_sink, self.n_local, self.scale,
-                                        self.n_splits, self.sel, self.sel_count, acc, ml, stream)
+                                        self.n_splits, self.sel, self.sel_count, acc, ml,
+                                        stream=stream)
         else:
             ops.ps_select_topk(g, self.scores, seq_lens, self.budget, self.n_sink, self.n_local,
                                self.sel, self.sel_count, stream)

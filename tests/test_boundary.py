@@ -138,9 +138,10 @@ def test_fused_select_decode_validation():
     lib = _lib.load()
     g = geom()
 
-    def call(g=g, sel=X, cnt=X, budget=8, ns=1, nl=2, splits=2, scores=X):
+    def call(g=g, sel=X, cnt=X, budget=8, ns=1, nl=2, splits=2, scores=X, acc=X, ml=X,
+             sink=None, out=None, lse=None):
         return lib.ps_select_sparse_decode(g, X, X, X, X, X, scores, budget, ns, nl, 0.1, splits,
-                                           sel, cnt, X, X, None)
+                                           sel, cnt, acc, ml, sink, out, lse, None)
     assert call(scores=None) == _lib.PS_ERR_NULL
     assert call(sel=None) == _lib.PS_ERR_NULL           # one of the pair
     assert call(cnt=None) == _lib.PS_ERR_NULL
@@ -151,7 +152,13 @@ def test_fused_select_decode_validation():
     assert call(g=geom(kv_dtype=_lib.PS_F32)) == _lib.PS_ERR_UNSUPPORTED
     assert call(g=geom(max_pages=8193)) == _lib.PS_ERR_UNSUPPORTED
     assert call(budget=1026, ns=0, nl=0, splits=2) == _lib.PS_ERR_UNSUPPORTED  # 513 per split
+    assert call(acc=None) == _lib.PS_ERR_NULL           # partials needed without out
+    assert call(out=X) == _lib.PS_ERR_BUDGET            # merged output needs one split
+    assert call(sink=X) == _lib.PS_ERR_BUDGET           # sink and lse only with out
+    assert call(lse=X) == _lib.PS_ERR_BUDGET
     assert call(g=geom(batch=0), sel=None, cnt=None) == _lib.PS_OK
+    assert call(g=geom(batch=0), splits=1, acc=None, ml=None, sink=X, out=X, lse=X) == \
+        _lib.PS_OK
 
 
 def test_partials_overflow():

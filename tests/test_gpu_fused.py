@@ -37,8 +37,10 @@ def _both(inp, budget=None, n_sink=None, n_local=None, n_splits=None):
                                inp["seq_lens"], inp["sink"])
         acc, ml = step.partials(step.n_splits)
         torch.cuda.synchronize()
-        res.append({k: v.clone() for k, v in dict(sel=step.sel, cnt=step.sel_count, acc=acc,
-                                                  ml=ml, out=out, lse=lse).items()})
+        got = dict(sel=step.sel, cnt=step.sel_count, out=out, lse=lse)
+        if step.n_splits > 1:  # with one split the fused launch writes no partials
+            got.update(acc=acc, ml=ml)
+        res.append({k: v.clone() for k, v in got.items()})
     return res
 
 
@@ -61,6 +63,7 @@ def test_fused_without_page_list_output():
     inp = wl.make_inputs(w, device="cuda")
     g = geometry(inp)
     a, _ = _both(inp)
+    assert w.n_splits > 1
     meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
     step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
                       inp["scale"])
@@ -71,6 +74,31 @@ def test_fused_without_page_list_output():
                                 w.n_local, inp["scale"], step.n_splits, None, None, acc, ml)
     torch.cuda.synchronize()
     assert torch.equal(acc, a["acc"]) and torch.equal(ml, a["ml"])
+
+
+@pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])
+def test_fused_one_split_merged_output_bitwise(w):
+    """With one split the fused launch also merges (sink in the denominator):
+    equal, bit for bit, to the unfused one-split decode followed by
+    ps_combine, page lists included."""
+    inp = wl.make_inputs(w, device="cuda")
+    a, b = _both(inp, n_splits=1)
+    for k in ("sel", "cnt", "out", "lse"):
+        assert torch.equal(a[k], b[k]), (w.name, k)
+    if inp["sink"] is not None:  # and without the sink
+        g = geometry(inp)
+        meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+        step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, 1, w.dense_splits,
+                          inp["scale"], fused=False)
+        want, _ = step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
+                              inp["seq_lens"], None)
+        want = want.clone()
+        step2 = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, 1, w.dense_splits,
+                           inp["scale"], fused=True)
+        got, _ = step2.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
+                              inp["seq_lens"], None)
+        torch.cuda.synchronize()
+        assert torch.equal(got, want)
 
 
 @pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])

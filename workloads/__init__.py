@@ -78,7 +78,7 @@ B8_16K = Workload("b8_16k_needles_sink_page", batch=8, num_q_heads=12, num_kv_he
                   seed=1002, n_splits=8, dense_splits=32)
 HEADLINE = Workload("b32_64k_needles_local4", batch=32, num_q_heads=12, num_kv_heads=2,
                     head_dim=128, context=65536, budget_pages=128, n_local=4, needles=8,
-                    seed=1003, n_splits=8, dense_splits=64)
+                    seed=1003, n_splits=4, dense_splits=64)
 SINK = Workload("b16_32k_learned_sink", batch=16, num_q_heads=64, num_kv_heads=8, head_dim=64,
                 context=32768, budget_pages=64, sink_logits=True, seed=1004, n_splits=4,
                 dense_splits=32)
