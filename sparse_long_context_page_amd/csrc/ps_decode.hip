@@ -335,6 +335,7 @@ void decode_mfma_kernel(
   // kSelect: the selection's workspace and this split's share of the list
   __shared__ SelectLds<MODE == kSelect ? W : 1> ssel;
   __shared__ int spages[MODE == kSelect ? kMaxSplitPages : 1];
+  __shared__ int sphys[MODE == kSelect ? kMaxSplitPages : 1];
 
   const int split = blockIdx.x % n_splits;
   const int unit = blockIdx.x / n_splits;  // b * hkv + g
@@ -372,11 +373,14 @@ void decode_mfma_kernel(
     const int per = ceil_div(budget, n_splits);
     first = split * per;
     int32_t* dst = sa.sel ? sa.sel + (int64_t)unit * budget : nullptr;
-    const int kept = select_unit<W, C>(
+    // The physical page of each kept page is read next to its score, so the
+    // pages' K and V can be requested right after the selection.
+    const int kept = select_unit<W, C, true>(
         sa.scores + (int64_t)unit * max_pages, ceil_div(len, kPage), budget, sa.n_sink,
-        sa.n_local, ssel, [&](int o, int p) {
+        sa.n_local, ssel, row, [&](int o, int p, int ph) {
           if (o >= first && o < first + per) {
             spages[o - first] = p;
+            sphys[o - first] = ph;
             if (dst) dst[o] = p;
           }
         });
@@ -418,7 +422,12 @@ void decode_mfma_kernel(
     for (int j = 0; j < P; ++j) {
       const bool ok = blk * P + j < n_items;
       const int pc = ok ? pg[j] : 0;
-      refs[j].phys = row[pc];
+      if constexpr (MODE == kSelect) {  // physical pages came with the selection
+        const int item = first + wave + (blk * P + j) * W;
+        refs[j].phys = ok ? sphys[min(item - first, kMaxSplitPages - 1)] : 0;
+      } else {
+        refs[j].phys = row[pc];
+      }
       refs[j].cnt = ok ? min(kPage, len - pc * kPage) : 0;
     }
   };

@@ -50,26 +50,27 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // Selects the kept pages of one unit whose n pages have the scores row[0..n).
 // Called by all WAVES*64 threads of the workgroup with the same arguments;
 // requires n <= WAVES*64*C and n_sink + n_local <= budget. Calls
-// emit(slot, page) once per kept page, slots 0..kept-1 in ascending page
-// order, and returns kept = min(budget, n). Ends with the workgroup's LDS
-// free for reuse only after a barrier of the caller.
+// emit(slot, page, phys) once per kept page, slots 0..kept-1 in ascending
+// page order, with phys = table[page] read next to the scores when a table
+// row is given (else -1), and returns kept = min(budget, n). Ends with the
+// workgroup's LDS free for reuse only after a barrier of the caller.
 //
 // The kept candidates are the r best in the order (key descending, page
 // ascending). Radix passes narrow the r-th key's bits; once its bin holds at
 // most 64 keys, those are gathered and wavefront 0 ranks them directly, which
 // fixes the cut exactly as (key, page); when every bit is decided first, the
 // bin's keys are equal and the cut is the remaining-th lowest page among them.
-template <int WAVES, int C, typename Emit>
+template <int WAVES, int C, bool PHYS, typename Emit>
 __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n, int budget,
                                            int n_sink, int n_local, SelectLds<WAVES>& sh,
-                                           Emit emit) {
+                                           const int32_t* __restrict__ table, Emit emit) {
   constexpr int kThreads = WAVES * kWave;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
   if (budget >= n) {  // dense: every page, ascending
-    for (int i = tid; i < n; i += kThreads) emit(i, i);
+    for (int i = tid; i < n; i += kThreads) emit(i, i, PHYS ? table[i] : -1);
     return n;
   }
 
@@ -82,8 +83,12 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
 
   // Keys (pages past the request re-read its last score and never count).
   uint32_t key[C];
+  int phys[PHYS ? C : 1];
 #pragma unroll
-  for (int j = 0; j < C; ++j) key[j] = order_key(row[min(page(j), n - 1)]);
+  for (int j = 0; j < C; ++j) {
+    key[j] = order_key(row[min(page(j), n - 1)]);
+    if constexpr (PHYS) phys[j] = table[min(page(j), n - 1)];
+  }
   uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
@@ -246,7 +251,7 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
       const bool keep = ((cls[j / 16] >> (2 * (j % 16))) & 3) != 0;
       const uint64_t km = __ballot(keep);
       const int o = slot + lanes_below(km);
-      if (keep && o < budget) emit(o, page(j));
+      if (keep && o < budget) emit(o, page(j), PHYS ? phys[PHYS ? j : 0] : -1);
       slot += __popcll(km);
     }
   } else {  // equal keys: the lowest `remaining` tied pages are kept
@@ -258,7 +263,7 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
       const bool keep = c == 2 || (c == 1 && tie_rank + lanes_below(tm) < remaining);
       const uint64_t km = __ballot(keep);
       const int o = slot + lanes_below(km);
-      if (keep && o < budget) emit(o, page(j));
+      if (keep && o < budget) emit(o, page(j), PHYS ? phys[PHYS ? j : 0] : -1);
       slot += __popcll(km);
       tie_rank += __popcll(tm);
     }

@@ -22,8 +22,9 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
   const int unit = blockIdx.x;  // b * hkv + g
   const int n = ceil_div(seq_lens[unit / hkv], kPage);
   int32_t* dst = sel + (int64_t)unit * budget;
-  const int kept = select_unit<kSelWaves, C>(scores + (int64_t)unit * max_pages, n, budget, n_sink,
-                                             n_local, sh, [&](int o, int p) { dst[o] = p; });
+  const int kept = select_unit<kSelWaves, C, false>(scores + (int64_t)unit * max_pages, n, budget,
+                                                    n_sink, n_local, sh, nullptr,
+                                                    [&](int o, int p, int) { dst[o] = p; });
   for (int i = kept + (int)threadIdx.x; i < budget; i += kSelThreads) dst[i] = -1;
   if (threadIdx.x == 0) sel_count[unit] = kept;
 }
