@@ -214,24 +214,24 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
       bn[kb] = ld16(src + D + kb * 32);
     }
   };
-  // The last page's keys, when this wavefront holds it (other wavefronts
-  // read page 0 instead, so that no load is conditional).
+  // Two tiles of metadata in flight, requested whatever the run's length.
+  uint4 xa[KB], na[KB], xb[KB], nb[KB];
+  load(0, xa, na);
+  load(1, xb, nb);
+  // The last page's keys, when this wavefront holds it, behind its first
+  // two tiles (waits for the tiles already cover them).
   const int tail = np - 1;
   const bool has_tail = REFRESH && n_tiles > 0 && tail < p0 + n_tiles * 16;
   const int col_tail = tail % 16;
   PageFold<bf16_t, D> tail_keys;
   int phys_tail = 0;
-  if constexpr (REFRESH) {
+  if (has_tail) {
     int pt = phys[0];
 #pragma unroll
     for (int t = 1; t < kMaxTiles; ++t) pt = t == (tail - p0) / 16 ? phys[t] : pt;
-    phys_tail = has_tail ? __builtin_amdgcn_readlane(pt, col_tail) : 0;
+    phys_tail = __builtin_amdgcn_readlane(pt, col_tail);
     tail_keys.load(k_pool + ((int64_t)phys_tail * hkv + g) * kPage * D, lane);
   }
-  // Two tiles of metadata in flight, requested whatever the run's length.
-  uint4 xa[KB], na[KB], xb[KB], nb[KB];
-  load(0, xa, na);
-  load(1, xb, nb);
   __builtin_amdgcn_sched_barrier(0);  // the split below overlaps these loads
 
   // 2. exact split of the queries, by sign, straight into A fragments:
