@@ -184,6 +184,13 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   // loads behind the length, a round trip more.
   const int len = seq_lens[b];
   __builtin_amdgcn_sched_barrier(0);
+  // table entries first: vector loads complete in order, and the first
+  // metadata requests wait only for the entries of the first tiles
+  const int32_t* row = page_table + (int64_t)b * max_pages;
+  int phys[kMaxTiles];
+#pragma unroll
+  for (int t = 0; t < kMaxTiles; ++t) phys[t] = row[min(p0 + t * 16 + col, max_pages - 1)];
+  __builtin_amdgcn_sched_barrier(0);
   const float* qh = q + ((int64_t)b * hkv * G + g * G + min(col, G - 1)) * D + kgrp * 8;
   float4 qv[KB][2];
 #pragma unroll
@@ -191,10 +198,6 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
     qv[kb][0] = *reinterpret_cast<const float4*>(qh + kb * 32);
     qv[kb][1] = *reinterpret_cast<const float4*>(qh + kb * 32 + 4);
   }
-  const int32_t* row = page_table + (int64_t)b * max_pages;
-  int phys[kMaxTiles];
-#pragma unroll
-  for (int t = 0; t < kMaxTiles; ++t) phys[t] = row[min(p0 + t * 16 + col, max_pages - 1)];
   __builtin_amdgcn_sched_barrier(0);  // issue all of the above first
 
   const int np = ceil_div(len, kPage);
