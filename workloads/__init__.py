@@ -84,7 +84,7 @@ SINK = Workload("b16_32k_learned_sink", batch=16, num_q_heads=64, num_kv_heads=8
                 dense_splits=32)
 RAGGED = Workload("b64_ragged_4k_128k_shared_pool", batch=64, num_q_heads=28, num_kv_heads=4,
                   head_dim=128, ctx_range=(4096, 131072), budget_pages=128, needles=8,
-                  permuted_pool=True, max_pages=8192, seed=1005, n_splits=8, dense_splits=64)
+                  permuted_pool=True, max_pages=8192, seed=1005, n_splits=1, dense_splits=64)
 
 WORKLOADS = {w.name: w for w in (TINY, TINY_DENSE, B8_16K, HEADLINE, SINK, RAGGED)}
 
