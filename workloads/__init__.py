@@ -80,7 +80,7 @@ HEADLINE = Workload("b32_64k_needles_local4", batch=32, num_q_heads=12, num_kv_h
                     head_dim=128, context=65536, budget_pages=128, n_local=4, needles=8,
                     seed=1003, n_splits=4, dense_splits=64)
 SINK = Workload("b16_32k_learned_sink", batch=16, num_q_heads=64, num_kv_heads=8, head_dim=64,
-                context=32768, budget_pages=64, sink_logits=True, seed=1004, n_splits=4,
+                context=32768, budget_pages=64, sink_logits=True, seed=1004, n_splits=1,
                 dense_splits=32)
 RAGGED = Workload("b64_ragged_4k_128k_shared_pool", batch=64, num_q_heads=28, num_kv_heads=4,
                   head_dim=128, ctx_range=(4096, 131072), budget_pages=128, needles=8,
