@@ -57,9 +57,10 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 //
 // The kept candidates are the r best in the order (key descending, page
 // ascending). Radix passes narrow the r-th key's bits; once its bin holds at
-// most 64 keys, those are gathered and wavefront 0 ranks them directly, which
-// fixes the cut exactly as (key, page); when every bit is decided first, the
-// bin's keys are equal and the cut is the remaining-th lowest page among them.
+// most 64 keys and more than one pass would still be needed, those keys are
+// gathered and wavefront 0 ranks them directly, which fixes the cut exactly as
+// (key, page); when every bit is decided first, the bin's keys are equal and
+// the cut is the remaining-th lowest page among them.
 template <int WAVES, int C, bool PHYS, typename Emit>
 __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n, int budget,
                                            int n_sink, int n_local, SelectLds<WAVES>& sh,
@@ -112,7 +113,9 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
 
   // Radix passes. Invariant: candidates with (k & pmask) > prefix are kept,
   // those with (k & pmask) < prefix are dropped, and `remaining` of the
-  // `in_bin` candidates with (k & pmask) == prefix are kept.
+  // `in_bin` candidates with (k & pmask) == prefix are kept. A pass costs one
+  // barrier and ranking the bin three, so a pass that decides every
+  // remaining bit is taken even when the bin is small enough to rank.
   const uint32_t diff = kmin ^ kmax;
   int top = diff ? 32 - __clz(diff) : 0;  // undecided low bits
   uint32_t pmask = top == 32 ? 0u : ~((1u << top) - 1u);
@@ -121,7 +124,8 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
   int in_bin = hi - lo;
   int pass = 0;
 #pragma unroll 1
-  while (remaining > 0 && in_bin > remaining && in_bin > kSelRankMax && top > 0) {
+  while (remaining > 0 && in_bin > remaining && top > 0 &&
+         (in_bin > kSelRankMax || top <= kSelDigitBits)) {
     const int width = top < kSelDigitBits ? top : kSelDigitBits;
     const int shift = top - width;
     int* h = sh.hist[pass % 3];

@@ -300,9 +300,15 @@ def test_select_register_tiles(max_pages):
     batch = len(lengths)
     g = Geometry(batch, 2, 1, 64, max_pages, 1)
     seq = torch.tensor([n * 16 - 5 if n > 1 else 3 for n in lengths], dtype=torch.int32)
-    for kind in ("normal", "ties"):
+    for kind in ("normal", "ties", "narrow"):
         if kind == "ties":
             sc = torch.randint(-3, 4, (batch, 1, max_pages), generator=gen).float()
+        elif kind == "narrow":
+            # exact fp32 values 1000 + j * 2^-14: the keys differ only in their
+            # low 14 bits, so after one 8-bit pass the bin is small and a
+            # second pass decides every bit (with some exact ties)
+            j = torch.randint(0, 1 << 14, (batch, 1, max_pages), generator=gen)
+            sc = 1000.0 + j.float() * 2.0 ** -14
         else:
             sc = torch.randn((batch, 1, max_pages), generator=gen) * 30 + 100
         for budget, ns, nl in ((128, 1, 4), (64, 0, 0), (2, 1, 1)):
