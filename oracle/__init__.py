@@ -16,6 +16,14 @@ from .pagesparse_ref import (  # noqa: F401
     unit_page_meta,
     page_meta_pool,
     unit_scores,
+    FP8_E4M3,
+    FP8_MAX,
+    fp8_e4m3_value,
+    fp8_e4m3_table,
+    fp8_round_up,
+    fp8_round_down,
+    widen_fp8,
+    fp8_bounds,
     select_pages,
     ambiguous_pages,
     gather_tokens,

@@ -168,6 +168,93 @@ def unit_scores(q_group: np.ndarray, kmax: np.ndarray, kmin: np.ndarray):
 
 
 # ---------------------------------------------------------------------------
+# Stage 1-2 variant: compressed metadata (8-bit bounds)
+#
+# "Faster Than Flash: Exploiting Attention Sparsity for Efficient Long-Context
+# Decoding", section "Methodology", item 1 (content-aware scanning via
+# low-bit quantization): the scan that decides which blocks to read runs on a
+# low-bit copy, and the kept blocks are then read at full precision. Applied
+# here to the page metadata, the stream that dominates the scan, with the
+# rounding directed so that the bound of "Don't read the haystack" ("Part
+# two: the skipping") stays an upper bound: kmax is rounded up and kmin down,
+# so the 8-bit box contains the exact one and, for every q, the bound can only
+# grow. The attention itself still reads the full-precision keys and values.
+#
+# Format (this build's reading; the pages name no 8-bit format): the 8-bit
+# floating point E4M3 of the OCP 8-bit floating point specification, the
+# variant without infinities: 1 sign bit, 4 exponent bits with bias 7, 3
+# mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; the two
+# codes with every exponent and mantissa bit set are NaN; the largest finite
+# magnitude is 448. A zero result is always code 0x00. A bound beyond +-448
+# saturates to +-448 (the fp8 metadata mode requires |K| <= 448; beyond it the
+# saturated bound is no longer admissible).
+
+FP8_E4M3 = "fp8_e4m3"
+FP8_MAX = 448.0
+
+
+def fp8_e4m3_value(code: int) -> float:
+    """Value of one E4M3 code, from the format's definition (NaN codes give nan)."""
+    code = int(code) & 0xFF
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * (m / 8.0) * 2.0 ** -6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+def fp8_e4m3_table() -> np.ndarray:
+    """float64 [256]: the value of every code."""
+    return np.array([fp8_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def _fp8_finite_sorted():
+    """(values ascending, their codes) over the finite codes, one code per
+    value (zero is 0x00)."""
+    t = fp8_e4m3_table()
+    by_val = {}
+    for c in range(256):
+        v = t[c]
+        if math.isnan(v):
+            continue
+        if v == 0.0:
+            c = 0x00
+        by_val.setdefault(v, c)
+    vals = np.array(sorted(by_val), dtype=np.float64)
+    return vals, np.array([by_val[v] for v in vals], dtype=np.uint8)
+
+
+def fp8_round_up(x) -> np.ndarray:
+    """Code of the smallest finite E4M3 value >= x (saturating at 448)."""
+    vals, codes = _fp8_finite_sorted()
+    x = np.asarray(x, dtype=np.float64)
+    i = np.searchsorted(vals, x, side="left")
+    return codes[np.minimum(i, len(vals) - 1)]
+
+
+def fp8_round_down(x) -> np.ndarray:
+    """Code of the largest finite E4M3 value <= x (saturating at -448)."""
+    vals, codes = _fp8_finite_sorted()
+    x = np.asarray(x, dtype=np.float64)
+    i = np.searchsorted(vals, x, side="right") - 1
+    return codes[np.maximum(i, 0)]
+
+
+def widen_fp8(codes) -> np.ndarray:
+    """float64 values of E4M3 codes (uint8)."""
+    return fp8_e4m3_table()[np.asarray(codes, dtype=np.uint8)]
+
+
+def fp8_bounds(kmax: np.ndarray, kmin: np.ndarray):
+    """The 8-bit metadata of exact bounds: (codes of kmax rounded up, codes of
+    kmin rounded down), uint8 arrays of the input shapes."""
+    return fp8_round_up(kmax), fp8_round_down(kmin)
+
+
+# ---------------------------------------------------------------------------
 # Stage 3: selection
 
 
@@ -310,7 +397,8 @@ def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None):
 
     inp: dict of host arrays with keys q [B,Hq,D] f32, k_pool, v_pool,
     kv_dtype, page_table, seq_lens, page_size, scale (the fp32 value the
-    device uses), sink ([Hq] f32 or None).
+    device uses), sink ([Hq] f32 or None), and optionally meta_format
+    (FP8_E4M3: pages are scored on the 8-bit bounds).
     sel_override: attend over this page list instead of the selected one.
     Returns a dict with u, scores, sel, forced, taken, out [G,D], lse [G].
     """
@@ -321,6 +409,9 @@ def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None):
     n = num_pages(int(inp["seq_lens"][b]), ps)
     kmax, kmin = unit_page_meta(inp["k_pool"], inp["kv_dtype"], inp["page_table"],
                                 inp["seq_lens"], b, g, ps)
+    if inp.get("meta_format") == FP8_E4M3:  # the scan reads the 8-bit bounds
+        cmax, cmin = fp8_bounds(kmax, kmin)
+        kmax, kmin = widen_fp8(cmax), widen_fp8(cmin)
     qg = q[b, g * grp:(g + 1) * grp].astype(np.float64)
     u, s = unit_scores(qg, kmax, kmin)
     sel, forced, taken = select_pages(s, n, budget, n_sink, n_local)

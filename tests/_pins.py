@@ -259,3 +259,94 @@ def check_split_ranges(ref):
                 assert len(ranges) == ns
                 covered = [i for lo, hi in ranges for i in range(lo, hi)]
                 assert covered == list(range(total))
+
+
+# ---------------------------------------------------------------------------
+# 8-bit metadata bounds
+
+
+def check_fp8_decode(ref):
+    """The E4M3 value table against values fixed by the format's definition
+    and against torch's float8_e4m3fn decoding of every code (a library
+    routine); positive codes increase, and the sign bit only negates."""
+    t = ref.fp8_e4m3_table()
+    anchors = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+               0x39: 1.125, 0x40: 2.0, 0x77: 240.0, 0x7E: 448.0, 0x80: 0.0, 0xB8: -1.0,
+               0xFE: -448.0}
+    for c, v in anchors.items():
+        assert t[c] == v, (hex(c), t[c], v)
+    assert math.isnan(t[0x7F]) and math.isnan(t[0xFF])
+    lib = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    lib = lib.to(torch.float64).numpy()
+    np.testing.assert_array_equal(np.isnan(lib), np.isnan(t))
+    fin = ~np.isnan(t)
+    np.testing.assert_array_equal(lib[fin], t[fin])
+    assert np.all(np.diff(t[:0x7F]) > 0)
+    np.testing.assert_array_equal(t[0x80:0xFF], -t[:0x7F])
+
+
+def check_fp8_directed_rounding(ref, seed=3):
+    """Rounding up gives a value >= x and rounding down one <= x, with no
+    representable value strictly between (the two are adjacent); exact values
+    map to themselves; torch's round-to-nearest lands on one of the two; zero
+    is always code 0x00; magnitudes beyond 448 saturate."""
+    t = ref.fp8_e4m3_table()
+    fin = np.array([c for c in range(256) if not math.isnan(t[c])])
+    vals = np.unique(t[fin])
+    # exact values round to themselves, in both directions
+    for v in vals:
+        cu, cd = int(ref.fp8_round_up(v)), int(ref.fp8_round_down(v))
+        assert t[cu] == v and t[cd] == v
+        if v == 0.0:
+            assert cu == 0 and cd == 0
+    rng = np.random.default_rng(seed)
+    x = np.concatenate([rng.normal(0, 3, 4000), rng.normal(0, 0.01, 1000),
+                        rng.uniform(-448, 448, 1000), [1e-12, -1e-12, 2.0 ** -10, -2.0 ** -10,
+                                                       447.9, -447.9, 0.0, -0.0]])
+    up, dn = t[ref.fp8_round_up(x)], t[ref.fp8_round_down(x)]
+    assert np.all(up >= x) and np.all(dn <= x)
+    iu = np.searchsorted(vals, up)
+    idn = np.searchsorted(vals, dn)
+    assert np.all((iu == idn) | (iu == idn + 1))  # adjacent (or equal when exact)
+    assert np.all((up == dn) == np.isin(x, vals))
+    assert np.all(ref.fp8_round_up(-np.abs(x[np.abs(x) < 2.0 ** -10])) == 0)
+    assert np.all(ref.fp8_round_down(np.abs(x[np.abs(x) < 2.0 ** -10])) == 0)
+    xs = x[np.abs(x) <= 448]
+    rne = torch.tensor(xs, dtype=torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.all((rne == t[ref.fp8_round_up(xs)]) | (rne == t[ref.fp8_round_down(xs)]))
+    assert int(ref.fp8_round_up(500.0)) == 0x7E and int(ref.fp8_round_down(-500.0)) == 0xFE
+    assert int(ref.fp8_round_down(500.0)) == 0x7E and int(ref.fp8_round_up(-500.0)) == 0xFE
+
+
+def check_fp8_bound_admissible(ref, h):
+    """For every query head and page, the bound on the 8-bit metadata is >=
+    the bound on the exact metadata, which is >= every q.k in the page; on a
+    page whose keys are all exact 8-bit values the two bounds are equal."""
+    ps = h["page_size"]
+    hq, hkv = h["q"].shape[1], h["k_pool"].shape[1]
+    grp = hq // hkv
+    for b in range(h["page_table"].shape[0]):
+        for g in range(hkv):
+            kmax, kmin = ref.unit_page_meta(h["k_pool"], h["kv_dtype"], h["page_table"],
+                                            h["seq_lens"], b, g, ps)
+            cmax, cmin = ref.fp8_bounds(kmax, kmin)
+            qg = h["q"][b, g * grp:(g + 1) * grp].astype(np.float64)
+            u16, _ = ref.unit_scores(qg, kmax, kmin)
+            u8, _ = ref.unit_scores(qg, ref.widen_fp8(cmax), ref.widen_fp8(cmin))
+            assert np.all(u8 >= u16)
+            for p in range(kmax.shape[0]):
+                keys = ref.gather_tokens(h["k_pool"], h["kv_dtype"], h["page_table"],
+                                         h["seq_lens"], b, g, [p], ps)
+                assert np.all(u8[:, p] >= (qg @ keys.T).max(axis=1))
+    # keys on the 8-bit grid: the 8-bit metadata is exact
+    rng = np.random.default_rng(11)
+    t = ref.fp8_e4m3_table()
+    grid = t[[c for c in range(256) if not math.isnan(t[c]) and abs(t[c]) <= 8]]
+    keys = rng.choice(grid, size=(16, 32))
+    kmax, kmin = keys.max(0)[None], keys.min(0)[None]
+    cmax, cmin = ref.fp8_bounds(kmax, kmin)
+    np.testing.assert_array_equal(ref.widen_fp8(cmax), kmax)
+    np.testing.assert_array_equal(ref.widen_fp8(cmin), kmin)
+    q = rng.normal(size=(3, 32))
+    np.testing.assert_array_equal(ref.unit_scores(q, ref.widen_fp8(cmax), ref.widen_fp8(cmin))[0],
+                                  ref.unit_scores(q, kmax, kmin)[0])

@@ -15,7 +15,8 @@ import pytest
 
 import oracle as ref
 import workloads as wl
-from _pins import (check_dense_is_exact_attention, check_meta_bounds, check_restricted_reference,
+from _pins import (check_dense_is_exact_attention, check_fp8_bound_admissible, check_fp8_decode,
+                   check_fp8_directed_rounding, check_meta_bounds, check_restricted_reference,
                    check_score_admissible, check_score_closed_forms, check_selection_bruteforce,
                    check_selection_rank_count, check_sink, check_split_invariance,
                    check_split_ranges, small_inputs)
@@ -71,6 +72,33 @@ def test_score_admissible_tiny(tiny):
 
 def test_score_closed_forms():
     check_score_closed_forms(ref)
+
+
+def test_fp8_decode():
+    check_fp8_decode(ref)
+
+
+def test_fp8_directed_rounding():
+    check_fp8_directed_rounding(ref)
+
+
+def test_fp8_bound_admissible(small):
+    check_fp8_bound_admissible(ref, small[2])
+
+
+def test_fp8_unit_step_scores_the_8bit_bounds(small):
+    """With meta_format = FP8_E4M3 the step ranks pages by the bound on the
+    8-bit metadata; attention is unchanged for the same page list."""
+    w, _, h = small
+    h8 = dict(h, meta_format=ref.FP8_E4M3)
+    for b in range(w.batch):
+        for g in range(w.num_kv_heads):
+            r16 = ref.unit_step(h, b, g, w.budget_pages, w.n_sink, w.n_local)
+            r8 = ref.unit_step(h8, b, g, w.budget_pages, w.n_sink, w.n_local)
+            assert np.all(r8["u"] >= r16["u"])
+            r16b = ref.unit_step(h, b, g, w.budget_pages, w.n_sink, w.n_local,
+                                 sel_override=r8["sel"])
+            np.testing.assert_array_equal(r16b["out"], r8["out"])
 
 
 def test_score_single_token_page_is_tight():
@@ -317,3 +345,32 @@ def test_mutation_gather_ignores_page_table(monkeypatch, small):
     monkeypatch.setattr(ref.pagesparse_ref, "gather_tokens", bad)
     w, _, h = small
     _expect_fail(check_pool_permutation, h, w.budget_pages, w.n_sink, w.n_local)
+
+
+def test_mutation_fp8_round_to_nearest(monkeypatch):
+    t = ref.fp8_e4m3_table()
+
+    def nearest(x):
+        fin = np.array([c for c in range(256) if not math.isnan(t[c]) and c != 0x80])
+        x = np.asarray(x, dtype=np.float64)
+        return fin[np.abs(t[fin][None, :] - x.reshape(-1, 1)).argmin(1)].astype(np.uint8).reshape(
+            x.shape)
+    monkeypatch.setattr(ref.pagesparse_ref, "fp8_round_up", nearest)
+    _expect_fail(check_fp8_directed_rounding, ref.pagesparse_ref)
+
+
+def test_mutation_fp8_exponent_bias(monkeypatch):
+    orig = ref.pagesparse_ref.fp8_e4m3_value
+    monkeypatch.setattr(ref.pagesparse_ref, "fp8_e4m3_value", lambda c: 2.0 * orig(c))
+    _expect_fail(check_fp8_decode, ref.pagesparse_ref)
+
+
+def test_mutation_fp8_signed_zero_code(monkeypatch):
+    orig = ref.pagesparse_ref.fp8_round_up
+
+    def bad(x):
+        c = np.array(orig(x))
+        c[(c == 0) & (np.asarray(x) < 0)] = 0x80
+        return c
+    monkeypatch.setattr(ref.pagesparse_ref, "fp8_round_up", bad)
+    _expect_fail(check_fp8_directed_rounding, ref.pagesparse_ref)
