@@ -59,6 +59,23 @@ typedef enum {
   PS_BF16 = 1  /* bfloat16 (the high 16 bits of a binary32), RNE-rounded */
 } ps_dtype;
 
+/* Element type of the metadata pool.
+ *   PS_META_KV        kmax and kmin in kv_dtype (exact).
+ *   PS_META_FP8_E4M3  8-bit bounds, bf16 pools only: kmax rounded up and
+ *                     kmin rounded down to OCP E4M3 (no infinities; bias 7;
+ *                     largest finite 448), so for every query the bound can
+ *                     only grow and stays an upper bound of q.k. The page
+ *                     score then reads half the metadata bytes. A zero bound
+ *                     is code 0x00. Requires |K| <= 448: a larger magnitude
+ *                     saturates to 448 and its bound is no longer admissible.
+ *   ("Faster Than Flash: Exploiting Attention Sparsity for Efficient
+ *   Long-Context Decoding", section "Methodology", item 1: the scan that
+ *   decides which blocks to read runs on a low-bit copy of the cache.) */
+typedef enum {
+  PS_META_KV = 0,
+  PS_META_FP8_E4M3 = 1
+} ps_meta_format;
+
 /* Geometry shared by every call of one decode step.
  *   batch           B  >= 0 (0: validate, enqueue nothing, return PS_OK)
  *   num_q_heads     Hq >= 1, a multiple of num_kv_heads, with
@@ -68,7 +85,12 @@ typedef enum {
  *   page_size       tokens per page, 16
  *   max_pages       row stride of page_table; >= n_b for every request
  *   num_phys_pages  rows of the K, V and metadata pools (>= 1)
- *   kv_dtype        element type of K, V and the metadata            */
+ *   kv_dtype        element type of K and V
+ *   meta_format     element type of the metadata (ps_meta_format); entry
+ *                   points that do not read metadata ignore it. A value
+ *                   outside ps_meta_format is PS_ERR_SHAPE, and
+ *                   PS_META_FP8_E4M3 with fp32 pools PS_ERR_UNSUPPORTED, in
+ *                   every entry point                                    */
 typedef struct {
   int32_t batch;
   int32_t num_q_heads;
@@ -77,13 +99,15 @@ typedef struct {
   int32_t page_size;
   int32_t max_pages;
   int64_t num_phys_pages;
-  int32_t kv_dtype; /* ps_dtype */
-  int32_t reserved; /* must be 0 */
+  int32_t kv_dtype;    /* ps_dtype */
+  int32_t meta_format; /* ps_meta_format */
 } ps_geom;
 
 /* Array layouts (all contiguous, row-major):
  *   k_pool, v_pool [num_phys_pages, Hkv, page_size, D]    kv_dtype
- *   meta           [num_phys_pages, Hkv, 2, D]            kv_dtype; [..,0,:] = kmax, [..,1,:] = kmin
+ *   meta           [num_phys_pages, Hkv, 2, D]            kv_dtype (PS_META_KV) or uint8 codes
+ *                                                          (PS_META_FP8_E4M3); [..,0,:] = kmax,
+ *                                                          [..,1,:] = kmin
  *   page_table     [B, max_pages]  int32, logical page -> physical page; entries
  *                  at p >= n_b are ignored
  *   seq_lens       [B]             int32
@@ -105,7 +129,8 @@ typedef struct {
  * when page_begin is NULL):
  *   meta[page_table[b,p], g, 0, d] = max over the page's valid tokens t of K[t, d]
  *   meta[page_table[b,p], g, 1, d] = min over the same tokens.
- * The result is exact (a selection among stored values). Passing
+ * The result is exact (a selection among stored values); with
+ * PS_META_FP8_E4M3 it is kmax rounded up and kmin rounded down to E4M3. Passing
  * page_begin[b] = n_b - 1 and n_pages = 1 refreshes only the tail page, the
  * incremental update of a decode step. Other metadata rows are untouched.
  * n_pages >= 1 (use max_pages for a full build).
@@ -125,8 +150,9 @@ int ps_build_page_meta(const ps_geom* geom, const void* k_pool, const int32_t* p
  * group makes one page list per KV head admissible for all its heads.
  * Computed in fp32 as sum_d (max(q,0)*kmax_d + min(q,0)*kmin_d) with exact
  * products and a fixed summation order (bf16 metadata: on the matrix cores,
- * q split exactly into three bf16 terms; fp32 metadata: fma), so results are
- * bitwise reproducible; entries at p >= n_b are not written.
+ * q split exactly into three bf16 terms; fp32 metadata: fma; 8-bit metadata:
+ * widened exactly to bf16, then as bf16), so results are bitwise
+ * reproducible; entries at p >= n_b are not written.
  * Device preconditions: as ps_build_page_meta, with meta built for every
  * page read. */
 int ps_score_pages(const ps_geom* geom, const float* q, const void* meta,

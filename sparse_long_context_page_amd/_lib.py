@@ -36,6 +36,10 @@ ENTRY_POINTS = (
 )
 
 
+PS_META_KV = 0
+PS_META_FP8_E4M3 = 1
+
+
 class PsGeom(ctypes.Structure):
     _fields_ = [
         ("batch", ctypes.c_int32),
@@ -46,7 +50,7 @@ class PsGeom(ctypes.Structure):
         ("max_pages", ctypes.c_int32),
         ("num_phys_pages", ctypes.c_int64),
         ("kv_dtype", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("meta_format", ctypes.c_int32),
     ]
 
 

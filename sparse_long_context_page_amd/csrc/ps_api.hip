@@ -31,7 +31,7 @@ bool prod_ok(std::initializer_list<int64_t> xs, int64_t* out) {
 
 int check_geom(const ps_geom* g, ps::Shape* s) {
   if (!g) return PS_ERR_NULL;
-  if (g->reserved != 0) return PS_ERR_SHAPE;
+  if (g->meta_format != PS_META_KV && g->meta_format != PS_META_FP8_E4M3) return PS_ERR_SHAPE;
   if (g->batch < 0 || g->num_q_heads < 1 || g->num_kv_heads < 1 || g->head_dim < 1 ||
       g->page_size < 1 || g->max_pages < 1 || g->num_phys_pages < 1)
     return PS_ERR_SHAPE;
@@ -41,6 +41,7 @@ int check_geom(const ps_geom* g, ps::Shape* s) {
   if (g->head_dim != 64 && g->head_dim != 128) return PS_ERR_UNSUPPORTED;
   if (g->page_size != ps::kPage) return PS_ERR_UNSUPPORTED;
   if (g->kv_dtype != PS_F32 && g->kv_dtype != PS_BF16) return PS_ERR_UNSUPPORTED;
+  if (g->meta_format == PS_META_FP8_E4M3 && g->kv_dtype != PS_BF16) return PS_ERR_UNSUPPORTED;
   const int64_t elem = g->kv_dtype == PS_BF16 ? 2 : 4;
   int64_t t;
   // token positions p * page_size and page counts stay inside int32
@@ -61,6 +62,7 @@ int check_geom(const ps_geom* g, ps::Shape* s) {
   s->max_pages = g->max_pages;
   s->num_phys_pages = g->num_phys_pages;
   s->kv_bf16 = g->kv_dtype == PS_BF16;
+  s->meta8 = g->meta_format == PS_META_FP8_E4M3;
   return PS_OK;
 }
 
@@ -231,4 +233,4 @@ PS_API const char* ps_strerror(int status) {
   }
 }
 
-PS_API int ps_abi_version(void) { return (1 << 16) | 2; }  // 1.2: fused entry points
+PS_API int ps_abi_version(void) { return (1 << 16) | 3; }  // 1.3: 8-bit metadata

@@ -11,6 +11,7 @@ struct Shape {
   int batch, hq, hkv, group, head_dim, max_pages;
   int64_t num_phys_pages;
   int kv_bf16;  // 1: bf16 pools, 0: fp32 pools
+  int meta8;    // 1: 8-bit metadata bounds (bf16 pools only), 0: metadata in the pool dtype
 };
 
 hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int32_t* page_table,

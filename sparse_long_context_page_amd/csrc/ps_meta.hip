@@ -2,7 +2,9 @@
 // ("Don't read the haystack", section "Part two: the skipping".)
 //
 // One wavefront per (request, logical page, KV head) folds the page
-// (PageFold), and two lane groups write the kmax and kmin rows.
+// (PageFold), and two lane groups write the kmax and kmin rows: in the key
+// dtype, or as 8-bit codes with kmax rounded up and kmin rounded down
+// (fp8_e4m3_directed).
 #include "ps_launch.h"
 #include "ps_meta.h"
 
@@ -10,11 +12,11 @@ namespace ps {
 
 constexpr int kMetaWaves = 4;
 
-template <typename T, int D>
+template <typename T, int D, bool META8>
 __global__ __launch_bounds__(kMetaWaves * kWave) void build_page_meta_kernel(
     const T* __restrict__ k_pool, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_begin, int n_pages,
-    int batch, int hkv, int max_pages, int items_per_req, T* __restrict__ meta) {
+    int batch, int hkv, int max_pages, int items_per_req, void* __restrict__ meta) {
   using L = RowLayout<T, D>;
   constexpr int V = L::kVec;
   const int wave = threadIdx.x / kWave;
@@ -41,8 +43,13 @@ __global__ __launch_bounds__(kMetaWaves * kWave) void build_page_meta_kernel(
   float mx[V], mn[V];
   pf.fold(cnt, lane, mx, mn);
   if (r0 < 2) {
-    T* dst = meta + ((int64_t)phys * hkv + g) * 2 * D + r0 * D + c * V;
-    st16(dst, r0 == 0 ? pack(mx) : pack(mn));
+    const int64_t off = ((int64_t)phys * hkv + g) * 2 * D + r0 * D + c * V;
+    if constexpr (META8) {
+      *reinterpret_cast<uint2*>(static_cast<uint8_t*>(meta) + off) =
+          r0 == 0 ? fp8_pack8(mx, true) : fp8_pack8(mn, false);
+    } else {
+      st16(static_cast<T*>(meta) + off, r0 == 0 ? pack(mx) : pack(mn));
+    }
   }
 }
 
@@ -55,11 +62,21 @@ hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int3
   const int64_t blocks = (waves + kMetaWaves - 1) / kMetaWaves;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)blocks), block(kMetaWaves * kWave);
+  if (s.meta8) {  // bf16 keys only (checked by the caller)
+    if (s.head_dim == 64)
+      hipLaunchKernelGGL((build_page_meta_kernel<bf16_t, 64, true>), grid, block, 0, st,
+                         static_cast<const bf16_t*>(k_pool), page_table, seq_lens, page_begin,
+                         pages, s.batch, s.hkv, s.max_pages, items_per_req, meta);
+    else
+      hipLaunchKernelGGL((build_page_meta_kernel<bf16_t, 128, true>), grid, block, 0, st,
+                         static_cast<const bf16_t*>(k_pool), page_table, seq_lens, page_begin,
+                         pages, s.batch, s.hkv, s.max_pages, items_per_req, meta);
+    return hipGetLastError();
+  }
   PS_WITH_KV(s.kv_bf16, s.head_dim, {
-    hipLaunchKernelGGL((build_page_meta_kernel<TElem, kD>), grid, block, 0, st,
+    hipLaunchKernelGGL((build_page_meta_kernel<TElem, kD, false>), grid, block, 0, st,
                        static_cast<const TElem*>(k_pool), page_table, seq_lens, page_begin,
-                       pages, s.batch, s.hkv, s.max_pages, items_per_req,
-                       static_cast<TElem*>(meta));
+                       pages, s.batch, s.hkv, s.max_pages, items_per_req, meta);
   });
   return hipGetLastError();
 }

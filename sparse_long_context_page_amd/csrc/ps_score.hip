@@ -125,6 +125,11 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
 // its own slice of the queries in registers (no LDS, no barrier), reads its
 // table entries once up front, and keeps the metadata of the next two tiles
 // in flight while the current tile is scored.
+// META8: the metadata are 8-bit codes, widened exactly to bf16 in registers
+// before the same contraction. Each lane then takes one contiguous quarter
+// of the page's coordinates (block kb of lane group kgrp holds coordinates
+// kgrp*D/4 + kb*8 .. +8, the queries use the same assignment), so a lane
+// reads D/4 contiguous bytes per bound instead of 16-byte pieces D/4 apart.
 template <int N>
 __device__ __forceinline__ f32x4_t tree_sum(const f32x4_t (&a)[N]) {
   if constexpr (N == 1) {
@@ -152,13 +157,17 @@ constexpr int kMaxTiles = 16;  // 16-page tiles one wavefront streams at most
 // REFRESH: the wavefront holding a request's last page first rebuilds that
 // page's metadata from its keys (the page a decode step appends to), writes
 // it to meta_out and scores the page with it.
-template <int D, int G, bool REFRESH>
+template <int D, int G, bool REFRESH, bool META8>
 __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel(
-    const float* __restrict__ q, const bf16_t* __restrict__ meta,
+    const float* __restrict__ q, const void* __restrict__ meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
     int max_pages, int last_phys, int chunks_per_unit, int tiles_per_wave,
-    float* __restrict__ scores, const bf16_t* __restrict__ k_pool, bf16_t* meta_out) {
+    float* __restrict__ scores, const bf16_t* __restrict__ k_pool, void* meta_out) {
   constexpr int KB = D / 32;  // 32-coordinate blocks
+  constexpr int ML = META8 ? KB / 2 : KB;  // 16-byte metadata loads per bound per tile
+  constexpr int EB = META8 ? 1 : 2;        // bytes per metadata element
+  // first coordinate of the 8 a lane of group kgrp holds in block kb
+  auto coord = [](int kgrp_, int kb) { return META8 ? kgrp_ * (D / 4) + kb * 8 : kb * 32 + kgrp_ * 8; };
   static_assert(G <= 8, "group size");
   // the refreshed last page: kmax, kmin (one wavefront of a workgroup at most
   // holds a request's last page)
@@ -191,12 +200,12 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
 #pragma unroll
   for (int t = 0; t < kMaxTiles; ++t) phys[t] = row[min(p0 + t * 16 + col, max_pages - 1)];
   __builtin_amdgcn_sched_barrier(0);
-  const float* qh = q + ((int64_t)b * hkv * G + g * G + min(col, G - 1)) * D + kgrp * 8;
+  const float* qh = q + ((int64_t)b * hkv * G + g * G + min(col, G - 1)) * D;
   float4 qv[KB][2];
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
-    qv[kb][0] = *reinterpret_cast<const float4*>(qh + kb * 32);
-    qv[kb][1] = *reinterpret_cast<const float4*>(qh + kb * 32 + 4);
+    qv[kb][0] = *reinterpret_cast<const float4*>(qh + coord(kgrp, kb));
+    qv[kb][1] = *reinterpret_cast<const float4*>(qh + coord(kgrp, kb) + 4);
   }
   __builtin_amdgcn_sched_barrier(0);  // issue all of the above first
 
@@ -209,16 +218,19 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
 #pragma unroll
   for (int t = 0; t < kMaxTiles; ++t)
     phys[t] = p0 + t * 16 + col < np ? min(max(phys[t], 0), last_phys) : 0;
-  auto load = [&](int t, uint4 (&bx)[KB], uint4 (&bn)[KB]) {
-    const bf16_t* src = meta + ((int64_t)phys[t] * hkv + g) * 2 * D + kgrp * 8;
+  auto load = [&](int t, uint4 (&bx)[ML], uint4 (&bn)[ML]) {
+    const uint8_t* src = static_cast<const uint8_t*>(meta) +
+                         (((int64_t)phys[t] * hkv + g) * 2 * D + coord(kgrp, 0)) * EB;
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bx[kb] = ld16(src + kb * 32);
-      bn[kb] = ld16(src + D + kb * 32);
+    for (int i = 0; i < ML; ++i) {
+      // bf16: block i's 8 coordinates; 8-bit: blocks 2i and 2i+1
+      const int off = (META8 ? i * 16 : i * 32) * EB;
+      bx[i] = ld16(src + off);
+      bn[i] = ld16(src + D * EB + off);
     }
   };
   // Two tiles of metadata in flight, requested whatever the run's length.
-  uint4 xa[KB], na[KB], xb[KB], nb[KB];
+  uint4 xa[ML], na[ML], xb[ML], nb[ML];
   load(0, xa, na);
   load(1, xb, nb);
   // The last page's keys, when this wavefront holds it, behind its first
@@ -274,9 +286,16 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
     const int r0 = lane / LP::kLanesPerRow;
     const int c = lane % LP::kLanesPerRow;
     if (r0 < 2) {
-      const uint4 v = r0 == 0 ? pack(mx) : pack(mn);
-      st16(meta_out + ((int64_t)phys_tail * hkv + g) * 2 * D + r0 * D + c * 8, v);
-      *reinterpret_cast<uint4*>(&tail_lds[r0][c * 8]) = v;
+      const int64_t off = ((int64_t)phys_tail * hkv + g) * 2 * D + r0 * D + c * 8;
+      if constexpr (META8) {
+        const uint2 codes = r0 == 0 ? fp8_pack8(mx, true) : fp8_pack8(mn, false);
+        *reinterpret_cast<uint2*>(static_cast<uint8_t*>(meta_out) + off) = codes;
+        *reinterpret_cast<uint4*>(&tail_lds[r0][c * 8]) = fp8x8_to_bf16x8(codes.x, codes.y);
+      } else {
+        const uint4 v = r0 == 0 ? pack(mx) : pack(mn);
+        st16(static_cast<bf16_t*>(meta_out) + off, v);
+        *reinterpret_cast<uint4*>(&tail_lds[r0][c * 8]) = v;
+      }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -286,18 +305,25 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   // 3. per tile: one accumulator per (sign, 32-coordinate block), lo then mid
   // then hi, summed in a fixed tree; max over the group's heads
   float* out = scores + (int64_t)unit * max_pages;
-  auto score_tile = [&](int t, const uint4 (&bx_in)[KB], const uint4 (&bn_in)[KB], bool last) {
+  auto score_tile = [&](int t, const uint4 (&bx_in)[ML], const uint4 (&bn_in)[ML], bool last) {
     uint4 bx[KB], bn[KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      bx[kb] = bx_in[kb];
-      bn[kb] = bn_in[kb];
+    for (int i = 0; i < ML; ++i) {
+      if constexpr (META8) {
+        bx[2 * i] = fp8x8_to_bf16x8(bx_in[i].x, bx_in[i].y);
+        bx[2 * i + 1] = fp8x8_to_bf16x8(bx_in[i].z, bx_in[i].w);
+        bn[2 * i] = fp8x8_to_bf16x8(bn_in[i].x, bn_in[i].y);
+        bn[2 * i + 1] = fp8x8_to_bf16x8(bn_in[i].z, bn_in[i].w);
+      } else {
+        bx[i] = bx_in[i];
+        bn[i] = bn_in[i];
+      }
     }
     if (REFRESH && last && has_tail && col == col_tail) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        bx[kb] = *reinterpret_cast<const uint4*>(&tail_lds[0][kb * 32 + kgrp * 8]);
-        bn[kb] = *reinterpret_cast<const uint4*>(&tail_lds[1][kb * 32 + kgrp * 8]);
+        bx[kb] = *reinterpret_cast<const uint4*>(&tail_lds[0][coord(kgrp, kb)]);
+        bn[kb] = *reinterpret_cast<const uint4*>(&tail_lds[1][coord(kgrp, kb)]);
       }
     }
     f32x4_t acc[2 * KB];
@@ -359,20 +385,25 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
     const dim3 grid((unsigned)blocks);
     const int last_phys = (int)std::min<int64_t>(s.num_phys_pages - 1, 0x7fffffff);
     const bf16_t* kp = static_cast<const bf16_t*>(k_pool);
-    bf16_t* mo = static_cast<bf16_t*>(meta_out);
-#define PS_SCORE_MFMA(DD, RR)                                                                 \
-  hipLaunchKernelGGL((score_pages_mfma_kernel<DD, kG, RR>), grid, block, 0, st, q,            \
-                     static_cast<const bf16_t*>(meta), page_table, seq_lens, s.hkv,          \
-                     s.max_pages, last_phys, chunks, tpw, scores, kp, mo)
+#define PS_SCORE_MFMA(DD, RR, M8)                                                          \
+  hipLaunchKernelGGL((score_pages_mfma_kernel<DD, kG, RR, M8>), grid, block, 0, st, q, meta, \
+                     page_table, seq_lens, s.hkv, s.max_pages, last_phys, chunks, tpw,       \
+                     scores, kp, meta_out)
+#define PS_SCORE_MFMA_M(DD, RR)             \
+  do {                                      \
+    if (s.meta8) PS_SCORE_MFMA(DD, RR, true);  \
+    else PS_SCORE_MFMA(DD, RR, false);         \
+  } while (0)
     PS_WITH_GROUP(s.group, {
       if (s.head_dim == 64) {
-        if (kp) PS_SCORE_MFMA(64, true);
-        else PS_SCORE_MFMA(64, false);
+        if (kp) PS_SCORE_MFMA_M(64, true);
+        else PS_SCORE_MFMA_M(64, false);
       } else {
-        if (kp) PS_SCORE_MFMA(128, true);
-        else PS_SCORE_MFMA(128, false);
+        if (kp) PS_SCORE_MFMA_M(128, true);
+        else PS_SCORE_MFMA_M(128, false);
       }
     });
+#undef PS_SCORE_MFMA_M
 #undef PS_SCORE_MFMA
     return hipGetLastError();
   }

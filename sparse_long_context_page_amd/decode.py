@@ -121,6 +121,6 @@ class DecodeStep:
 def build_meta(geom: Geometry, k_pool, page_table, seq_lens, stream=None) -> torch.Tensor:
     """Allocate and fill the metadata pool for every mapped page."""
     meta = torch.empty((geom.num_phys_pages, geom.num_kv_heads, 2, geom.head_dim),
-                       device=k_pool.device, dtype=geom.kv_dtype)
+                       device=k_pool.device, dtype=geom.meta_dtype)
     ops.ps_build_page_meta(geom, k_pool, page_table, seq_lens, None, geom.max_pages, meta, stream)
     return meta

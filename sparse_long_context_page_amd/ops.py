@@ -18,6 +18,7 @@ import torch
 from . import _lib
 
 KV_DTYPES = {torch.bfloat16: _lib.PS_BF16, torch.float32: _lib.PS_F32}
+META_FORMATS = {"kv": _lib.PS_META_KV, "fp8": _lib.PS_META_FP8_E4M3}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -30,6 +31,12 @@ class Geometry:
     num_phys_pages: int
     kv_dtype: torch.dtype = torch.bfloat16
     page_size: int = 16
+    meta_format: str = "kv"  # "kv": metadata in kv_dtype; "fp8": 8-bit E4M3 bounds
+
+    @property
+    def meta_dtype(self) -> torch.dtype:
+        """torch dtype of the metadata pool (uint8 codes for "fp8")."""
+        return torch.uint8 if self.meta_format == "fp8" else self.kv_dtype
 
     @property
     def group(self) -> int:
@@ -38,17 +45,20 @@ class Geometry:
     def c(self) -> _lib.PsGeom:
         if self.kv_dtype not in KV_DTYPES:
             raise TypeError(f"unsupported kv dtype {self.kv_dtype}")
+        if self.meta_format not in META_FORMATS:
+            raise ValueError(f"unknown metadata format {self.meta_format!r}")
         return _lib.PsGeom(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
                            self.page_size, self.max_pages, self.num_phys_pages,
-                           KV_DTYPES[self.kv_dtype], 0)
+                           KV_DTYPES[self.kv_dtype], META_FORMATS[self.meta_format])
 
     @staticmethod
-    def of(q: torch.Tensor, k_pool: torch.Tensor, page_table: torch.Tensor) -> "Geometry":
+    def of(q: torch.Tensor, k_pool: torch.Tensor, page_table: torch.Tensor,
+           meta_format: str = "kv") -> "Geometry":
         b, hq, d = q.shape
         p_phys, hkv, ps, d2 = k_pool.shape
         if d2 != d or page_table.shape[0] != b:
             raise ValueError("q, k_pool and page_table disagree on batch or head_dim")
-        return Geometry(b, hq, hkv, d, page_table.shape[1], p_phys, k_pool.dtype, ps)
+        return Geometry(b, hq, hkv, d, page_table.shape[1], p_phys, k_pool.dtype, ps, meta_format)
 
 
 def _stream(stream) -> int:
@@ -91,7 +101,7 @@ def ps_build_page_meta(g: Geometry, k_pool, page_table, seq_lens, page_begin, n_
         _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
         _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
         _ptr(page_begin, "page_begin", torch.int32, (g.batch,), optional=True), int(n_pages),
-        _ptr(meta, "meta", g.kv_dtype, _meta_shape(g)), _stream(stream))
+        _ptr(meta, "meta", g.meta_dtype, _meta_shape(g)), _stream(stream))
     _lib.check("ps_build_page_meta", rc)
 
 
@@ -99,7 +109,7 @@ def ps_score_pages(g: Geometry, q, meta, page_table, seq_lens, scores, stream=No
     lib = _lib.load()
     rc = lib.ps_score_pages(
         g.c(), _ptr(q, "q", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
-        _ptr(meta, "meta", g.kv_dtype, _meta_shape(g)),
+        _ptr(meta, "meta", g.meta_dtype, _meta_shape(g)),
         _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
         _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
         _ptr(scores, "scores", torch.float32, (g.batch, g.num_kv_heads, g.max_pages)),
@@ -115,7 +125,7 @@ def ps_refresh_score_pages(g: Geometry, q, k_pool, meta, page_table, seq_lens, s
     rc = lib.ps_refresh_score_pages(
         g.c(), _ptr(q, "q", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
         _ptr(k_pool, "k_pool", g.kv_dtype, _pool_shape(g)),
-        _ptr(meta, "meta", g.kv_dtype, _meta_shape(g)),
+        _ptr(meta, "meta", g.meta_dtype, _meta_shape(g)),
         _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
         _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
         _ptr(scores, "scores", torch.float32, (g.batch, g.num_kv_heads, g.max_pages)),

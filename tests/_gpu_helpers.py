@@ -19,13 +19,14 @@ def gate(w) -> float:
     return BF16_GATE if w.kv_dtype == "bf16" else F32_GATE
 
 
-def geometry(inp) -> Geometry:
-    return Geometry.of(inp["q"], inp["k_pool"], inp["page_table"])
+def geometry(inp, meta_format="kv") -> Geometry:
+    return Geometry.of(inp["q"], inp["k_pool"], inp["page_table"], meta_format)
 
 
-def unit_host(inp, b, g):
+def unit_host(inp, b, g, meta_format="kv"):
     """Oracle view of one (request, KV head): the unit's pages gathered into a
-    compact host pool with an identity page table (plain torch indexing)."""
+    compact host pool with an identity page table (plain torch indexing).
+    meta_format "fp8": the oracle scores the 8-bit bounds."""
     w = inp["workload"]
     grp = w.group
     n = int(inp["n_pages_host"][b])
@@ -43,13 +44,15 @@ def unit_host(inp, b, g):
         "page_size": w.page_size,
         "scale": inp["scale"],
         "sink": sink,
+        "meta_format": ref.FP8_E4M3 if meta_format == "fp8" else None,
     }
 
 
-def run_step(inp, budget=None, n_splits=None, n_sink=None, n_local=None, sink="input"):
+def run_step(inp, budget=None, n_splits=None, n_sink=None, n_local=None, sink="input",
+             meta_format="kv"):
     """Metadata build + sparse step on the device; returns host copies."""
     w = inp["workload"]
-    g = geometry(inp)
+    g = geometry(inp, meta_format)
     budget = w.budget_pages if budget is None else budget
     step = DecodeStep(g, budget, w.n_sink if n_sink is None else n_sink,
                       w.n_local if n_local is None else n_local,

@@ -48,7 +48,8 @@ def test_abi_version_and_strerror():
 
 def geom(**kw):
     base = dict(batch=2, num_q_heads=12, num_kv_heads=2, head_dim=128, page_size=16,
-                max_pages=64, num_phys_pages=128, kv_dtype=_lib.PS_BF16, reserved=0)
+                max_pages=64, num_phys_pages=128, kv_dtype=_lib.PS_BF16,
+                meta_format=_lib.PS_META_KV)
     base.update(kw)
     return _lib.PsGeom(**base)
 
@@ -61,7 +62,9 @@ def score(g):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(reserved=1), _lib.PS_ERR_SHAPE),
+    (dict(meta_format=2), _lib.PS_ERR_SHAPE),
+    (dict(meta_format=-1), _lib.PS_ERR_SHAPE),
+    (dict(meta_format=_lib.PS_META_FP8_E4M3, kv_dtype=_lib.PS_F32), _lib.PS_ERR_UNSUPPORTED),
     (dict(batch=-1), _lib.PS_ERR_SHAPE),
     (dict(num_q_heads=0), _lib.PS_ERR_SHAPE),
     (dict(num_q_heads=13), _lib.PS_ERR_SHAPE),
@@ -82,6 +85,16 @@ def score(g):
 ])
 def test_geometry_validation(kw, code):
     assert score(geom(**kw)) == code
+
+
+def test_fp8_metadata_geometry_accepted():
+    """8-bit metadata with bf16 pools passes the geometry checks (a call with
+    batch 0 validates and enqueues nothing)."""
+    g = geom(meta_format=_lib.PS_META_FP8_E4M3, batch=0)
+    lib = _lib.load()
+    assert lib.ps_score_pages(g, X, X, X, X, X, None) == _lib.PS_OK
+    assert lib.ps_build_page_meta(g, X, X, X, None, 4, X, None) == _lib.PS_OK
+    assert lib.ps_refresh_score_pages(g, X, X, X, X, X, X, None) == _lib.PS_OK
 
 
 def test_null_geometry():
