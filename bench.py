@@ -18,6 +18,10 @@ Printed: one JSON line with the step time (us per decode step), effective
 HBM bandwidth on algorithmic bytes, the score kernel's roofline (the kernel
 that moves the most bytes), per-kernel times, the in-house dense decode's
 step time and the speedup over it, and the oracle timed on host cores.
+With the default bf16 metadata the same inputs are also run with 8-bit
+metadata bounds (--meta-format fp8 makes that the timed step): its step
+time, score-launch time and parity against the oracle on the 8-bit bounds
+are reported under "metadata_fp8".
 """
 
 from __future__ import annotations
@@ -54,6 +58,10 @@ def parse():
     ap.add_argument("--dense-splits", type=int, default=None,
                     help="override the dense split count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--meta-format", default="kv", choices=("kv", "fp8"),
+                    help="page metadata: in the key dtype (kv) or 8-bit E4M3 bounds (fp8)")
+    ap.add_argument("--no-fp8-line", action="store_true",
+                    help="skip the 8-bit metadata measurement of a default run")
     ap.add_argument("--only-kernel", default=None,
                     help="profiling aid: after setup, launch only this stage --steps times "
                          "(score | step | copy: a 1 GiB device-to-device copy)")
@@ -64,15 +72,16 @@ def parse():
 # setup
 
 
-def make_set(w, seed, torch, wl, ps):
-    inp = wl.make_inputs(w, device="cuda", seed=seed)
-    g = ps.Geometry.of(inp["q"], inp["k_pool"], inp["page_table"])
+def make_set(w, seed, torch, wl, ps, meta_format="kv", inp=None):
+    inp = wl.make_inputs(w, device="cuda", seed=seed) if inp is None else inp
+    g = ps.Geometry.of(inp["q"], inp["k_pool"], inp["page_table"], meta_format)
     meta = ps.build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
     step = ps.DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
                          inp["scale"])
     tail = torch.tensor([int(n) - 1 for n in inp["n_pages_host"]], device="cuda",
                         dtype=torch.int32)
-    return {"inp": inp, "g": g, "meta": meta, "step": step, "tail": tail}
+    return {"inp": inp, "g": g, "meta": meta, "step": step, "tail": tail,
+            "meta_format": meta_format}
 
 
 def run_sparse_step(s):
@@ -108,7 +117,7 @@ def capture(fn, s, torch):
 # oracle views (host copies of one (request, KV head) unit)
 
 
-def unit_host(inp, b, g, wl):
+def unit_host(inp, b, g, wl, meta_format="kv"):
     w = inp["workload"]
     grp = w.group
     n = int(inp["n_pages_host"][b])
@@ -125,6 +134,7 @@ def unit_host(inp, b, g, wl):
         "page_size": w.page_size,
         "scale": inp["scale"],
         "sink": sink,
+        "meta_format": "fp8_e4m3" if meta_format == "fp8" else None,
     }
 
 
@@ -150,7 +160,7 @@ def parity_gate(s, w, units, wl):
     out = step.out.cpu().double().numpy()
     worst, n_amb, n_diff = 0.0, 0, 0
     for b, g in units:
-        hu = unit_host(inp, b, g, wl)
+        hu = unit_host(inp, b, g, wl, s["meta_format"])
         r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local)
         k = min(w.budget_pages, r["n"])
         if int(cnt[b, g]) != k:
@@ -271,7 +281,10 @@ def main():
     if args.dense_splits:
         w = w.replace(dense_splits=args.dense_splits)
     print(f"# setup {w.name}: {args.sets} input sets", file=sys.stderr, flush=True)
-    sets = [make_set(w, w.seed + 17 * i, torch, wl, ps) for i in range(args.sets)]
+    sets = [make_set(w, w.seed + 17 * i, torch, wl, ps, args.meta_format)
+            for i in range(args.sets)]
+    if args.meta_format == "fp8" and w.kv_dtype != "bf16":
+        raise SystemExit("8-bit metadata needs bf16 K/V")
     torch.cuda.synchronize()
 
     # -- parity gate on set 0 (eager) --------------------------------------
@@ -461,7 +474,8 @@ def main():
     inp0 = s0["inp"]
     lens = [int(x) for x in inp0["seq_lens_host"]]
     elem = 2 if w.kv_dtype == "bf16" else 4
-    meta_b = acc.meta_bytes(lens, w.num_kv_heads, w.head_dim, elem, w.page_size)
+    meta_elem = 1 if args.meta_format == "fp8" else elem
+    meta_b = acc.meta_bytes(lens, w.num_kv_heads, w.head_dim, meta_elem, w.page_size)
     run_sparse_step(s0)
     torch.cuda.synchronize()
     sel_h = s0["step"].sel.cpu().numpy()
@@ -477,14 +491,14 @@ def main():
     # read and its metadata written
     units = w.batch * w.num_kv_heads
     scores_b = sum(-(-n // w.page_size) for n in lens) * w.num_kv_heads * 4
-    tail_b = units * (w.page_size + 2) * w.head_dim * elem if fused else 0
+    tail_b = (units * (w.page_size * elem + 2 * meta_elem) * w.head_dim) if fused else 0
     dom_key = "refresh_score" if fused else "score"
     dom_b = meta_b + scores_b + tail_b
     score_gbps = dom_b / (kern_us[dom_key] * 1e-6) / 1e9
     dec_key = "select_decode" if fused else "sparse_decode"
     decode_gbps = kv_b / (kern_us[dec_key] * 1e-6) / 1e9
 
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(w.name + ("_fp8meta" if args.meta_format == "fp8" else ""))
     result = {
         "metric": METRIC,
         "value": round(step_us, 3),
@@ -503,7 +517,8 @@ def main():
                    "context": w.context if w.context else list(w.ctx_range),
                    "page_size": w.page_size, "budget_pages": w.budget_pages,
                    "n_sink_pages": w.n_sink, "n_local_pages": w.n_local, "needles": w.needles,
-                   "kv_storage": w.kv_dtype, "n_splits": w.n_splits, "input_sets": len(sets),
+                   "kv_storage": w.kv_dtype, "metadata": args.meta_format,
+                   "n_splits": w.n_splits, "input_sets": len(sets),
                    "path": path,
                    "graph_captured": f"{len(sets)} steps (one per input set) per graph"},
         "effective_hbm_gbps": round(eff_gbps, 1),
@@ -537,10 +552,81 @@ def main():
                      "algorithmic_bytes_per_launch": dom_b,
                      "avg_launch_us": round(kern_us[dom_key], 3)},
     }
+    if args.meta_format == "kv" and w.kv_dtype == "bf16" and not args.no_fp8_line:
+        print("# 8-bit metadata", file=sys.stderr, flush=True)
+        result["metadata_fp8"] = fp8_line(args, w, sets, step_us, torch, wl, ps, acc)
     if not args.no_cpu_baseline:
         print("# cpu baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(s0, w, sample_units(w, args.cpu_units), wl)
     print(json.dumps(result), flush=True)
+
+
+def fp8_line(args, w, sets, step_us_kv, torch, wl, ps, acc):
+    """The same inputs with 8-bit metadata bounds: parity against the oracle
+    scoring the 8-bit bounds, then the step timed as the main one (one graph
+    of one step per input set) and the refresh+score launch on its own."""
+    sets8 = [make_set(w, None, torch, wl, ps, "fp8", inp=s["inp"]) for s in sets]
+    run_sparse_step(sets8[0])
+    torch.cuda.synchronize()
+    parity = parity_gate(sets8[0], w, sample_units(w, args.parity_units), wl)
+
+    def all_sets(_):
+        for s in sets8:
+            run_sparse_step(s)
+    multi = capture(all_sets, None, torch)
+    for _ in range(3):
+        multi.replay()
+    torch.cuda.synchronize()
+    reps = max(args.steps // len(sets8), 1)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        multi.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) / (reps * len(sets8)) * 1e3
+
+    n_k = 40
+
+    def batch(_):
+        for i in range(n_k):
+            s = sets8[i % len(sets8)]
+            inp = s["inp"]
+            ps.ps_refresh_score_pages(s["g"], inp["q"], inp["k_pool"], s["meta"],
+                                      inp["page_table"], inp["seq_lens"], s["step"].scores)
+    gk = capture(batch, None, torch)
+    gk.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        gk.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    score_us = e0.elapsed_time(e1) / (reps * n_k) * 1e3
+    for s in sets8:  # leave the pools as whole steps leave them
+        run_sparse_step(s)
+    torch.cuda.synchronize()
+
+    lens = [int(x) for x in sets8[0]["inp"]["seq_lens_host"]]
+    meta_b = acc.meta_bytes(lens, w.num_kv_heads, w.head_dim, 1, w.page_size)
+    units = w.batch * w.num_kv_heads
+    scores_b = sum(-(-n // w.page_size) for n in lens) * w.num_kv_heads * 4
+    dom_b = meta_b + scores_b + units * (w.page_size * 2 + 2) * w.head_dim
+    sel_h = sets8[0]["step"].sel.cpu().numpy()
+    lists = {(b, g): list(sel_h[b, g]) for b in range(w.batch) for g in range(w.num_kv_heads)}
+    kv_b = acc.selected_kv_bytes(lens, lists, w.head_dim, 2, w.page_size)
+    del sets8
+    gbps = dom_b / (score_us * 1e-6) / 1e9
+    return {"us_per_step": round(step_us, 3),
+            "speedup_vs_bf16_metadata": round(step_us_kv / step_us, 3),
+            "touched_bytes": meta_b + kv_b,
+            "effective_hbm_gbps": round((meta_b + kv_b) / (step_us * 1e-6) / 1e9, 1),
+            "refresh_score_us": round(score_us, 3),
+            "refresh_score_gbps": round(gbps, 1),
+            "refresh_score_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+            "refresh_score_algorithmic_bytes": dom_b,
+            "parity": dict(parity, oracle="scores on the 8-bit bounds")}
 
 
 def profile_only(args, sets, torch, ps):
