@@ -25,6 +25,9 @@ from .pagesparse_ref import (  # noqa: F401
     widen_fp8,
     fp8_bounds,
     select_pages,
+    pseudo_max,
+    select_pages_topdelta,
+    ambiguous_pages_topdelta,
     ambiguous_pages,
     gather_tokens,
     attend,

@@ -304,6 +304,84 @@ def ambiguous_pages(scores, n, budget, n_sink, n_local, rel=AMBIGUITY_REL):
 
 
 # ---------------------------------------------------------------------------
+# Stage 3 variant: top-delta threshold selection
+#
+# "Faster Than Flash: Exploiting Attention Sparsity for Efficient Long-Context
+# Decoding", section "Methodology", item 2 (Top-delta selection criterion),
+# eq. (1)-(3) and section "Pseudo-Max Robustness as Fail-Safe": a block is
+# kept when its logit is at least the row maximum minus delta; the maximum is
+# replaced by a pseudo-max taken over the sink and local tokens only, which is
+# never larger, so the kept set can only grow. Readings for a page list
+# shared by a group of query heads, scored by the page bound:
+# * the pseudo-max of head h is the largest scale*q_h.k_t over the valid
+#   tokens of the forced pages (the first n_sink and last n_local pages); with
+#   no forced page there is no pseudo-max and the threshold is -inf;
+# * the group threshold is the smallest of its heads' pseudo-maxima minus
+#   delta, so that the list keeps, for every head, every page the per-head
+#   criterion would keep;
+# * a page passes when scale*S(p) >= threshold (S the group's bound, which is
+#   >= every q_h.k_t of the page), so every token passing the criterion with
+#   the true maximum lies on a kept page;
+# * the count is capped at the budget to stay graph-capturable: the forced
+#   pages and then the passing pages by decreasing score (ties to the lower
+#   page), at most budget - |forced| of them.
+
+
+def pseudo_max(q_group: np.ndarray, keys_forced: np.ndarray, scale: float) -> np.ndarray:
+    """Per query head, max over the forced tokens of scale * q_h . k_t
+    ([FFD] eq. (3)); -inf for every head when there is no forced token."""
+    q = np.asarray(q_group, dtype=np.float64)
+    if keys_forced.shape[0] == 0:
+        return np.full(q.shape[0], -np.inf)
+    return (float(scale) * (q @ np.asarray(keys_forced, dtype=np.float64).T)).max(axis=1)
+
+
+def select_pages_topdelta(scores, n, budget, n_sink, n_local, scale, m_tilde, delta):
+    """Kept pages of one (request, KV head) under the top-delta criterion.
+
+    Returns (sel ascending, forced, taken in the order taken, threshold).
+    With budget >= n every page is kept (threshold None).
+    """
+    if budget >= n:
+        return np.arange(n, dtype=np.int64), list(range(n)), [], None
+    forced = _forced(n, n_sink, n_local)
+    r = budget - len(forced)
+    if r < 0:
+        raise ValueError("forced pages exceed the budget")
+    tau = float(np.min(m_tilde)) - float(delta) if len(forced) else -math.inf
+    fset = set(forced)
+    s = np.asarray(scores, dtype=np.float64)
+    cand = np.array([p for p in range(n) if p not in fset and float(scale) * s[p] >= tau],
+                    dtype=np.int64)
+    order = np.lexsort((cand, -s[cand])) if len(cand) else np.array([], dtype=np.int64)
+    taken = [int(p) for p in cand[order[:r]]]
+    sel = np.array(sorted(fset | set(taken)), dtype=np.int64)
+    return sel, forced, taken, tau
+
+
+def ambiguous_pages_topdelta(scores, n, budget, n_sink, n_local, scale, m_tilde, delta,
+                             rel=AMBIGUITY_REL):
+    """Pages an fp32 device may decide differently: scaled scores within
+    rel of the threshold (it is itself an fp32 result on the device), and,
+    when the cap binds, scores within rel of the last taken one."""
+    sel, forced, taken, tau = select_pages_topdelta(scores, n, budget, n_sink, n_local, scale,
+                                                    m_tilde, delta)
+    if tau is None:
+        return set()
+    s = np.asarray(scores, dtype=np.float64)
+    fset = set(forced)
+    amb = set()
+    if math.isfinite(tau):
+        amb |= {p for p in range(n) if p not in fset and
+                abs(float(scale) * s[p] - tau) <= rel * max(abs(tau), 1.0)}
+    r = budget - len(forced)
+    if taken and len(taken) == r:
+        s_k = float(s[taken[-1]])
+        amb |= {p for p in range(n) if p not in fset and abs(s[p] - s_k) <= rel * abs(s_k)}
+    return amb
+
+
+# ---------------------------------------------------------------------------
 # Stage 4: attention over the kept tokens
 
 
@@ -392,7 +470,7 @@ def dense_split_pages(n: int, n_splits: int):
 # Whole step
 
 
-def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None):
+def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None, delta=None):
     """Score, select and attend for one (request b, KV head g).
 
     inp: dict of host arrays with keys q [B,Hq,D] f32, k_pool, v_pool,
@@ -400,6 +478,7 @@ def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None):
     device uses), sink ([Hq] f32 or None), and optionally meta_format
     (FP8_E4M3: pages are scored on the 8-bit bounds).
     sel_override: attend over this page list instead of the selected one.
+    delta: select by the top-delta criterion with this delta (None: top-k).
     Returns a dict with u, scores, sel, forced, taken, out [G,D], lse [G].
     """
     q = inp["q"]
@@ -414,7 +493,16 @@ def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None):
         kmax, kmin = widen_fp8(cmax), widen_fp8(cmin)
     qg = q[b, g * grp:(g + 1) * grp].astype(np.float64)
     u, s = unit_scores(qg, kmax, kmin)
-    sel, forced, taken = select_pages(s, n, budget, n_sink, n_local)
+    tau = None
+    if delta is None:
+        sel, forced, taken = select_pages(s, n, budget, n_sink, n_local)
+    else:  # top-delta: the pseudo-max over the forced pages' tokens
+        fpages = _forced(n, n_sink, n_local) if budget < n else []
+        kf = gather_tokens(inp["k_pool"], inp["kv_dtype"], inp["page_table"], inp["seq_lens"],
+                           b, g, fpages, ps)
+        m_tilde = pseudo_max(qg, kf, inp["scale"])
+        sel, forced, taken, tau = select_pages_topdelta(s, n, budget, n_sink, n_local,
+                                                        inp["scale"], m_tilde, delta)
     pages = sel if sel_override is None else np.asarray(sel_override, dtype=np.int64)
     keys = gather_tokens(inp["k_pool"], inp["kv_dtype"], inp["page_table"], inp["seq_lens"],
                          b, g, pages, ps)
@@ -428,7 +516,7 @@ def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None):
         outs.append(o)
         lses.append(l)
     return {"u": u, "scores": s, "sel": sel, "forced": forced, "taken": taken,
-            "out": np.stack(outs), "lse": np.array(lses), "n": n}
+            "out": np.stack(outs), "lse": np.array(lses), "n": n, "tau": tau}
 
 
 def decode_step(inp, budget, n_sink, n_local, units=None):

@@ -350,3 +350,107 @@ def check_fp8_bound_admissible(ref, h):
     q = rng.normal(size=(3, 32))
     np.testing.assert_array_equal(ref.unit_scores(q, ref.widen_fp8(cmax), ref.widen_fp8(cmin))[0],
                                   ref.unit_scores(q, kmax, kmin)[0])
+
+
+# ---------------------------------------------------------------------------
+# top-delta threshold selection
+
+
+def tight_small_inputs(group=1, **kw):
+    """Small inputs whose page bounds are tight (wl.tighten_pages), with a
+    sink page and two local pages, where the top-delta threshold keeps fewer
+    pages than the budget in several units (group 1: seed 7, centres N(0, 4);
+    group 2: seed 8, centres N(0, 2.25))."""
+    base = dict(num_q_heads=2 * group, batch=4, n_sink=1, n_local=2, budget_pages=9, needles=0,
+                ctx_range=(200, 400), max_pages=26, seed=7 if group == 1 else 8)
+    base.update(kw)
+    w, inp, _ = small_inputs(**base)
+    wl.tighten_pages(inp, center_std=2.0 if group == 1 else 1.5)
+    return w, inp, wl.host_inputs(inp)
+
+
+def _unit_arrays(ref, h, b, g):
+    ps = h["page_size"]
+    hq, hkv = h["q"].shape[1], h["k_pool"].shape[1]
+    grp = hq // hkv
+    n = ref.num_pages(int(h["seq_lens"][b]), ps)
+    kmax, kmin = ref.unit_page_meta(h["k_pool"], h["kv_dtype"], h["page_table"], h["seq_lens"],
+                                    b, g, ps)
+    qg = h["q"][b, g * grp:(g + 1) * grp].astype(np.float64)
+    _, s = ref.unit_scores(qg, kmax, kmin)
+    keys = [ref.gather_tokens(h["k_pool"], h["kv_dtype"], h["page_table"], h["seq_lens"], b, g,
+                              [p], ps) for p in range(n)]
+    return n, qg, s, keys
+
+
+def check_topdelta(ref, h, w, deltas=(0.0, 0.3, 1.0, 3.0)):
+    """[FFD] eq. (1)-(3) and its fail-safe: with the cap not binding, every
+    token whose logit is within delta of its head's TRUE maximum lies on a
+    kept page; the pseudo-max never exceeds the true maximum and equals
+    torch's product over the forced tokens; kept sets grow with delta; the
+    passing pages are exactly those with scale*S >= min pseudo-max - delta
+    (found by a direct scan); delta = inf gives the top-k selection; and the
+    cap keeps the best passing pages (rank counting)."""
+    scale = h["scale"]
+    bound_binds = 0
+    for b in range(h["page_table"].shape[0]):
+        for g in range(h["k_pool"].shape[1]):
+            n, qg, s, keys = _unit_arrays(ref, h, b, g)
+            forced = sorted(set(range(min(w.n_sink, n))) | set(range(max(0, n - w.n_local), n)))
+            kf = np.concatenate([keys[p] for p in forced]) if forced else np.zeros((0, qg.shape[1]))
+            mt = ref.pseudo_max(qg, kf, scale)
+            allk = np.concatenate(keys)
+            true_max = (scale * (qg @ allk.T)).max(axis=1)
+            assert np.all(mt <= true_max)
+            if forced:
+                lib = (scale * torch.from_numpy(qg) @ torch.from_numpy(kf).T).max(dim=1).values
+                np.testing.assert_allclose(mt, lib.numpy(), rtol=1e-12, atol=0)
+            prev = None
+            for d in deltas:
+                for budget in (w.budget_pages, n - 1, n + 3):
+                    sel, fo, taken, tau = ref.select_pages_topdelta(s, n, budget, w.n_sink,
+                                                                    w.n_local, scale, mt, d)
+                    if budget >= n:
+                        assert list(sel) == list(range(n))
+                        continue
+                    assert set(fo) <= set(int(p) for p in sel)
+                    passing = [p for p in range(n) if p not in fo and scale * s[p] >= tau]
+                    r = budget - len(fo)
+                    if len(passing) <= r:  # cap not binding: exactly the passing pages
+                        assert set(int(p) for p in sel) == set(fo) | set(passing)
+                        for hh in range(qg.shape[0]):
+                            for p in range(n):
+                                if (scale * (qg[hh] @ keys[p].T)).max() >= true_max[hh] - d:
+                                    assert p in set(int(x) for x in sel), (b, g, hh, p, d)
+                    else:  # cap binds: the r best passing pages (rank counting)
+                        bound_binds += 1
+                        for p in passing:
+                            better = sum(1 for o in passing
+                                         if s[o] > s[p] or (s[o] == s[p] and o < p))
+                            assert (p in set(int(x) for x in sel)) == (better < r)
+                    if budget == n - 1:
+                        cur = set(int(x) for x in sel)
+                        if prev is not None and len(taken) < r:
+                            assert prev <= cur
+                        prev = cur if len(taken) < r else None
+            # delta = inf is the top-k selection
+            for budget in (w.budget_pages, n - 1):
+                a, _, _, _ = ref.select_pages_topdelta(s, n, budget, w.n_sink, w.n_local, scale,
+                                                       mt, math.inf)
+                bsel, _, _ = ref.select_pages(s, n, budget, w.n_sink, w.n_local)
+                assert list(a) == list(bsel)
+    return bound_binds
+
+
+def check_topdelta_no_forced_is_topk(ref, h, w):
+    """With no sink or local page there is no pseudo-max: top-delta keeps
+    the top-k pages whatever delta is."""
+    for b in range(h["page_table"].shape[0]):
+        for g in range(h["k_pool"].shape[1]):
+            n, qg, s, _ = _unit_arrays(ref, h, b, g)
+            mt = ref.pseudo_max(qg, np.zeros((0, qg.shape[1])), h["scale"])
+            for budget in (2, 5):
+                a, _, _, tau = ref.select_pages_topdelta(s, n, budget, 0, 0, h["scale"], mt, 0.0)
+                bsel, _, _ = ref.select_pages(s, n, budget, 0, 0)
+                assert list(a) == list(bsel)
+                assert budget >= n or tau == -math.inf

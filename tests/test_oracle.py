@@ -16,6 +16,7 @@ import pytest
 import oracle as ref
 import workloads as wl
 from _pins import (check_dense_is_exact_attention, check_fp8_bound_admissible, check_fp8_decode,
+                   check_topdelta, check_topdelta_no_forced_is_topk, tight_small_inputs,
                    check_fp8_directed_rounding, check_meta_bounds, check_restricted_reference,
                    check_score_admissible, check_score_closed_forms, check_selection_bruteforce,
                    check_selection_rank_count, check_sink, check_split_invariance,
@@ -72,6 +73,31 @@ def test_score_admissible_tiny(tiny):
 
 def test_score_closed_forms():
     check_score_closed_forms(ref)
+
+
+@pytest.mark.parametrize("group", [1, 2])
+def test_topdelta_selection(group):
+    w, _, h = tight_small_inputs(group)
+    binds = check_topdelta(ref, h, w)
+    assert binds > 0  # some cases exercise the cap
+
+
+@pytest.mark.parametrize("group", [1, 2])
+def test_topdelta_threshold_separates_tight_pages(group):
+    """On tight pages the threshold keeps fewer pages than the budget for
+    some units (the criterion is exercised, not only the cap)."""
+    w, _, h = tight_small_inputs(group)
+    fewer = 0
+    for b in range(w.batch):
+        for g in range(w.num_kv_heads):
+            r = ref.unit_step(h, b, g, w.budget_pages, w.n_sink, w.n_local, delta=0.3)
+            fewer += len(r["sel"]) < min(w.budget_pages, r["n"])
+    assert fewer > 0
+
+
+def test_topdelta_no_forced_is_topk():
+    w, _, h = tight_small_inputs()
+    check_topdelta_no_forced_is_topk(ref, h, w)
 
 
 def test_fp8_decode():
@@ -374,3 +400,24 @@ def test_mutation_fp8_signed_zero_code(monkeypatch):
         return c
     monkeypatch.setattr(ref.pagesparse_ref, "fp8_round_up", bad)
     _expect_fail(check_fp8_directed_rounding, ref.pagesparse_ref)
+
+
+def test_mutation_topdelta_max_over_heads(monkeypatch):
+    """Taking the largest pseudo-max of the group (instead of the smallest)
+    drops pages some head needs."""
+    orig = ref.pagesparse_ref.select_pages_topdelta
+
+    def bad(scores, n, budget, n_sink, n_local, scale, m_tilde, delta):
+        return orig(scores, n, budget, n_sink, n_local, scale,
+                    np.full_like(m_tilde, np.max(m_tilde)), delta)
+    monkeypatch.setattr(ref.pagesparse_ref, "select_pages_topdelta", bad)
+    w, _, h = tight_small_inputs(2)
+    _expect_fail(check_topdelta, ref.pagesparse_ref, h, w)
+
+
+def test_mutation_topdelta_unscaled_bound(monkeypatch):
+    orig = ref.pagesparse_ref.select_pages_topdelta
+    monkeypatch.setattr(ref.pagesparse_ref, "select_pages_topdelta",
+                        lambda s, n, bu, ns, nl, sc, mt, d: orig(s, n, bu, ns, nl, 1.0, mt, d))
+    w, _, h = tight_small_inputs()
+    _expect_fail(check_topdelta, ref.pagesparse_ref, h, w)

@@ -203,6 +203,22 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None):
     }
 
 
+def tighten_pages(inp, spread: float = 0.05, center_std: float = 0.6, seed: int = 77):
+    """Replace the keys of every physical page by a per-(page, KV head) centre
+    drawn N(0, center_std^2) plus N(0, spread^2) noise per token, in place,
+    keeping the sentinel of unused slots. The page bounds then sit close to
+    the keys, so a threshold on them separates pages (used by the threshold
+    selection tests; input drawing only)."""
+    k = inp["k_pool"]
+    gen = torch.Generator(device=k.device).manual_seed(seed)
+    p, h, t, d = k.shape
+    centre = torch.randn((p, h, 1, d), generator=gen, device=k.device) * center_std
+    noise = torch.randn((p, h, t, d), generator=gen, device=k.device) * spread
+    keep = k == SENTINEL
+    k.copy_(torch.where(keep, k, (centre + noise).to(k.dtype)))
+    return inp
+
+
 def kv_bits_numpy(t: torch.Tensor) -> np.ndarray:
     """Host copy of a K/V/meta tensor as the oracle takes it (bf16 as uint16 bits)."""
     t = t.detach().cpu().contiguous()
