@@ -7,6 +7,7 @@
  *   1. ps_build_page_meta  per-page elementwise key max/min   (metadata)
  *   2. ps_score_pages      per-page upper bound of q.k         (page score)
  *   3. ps_select_topk      forced pages + top-k per KV head    (selection)
+ *      ps_select_topdelta  the same, kept pages also above a threshold
  *   4. ps_sparse_decode    split-KV softmax partials over the kept pages
  *      ps_full_decode      the same over every page            (dense twin)
  *   5. ps_combine          log-sum-exp merge of the partials + optional sink
@@ -191,6 +192,32 @@ int ps_refresh_score_pages(const ps_geom* geom, const float* q, const void* k_po
 int ps_select_topk(const ps_geom* geom, const float* scores, const int32_t* seq_lens,
                    int32_t budget_pages, int32_t n_sink_pages, int32_t n_local_pages,
                    int32_t* sel, int32_t* sel_count, void* stream);
+
+/* 3'. Top-delta selection. ("Faster Than Flash: Exploiting Attention
+ * Sparsity for Efficient Long-Context Decoding", section "Methodology", item
+ * 2, eq. (1)-(3): a block is kept when its logit is at least the maximum
+ * minus delta, the maximum replaced by a pseudo-max over the sink and local
+ * tokens; "Pseudo-Max Robustness as Fail-Safe": the pseudo-max is never
+ * larger, so the kept set only grows.) For every (b, g) with n = n_b:
+ *   if budget_pages >= n: every page 0..n-1 is kept (as ps_select_topk);
+ *   else, with F the first n_sink_pages and last n_local_pages pages,
+ *     m_h = max over the valid tokens t of the pages of F of
+ *           scale * q[b,h,:] . K[t, g, :]   for each query head h of g,
+ *     tau = min_h m_h - delta  (-infinity when F is empty),
+ *   the pages of F and, of the other pages with scale * scores[b,g,p] >= tau,
+ *   the best by decreasing score (ties to the lower p), at most
+ *   budget_pages - |F| of them, are kept.
+ * The logits and the comparison are evaluated in fp64 (exact products).
+ * sel and sel_count as ps_select_topk; sel_count[b,g] <= min(budget_pages, n)
+ * (fewer pages when few pass the threshold).
+ * Host checks: those of ps_select_topk; delta >= 0 (+infinity gives
+ * ps_select_topk's selection) and 0 < scale < infinity (else PS_ERR_BUDGET).
+ * Device preconditions: those of ps_select_topk and ps_score_pages. */
+int ps_select_topdelta(const ps_geom* geom, const float* q, const void* k_pool,
+                       const int32_t* page_table, const int32_t* seq_lens, const float* scores,
+                       int32_t budget_pages, int32_t n_sink_pages, int32_t n_local_pages,
+                       float scale, float delta, int32_t* sel, int32_t* sel_count, void* stream);
+
 
 /* 4a. Sparse split-KV decode. ("Don't read the haystack", sections "Part one:
  * hitting the wall on purpose" and "Part two: the skipping": the sparse twin

@@ -27,6 +27,7 @@ ENTRY_POINTS = (
     "ps_score_pages",
     "ps_refresh_score_pages",
     "ps_select_topk",
+    "ps_select_topdelta",
     "ps_sparse_decode",
     "ps_select_sparse_decode",
     "ps_full_decode",
@@ -75,6 +76,7 @@ _SIGS = {
     "ps_score_pages": [_G, _P, _P, _P, _P, _P, _P],
     "ps_refresh_score_pages": [_G, _P, _P, _P, _P, _P, _P, _P],
     "ps_select_topk": [_G, _P, _P, _I, _I, _I, _P, _P, _P],
+    "ps_select_topdelta": [_G, _P, _P, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P],
     "ps_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _P, _I, _F, _I, _P, _P, _P],
     "ps_select_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P, _P, _P,
                                 _P, _P, _P, _P, _P],

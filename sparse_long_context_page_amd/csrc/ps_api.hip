@@ -133,6 +133,28 @@ PS_API int ps_select_topk(const ps_geom* geom, const float* scores, const int32_
                                            n_local_pages, sel, sel_count, (hipStream_t)stream));
 }
 
+PS_API int ps_select_topdelta(const ps_geom* geom, const float* q, const void* k_pool,
+                              const int32_t* page_table, const int32_t* seq_lens,
+                              const float* scores, int32_t budget_pages, int32_t n_sink_pages,
+                              int32_t n_local_pages, float scale, float delta, int32_t* sel,
+                              int32_t* sel_count, void* stream) {
+  ps::Shape s;
+  int rc = check_geom(geom, &s);
+  if (rc) return rc;
+  if (!q || !k_pool || !page_table || !seq_lens || !scores || !sel || !sel_count)
+    return PS_ERR_NULL;
+  if (budget_pages < 1 || n_sink_pages < 0 || n_local_pages < 0) return PS_ERR_BUDGET;
+  if ((int64_t)n_sink_pages + n_local_pages > budget_pages) return PS_ERR_BUDGET;
+  if (!(delta >= 0.0f) || !(scale > 0.0f) || !(scale < INFINITY)) return PS_ERR_BUDGET;
+  if (s.max_pages > ps::kSelectMaxPages) return PS_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!prod_ok({s.batch, s.hkv, budget_pages, 4}, &t)) return PS_ERR_OVERFLOW;
+  if (s.batch == 0) return PS_OK;
+  return hip_status(ps::launch_select_topdelta(s, q, k_pool, page_table, scores, seq_lens,
+                                               budget_pages, n_sink_pages, n_local_pages, scale,
+                                               delta, sel, sel_count, (hipStream_t)stream));
+}
+
 PS_API int ps_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool,
                             const void* v_pool, const int32_t* page_table,
                             const int32_t* seq_lens, const int32_t* sel,
@@ -233,4 +255,4 @@ PS_API const char* ps_strerror(int status) {
   }
 }
 
-PS_API int ps_abi_version(void) { return (1 << 16) | 3; }  // 1.3: 8-bit metadata
+PS_API int ps_abi_version(void) { return (1 << 16) | 4; }  // 1.4: top-delta selection

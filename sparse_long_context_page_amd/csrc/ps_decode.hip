@@ -375,7 +375,7 @@ void decode_mfma_kernel(
     int32_t* dst = sa.sel ? sa.sel + (int64_t)unit * budget : nullptr;
     // The physical page of each kept page is read next to its score, so the
     // pages' K and V can be requested right after the selection.
-    const int kept = select_unit<W, C, true>(
+    const int kept = select_unit<W, C, true, false>(
         sa.scores + (int64_t)unit * max_pages, ceil_div(len, kPage), budget, sa.n_sink,
         sa.n_local, ssel, row, [&](int o, int p, int ph) {
           if (o >= first && o < first + per) {

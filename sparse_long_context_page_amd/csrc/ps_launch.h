@@ -36,6 +36,12 @@ hipError_t launch_select_topk(const Shape& s, const float* scores, const int32_t
                               int budget, int n_sink, int n_local, int32_t* sel,
                               int32_t* sel_count, hipStream_t st);
 
+hipError_t launch_select_topdelta(const Shape& s, const float* q, const void* k_pool,
+                                  const int32_t* page_table, const float* scores,
+                                  const int32_t* seq_lens, int budget, int n_sink, int n_local,
+                                  float scale, float delta, int32_t* sel, int32_t* sel_count,
+                                  hipStream_t st);
+
 hipError_t launch_select_decode(const Shape& s, const float* q, const void* k_pool,
                                 const void* v_pool, const int32_t* page_table,
                                 const int32_t* seq_lens, const float* scores, int budget,

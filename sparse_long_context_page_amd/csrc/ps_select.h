@@ -32,6 +32,7 @@ struct SelectLds {
   int hist[3][kSelBins];
   uint32_t wave_min[WAVES], wave_max[WAVES];
   int wave_cnt[WAVES];
+  int wave_pass[WAVES];  // FILTER: candidates passing the threshold, per wavefront
   uint64_t bin_val[kSelRankMax];  // the threshold bin as (key, ~page) values
   uint64_t cut;  // kept: every candidate at or above this value
 };
@@ -55,16 +56,22 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // row is given (else -1), and returns kept = min(budget, n). Ends with the
 // workgroup's LDS free for reuse only after a barrier of the caller.
 //
+// FILTER (top-delta selection, "Faster Than Flash: Exploiting Attention
+// Sparsity for Efficient Long-Context Decoding", section "Methodology", item
+// 2): only pages with scale * score >= tau (compared in fp64) are candidates,
+// and r = min(budget - |forced|, passing candidates); the others are dropped.
+//
 // The kept candidates are the r best in the order (key descending, page
 // ascending). Radix passes narrow the r-th key's bits; once its bin holds at
 // most 64 keys and more than one pass would still be needed, those keys are
 // gathered and wavefront 0 ranks them directly, which fixes the cut exactly as
 // (key, page); when every bit is decided first, the bin's keys are equal and
 // the cut is the remaining-th lowest page among them.
-template <int WAVES, int C, bool PHYS, typename Emit>
+template <int WAVES, int C, bool PHYS, bool FILTER, typename Emit>
 __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n, int budget,
                                            int n_sink, int n_local, SelectLds<WAVES>& sh,
-                                           const int32_t* __restrict__ table, Emit emit) {
+                                           const int32_t* __restrict__ table, Emit emit,
+                                           double scale = 0.0, double tau = 0.0) {
   constexpr int kThreads = WAVES * kWave;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -77,39 +84,54 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
 
   const int lo = n_sink;  // candidates are the pages [lo, hi)
   const int hi = n - n_local;
-  const int r = budget - n_sink - n_local;  // candidates to keep (hi - lo > r)
   const int seg = wave * kWave * C;
   auto page = [&](int j) { return seg + j * kWave + lane; };
-  auto is_cand = [&](int p) { return p >= lo && p < hi; };
+  auto in_range = [&](int p) { return p >= lo && p < hi; };
 
   // Keys (pages past the request re-read its last score and never count).
   uint32_t key[C];
   int phys[PHYS ? C : 1];
+  // FILTER: bit j % 32 of word j / 32 set when page(j) passes the threshold
+  uint32_t pass_bits[FILTER ? (C + 31) / 32 : 1];
+#pragma unroll
+  for (int i = 0; i < (FILTER ? (C + 31) / 32 : 1); ++i) pass_bits[i] = 0u;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
-    key[j] = order_key(row[min(page(j), n - 1)]);
+    const float sc = row[min(page(j), n - 1)];
+    key[j] = order_key(sc);
+    if constexpr (FILTER) pass_bits[j / 32] |= (scale * (double)sc >= tau ? 1u : 0u) << (j % 32);
     if constexpr (PHYS) phys[j] = table[min(page(j), n - 1)];
   }
+  auto cand_j = [&](int j) {
+    return in_range(page(j)) && (!FILTER || ((pass_bits[FILTER ? j / 32 : 0] >> (j % 32)) & 1u));
+  };
   uint32_t kmin = 0xffffffffu, kmax = 0u;
+  int n_pass = 0;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
-    const bool c = is_cand(page(j));
+    const bool c = cand_j(j);
     kmin = c ? min(kmin, key[j]) : kmin;
     kmax = c ? max(kmax, key[j]) : kmax;
+    if constexpr (FILTER) n_pass += __popcll(__ballot(c));
   }
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
   if (lane == 0) {
     sh.wave_min[wave] = kmin;
     sh.wave_max[wave] = kmax;
+    if constexpr (FILTER) sh.wave_pass[wave] = n_pass;
   }
   for (int i = tid; i < 2 * kSelBins; i += kThreads) sh.hist[i / kSelBins][i % kSelBins] = 0;
   __syncthreads();
+  int cands = hi - lo;  // candidates (all scored pages, or those passing the threshold)
+  if constexpr (FILTER) cands = 0;
 #pragma unroll
   for (int w = 0; w < WAVES; ++w) {
     kmin = min(kmin, sh.wave_min[w]);
     kmax = max(kmax, sh.wave_max[w]);
+    if constexpr (FILTER) cands += sh.wave_pass[w];
   }
+  const int r = min(budget - n_sink - n_local, cands);  // candidates to keep
 
   // Radix passes. Invariant: candidates with (k & pmask) > prefix are kept,
   // those with (k & pmask) < prefix are dropped, and `remaining` of the
@@ -121,7 +143,7 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
   uint32_t pmask = top == 32 ? 0u : ~((1u << top) - 1u);
   uint32_t prefix = kmin & pmask;
   int remaining = r;
-  int in_bin = hi - lo;
+  int in_bin = cands;
   int pass = 0;
 #pragma unroll 1
   while (remaining > 0 && in_bin > remaining && top > 0 &&
@@ -132,7 +154,7 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
 #pragma unroll
     for (int j = 0; j < C; ++j) {
       const uint32_t k = key[j];
-      if (is_cand(page(j)) && (k & pmask) == prefix)
+      if (cand_j(j) && (k & pmask) == prefix)
         atomicAdd(&h[(k >> shift) & (kSelBins - 1)], 1);
     }
     for (int i = tid; i < kSelBins; i += kThreads) sh.hist[(pass + 1) % 3][i] = 0;
@@ -180,7 +202,7 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
     // 64 or fewer keys in the bin: gather them (slots from per-wavefront
     // ballot counts); wavefront 0 ranks them in vector registers, reading
     // the gathered values as LDS broadcasts
-    auto in_bin_key = [&](int j) { return is_cand(page(j)) && (key[j] & pmask) == prefix; };
+    auto in_bin_key = [&](int j) { return cand_j(j) && (key[j] & pmask) == prefix; };
     int mine_cnt = 0;
 #pragma unroll
     for (int j = 0; j < C; ++j) mine_cnt += __popcll(__ballot(in_bin_key(j)));
@@ -230,7 +252,8 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
     const bool above = ranked ? order64(k, p) >= cut : km > prefix;
     const bool tie = !ranked && km == prefix;
     const int cc = above ? 2 : (tie ? 1 : 0);
-    const int c = p >= n ? 0 : (!is_cand(p) ? 2 : (remaining == 0 ? 0 : cc));
+    // out of range = forced (kept); in range but below the threshold: dropped
+    const int c = p >= n ? 0 : (!in_range(p) ? 2 : (!cand_j(j) || remaining == 0 ? 0 : cc));
     cls[j / 16] |= (uint32_t)c << (2 * (j % 16));
     cnt_keep += c == 2 ? 1 : 0;
     cnt_tie += c == 1 ? 1 : 0;

@@ -25,7 +25,7 @@ from .ops import Geometry
 class DecodeStep:
     def __init__(self, geom: Geometry, budget_pages: int, n_sink: int = 0, n_local: int = 0,
                  n_splits: int = 8, dense_splits: int = 32, scale: Optional[float] = None,
-                 device="cuda", fused: bool = True):
+                 device="cuda", fused: bool = True, delta: Optional[float] = None):
         self.g = geom
         self.budget = int(budget_pages)
         self.n_sink = int(n_sink)
@@ -33,9 +33,11 @@ class DecodeStep:
         self.n_splits = int(min(n_splits, self.budget))
         self.dense_splits = int(min(dense_splits, geom.max_pages))
         self.scale = ops.default_scale(geom.head_dim) if scale is None else float(scale)
+        # top-delta selection (ps_select_topdelta) instead of top-k when set
+        self.delta = None if delta is None else float(delta)
         # selection fused into the sparse decode (one launch) when supported
-        self.fused = bool(fused) and ops.select_decode_supported(geom, self.budget,
-                                                                 self.n_splits)
+        self.fused = (bool(fused) and self.delta is None and
+                      ops.select_decode_supported(geom, self.budget, self.n_splits))
         b, hq, hkv, d = geom.batch, geom.num_q_heads, geom.num_kv_heads, geom.head_dim
         f32 = dict(device=device, dtype=torch.float32)
         self.scores = torch.empty((b, hkv, geom.max_pages), **f32)
@@ -66,10 +68,12 @@ class DecodeStep:
                refresh_tail=False, tail_begin=None):
         """Score, select, decode and merge. With refresh_tail the metadata of
         each request's last page is rebuilt first: inside the score launch on
-        the fused path, else by ps_build_page_meta from tail_begin[b] = n_b - 1
-        (a device int32 tensor the caller provides)."""
+        the fused path and for top-delta selection (bf16 pools), else by
+        ps_build_page_meta from tail_begin[b] = n_b - 1 (a device int32
+        tensor the caller provides)."""
         g = self.g
-        if refresh_tail and self.fused:
+        in_score = self.fused or (self.delta is not None and g.kv_dtype == torch.bfloat16)
+        if refresh_tail and in_score:
             ops.ps_refresh_score_pages(g, q, k_pool, meta, page_table, seq_lens, self.scores,
                                        stream)
         else:
@@ -91,8 +95,13 @@ class DecodeStep:
                                         self.n_splits, self.sel, self.sel_count, acc, ml,
                                         stream=stream)
         else:
-            ops.ps_select_topk(g, self.scores, seq_lens, self.budget, self.n_sink, self.n_local,
-                               self.sel, self.sel_count, stream)
+            if self.delta is None:
+                ops.ps_select_topk(g, self.scores, seq_lens, self.budget, self.n_sink,
+                                   self.n_local, self.sel, self.sel_count, stream)
+            else:
+                ops.ps_select_topdelta(g, q, k_pool, page_table, seq_lens, self.scores,
+                                       self.budget, self.n_sink, self.n_local, self.scale,
+                                       self.delta, self.sel, self.sel_count, stream)
             ops.ps_sparse_decode(g, q, k_pool, v_pool, page_table, seq_lens, self.sel,
                                  self.sel_count, self.budget, self.scale, self.n_splits, acc, ml,
                                  stream)

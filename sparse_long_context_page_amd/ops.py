@@ -145,6 +145,25 @@ def ps_select_topk(g: Geometry, scores, seq_lens, budget_pages: int, n_sink_page
     _lib.check("ps_select_topk", rc)
 
 
+def ps_select_topdelta(g: Geometry, q, k_pool, page_table, seq_lens, scores, budget_pages: int,
+                       n_sink_pages: int, n_local_pages: int, scale: float, delta: float, sel,
+                       sel_count, stream=None) -> None:
+    """Top-delta selection: forced pages plus the best pages whose scaled
+    score reaches the smallest pseudo-max of the group minus delta, at most
+    budget_pages in all."""
+    lib = _lib.load()
+    rc = lib.ps_select_topdelta(
+        g.c(), _ptr(q, "q", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
+        _ptr(k_pool, "k_pool", g.kv_dtype, _pool_shape(g)),
+        _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
+        _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
+        _ptr(scores, "scores", torch.float32, (g.batch, g.num_kv_heads, g.max_pages)),
+        int(budget_pages), int(n_sink_pages), int(n_local_pages), float(scale), float(delta),
+        _ptr(sel, "sel", torch.int32, (g.batch, g.num_kv_heads, budget_pages)),
+        _ptr(sel_count, "sel_count", torch.int32, (g.batch, g.num_kv_heads)), _stream(stream))
+    _lib.check("ps_select_topdelta", rc)
+
+
 def ps_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens, sel, sel_count,
                      budget_pages: int, scale: float, n_splits: int, part_acc, part_ml,
                      stream=None) -> None:

@@ -114,6 +114,22 @@ def test_null_pointers():
     assert lib.ps_combine(g, X, X, 2, None, None, None, None) == _lib.PS_ERR_NULL
 
 
+def test_topdelta_validation():
+    lib = _lib.load()
+    g = geom()
+    f = lib.ps_select_topdelta
+    assert f(g, None, X, X, X, X, 8, 0, 1, 0.1, 1.0, X, X, None) == _lib.PS_ERR_NULL
+    assert f(g, X, None, X, X, X, 8, 0, 1, 0.1, 1.0, X, X, None) == _lib.PS_ERR_NULL
+    assert f(g, X, X, X, X, X, 8, 0, 1, 0.1, -1.0, X, X, None) == _lib.PS_ERR_BUDGET
+    assert f(g, X, X, X, X, X, 8, 0, 1, 0.1, float("nan"), X, X, None) == _lib.PS_ERR_BUDGET
+    assert f(g, X, X, X, X, X, 8, 0, 1, 0.0, 1.0, X, X, None) == _lib.PS_ERR_BUDGET
+    assert f(g, X, X, X, X, X, 8, 0, 1, float("inf"), 1.0, X, X, None) == _lib.PS_ERR_BUDGET
+    assert f(g, X, X, X, X, X, 8, 5, 4, 0.1, 1.0, X, X, None) == _lib.PS_ERR_BUDGET
+    assert f(geom(max_pages=65537), X, X, X, X, X, 8, 0, 1, 0.1, 1.0, X, X, None) == \
+        _lib.PS_ERR_UNSUPPORTED
+    assert f(geom(batch=0), X, X, X, X, X, 8, 0, 1, 0.1, float("inf"), X, X, None) == _lib.PS_OK
+
+
 def test_budget_and_split_validation():
     lib = _lib.load()
     g = geom()
