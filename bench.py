@@ -21,7 +21,9 @@ step time and the speedup over it, and the oracle timed on host cores.
 With the default bf16 metadata the same inputs are also run with 8-bit
 metadata bounds (--meta-format fp8 makes that the timed step): its step
 time, score-launch time and parity against the oracle on the 8-bit bounds
-are reported under "metadata_fp8".
+are reported under "metadata_fp8". They are also run with top-delta
+selection (--delta, default 5): step time, selection-launch time, pages kept
+and parity against the oracle's top-delta rule, under "topdelta_selection".
 """
 
 from __future__ import annotations
@@ -62,6 +64,10 @@ def parse():
                     help="page metadata: in the key dtype (kv) or 8-bit E4M3 bounds (fp8)")
     ap.add_argument("--no-fp8-line", action="store_true",
                     help="skip the 8-bit metadata measurement of a default run")
+    ap.add_argument("--no-topdelta-line", action="store_true",
+                    help="skip the top-delta selection measurement of a default run")
+    ap.add_argument("--delta", type=float, default=5.0,
+                    help="delta of the top-delta selection line (natural-log units)")
     ap.add_argument("--only-kernel", default=None,
                     help="profiling aid: after setup, launch only this stage --steps times "
                          "(score | step | copy: a 1 GiB device-to-device copy)")
@@ -155,17 +161,29 @@ def parity_gate(s, w, units, wl):
 
     gate = 2e-3 if w.kv_dtype == "bf16" else 1e-5
     step, inp = s["step"], s["inp"]
+    delta = step.delta  # top-delta selection when set
     sel = step.sel.cpu().numpy()
     cnt = step.sel_count.cpu().numpy()
     out = step.out.cpu().double().numpy()
     worst, n_amb, n_diff = 0.0, 0, 0
     for b, g in units:
         hu = unit_host(inp, b, g, wl, s["meta_format"])
-        r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local)
-        k = min(w.budget_pages, r["n"])
-        if int(cnt[b, g]) != k:
-            raise AssertionError(f"parity: sel_count {cnt[b, g]} != {k} at unit {(b, g)}")
-        amb, _ = ref.ambiguous_pages(r["scores"], r["n"], w.budget_pages, w.n_sink, w.n_local)
+        r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local, delta=delta)
+        k = int(cnt[b, g])
+        if delta is None:
+            if k != min(w.budget_pages, r["n"]):
+                raise AssertionError(f"parity: sel_count {k} at unit {(b, g)}")
+            amb, _ = ref.ambiguous_pages(r["scores"], r["n"], w.budget_pages, w.n_sink,
+                                         w.n_local)
+        else:  # threshold band: the device compares its fp32 scores
+            n = r["n"]
+            forced = sorted(set(range(min(w.n_sink, n))) | set(range(max(0, n - w.n_local), n)))
+            kf = ref.gather_tokens(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
+                                   hu["seq_lens"], 0, 0, forced if w.budget_pages < n else [],
+                                   hu["page_size"])
+            mt = ref.pseudo_max(hu["q"][0].astype(np.float64), kf, hu["scale"])
+            amb = ref.ambiguous_pages_topdelta(r["scores"], n, w.budget_pages, w.n_sink,
+                                               w.n_local, hu["scale"], mt, delta, rel=1e-5)
         got = set(int(x) for x in sel[b, g, :k])
         want = set(int(x) for x in r["sel"])
         if got - amb != want - amb:
@@ -555,10 +573,79 @@ def main():
     if args.meta_format == "kv" and w.kv_dtype == "bf16" and not args.no_fp8_line:
         print("# 8-bit metadata", file=sys.stderr, flush=True)
         result["metadata_fp8"] = fp8_line(args, w, sets, step_us, torch, wl, ps, acc)
+    if args.meta_format == "kv" and not args.no_topdelta_line:
+        print("# top-delta selection", file=sys.stderr, flush=True)
+        result["topdelta_selection"] = topdelta_line(args, w, sets, step_us, torch, wl, ps)
     if not args.no_cpu_baseline:
         print("# cpu baseline", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(s0, w, sample_units(w, args.cpu_units), wl)
     print(json.dumps(result), flush=True)
+
+
+def topdelta_line(args, w, sets, step_us_topk, torch, wl, ps):
+    """The same inputs with top-delta selection (delta = args.delta): parity
+    against the oracle's top-delta rule, the step timed as the main one
+    (refresh+score, top-delta select, sparse decode, merge: four launches),
+    the selection launch on its own, and the pages kept per unit."""
+    import numpy as np
+
+    sets_d = []
+    for s in sets:
+        inp = s["inp"]
+        step = ps.DecodeStep(s["g"], w.budget_pages, w.n_sink, w.n_local, w.n_splits,
+                             w.dense_splits, inp["scale"], delta=args.delta)
+        sets_d.append(dict(s, step=step))
+    run_sparse_step(sets_d[0])
+    torch.cuda.synchronize()
+    parity = parity_gate(sets_d[0], w, sample_units(w, args.parity_units), wl)
+    kept = sets_d[0]["step"].sel_count.cpu().numpy()
+
+    def all_sets(_):
+        for s in sets_d:
+            run_sparse_step(s)
+    multi = capture(all_sets, None, torch)
+    for _ in range(3):
+        multi.replay()
+    torch.cuda.synchronize()
+    reps = max(args.steps // len(sets_d), 1)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        multi.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) / (reps * len(sets_d)) * 1e3
+
+    n_k = 40
+
+    def batch(_):
+        for i in range(n_k):
+            s = sets_d[i % len(sets_d)]
+            inp, st = s["inp"], s["step"]
+            ps.ps_select_topdelta(s["g"], inp["q"], inp["k_pool"], inp["page_table"],
+                                  inp["seq_lens"], st.scores, st.budget, st.n_sink, st.n_local,
+                                  st.scale, st.delta, st.sel, st.sel_count)
+    gk = capture(batch, None, torch)
+    gk.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        gk.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    sel_us = e0.elapsed_time(e1) / (reps * n_k) * 1e3
+    for s in sets_d:  # leave the pools as whole steps leave them
+        run_sparse_step(s)
+    torch.cuda.synchronize()
+    return {"delta": args.delta, "us_per_step": round(step_us, 3),
+            "vs_topk_step": round(step_us / step_us_topk, 3),
+            "select_topdelta_us": round(sel_us, 3),
+            "kept_pages_per_unit": {"mean": round(float(np.mean(kept)), 2),
+                                    "min": int(kept.min()), "max": int(kept.max())},
+            "launches": ["ps_refresh_score_pages", "ps_select_topdelta", "ps_sparse_decode",
+                         "ps_combine"],
+            "parity": dict(parity, oracle="top-delta rule")}
 
 
 def fp8_line(args, w, sets, step_us_kv, torch, wl, ps, acc):

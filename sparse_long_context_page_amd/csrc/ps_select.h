@@ -60,6 +60,8 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // Sparsity for Efficient Long-Context Decoding", section "Methodology", item
 // 2): only pages with scale * score >= tau (compared in fp64) are candidates,
 // and r = min(budget - |forced|, passing candidates); the others are dropped.
+// tau = tau_fn(), called by every thread once the scores are requested, so
+// the threshold's own work overlaps their loads (it may hold barriers).
 //
 // The kept candidates are the r best in the order (key descending, page
 // ascending). Radix passes narrow the r-th key's bits; once its bin holds at
@@ -67,11 +69,15 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // gathered and wavefront 0 ranks them directly, which fixes the cut exactly as
 // (key, page); when every bit is decided first, the bin's keys are equal and
 // the cut is the remaining-th lowest page among them.
-template <int WAVES, int C, bool PHYS, bool FILTER, typename Emit>
+struct NoThreshold {
+  __device__ double operator()() const { return 0.0; }
+};
+
+template <int WAVES, int C, bool PHYS, bool FILTER, typename Emit, typename TauFn = NoThreshold>
 __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n, int budget,
                                            int n_sink, int n_local, SelectLds<WAVES>& sh,
                                            const int32_t* __restrict__ table, Emit emit,
-                                           double scale = 0.0, double tau = 0.0) {
+                                           double scale = 0.0, TauFn tau_fn = TauFn()) {
   constexpr int kThreads = WAVES * kWave;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
@@ -95,12 +101,19 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
   uint32_t pass_bits[FILTER ? (C + 31) / 32 : 1];
 #pragma unroll
   for (int i = 0; i < (FILTER ? (C + 31) / 32 : 1); ++i) pass_bits[i] = 0u;
+  float sc[C];
 #pragma unroll
   for (int j = 0; j < C; ++j) {
-    const float sc = row[min(page(j), n - 1)];
-    key[j] = order_key(sc);
-    if constexpr (FILTER) pass_bits[j / 32] |= (scale * (double)sc >= tau ? 1u : 0u) << (j % 32);
+    sc[j] = row[min(page(j), n - 1)];
     if constexpr (PHYS) phys[j] = table[min(page(j), n - 1)];
+  }
+  double tau = 0.0;
+  if constexpr (FILTER) tau = tau_fn();
+#pragma unroll
+  for (int j = 0; j < C; ++j) {
+    key[j] = order_key(sc[j]);
+    if constexpr (FILTER)
+      pass_bits[j / 32] |= (scale * (double)sc[j] >= tau ? 1u : 0u) << (j % 32);
   }
   auto cand_j = [&](int j) {
     return in_range(page(j)) && (!FILTER || ((pass_bits[FILTER ? j / 32 : 0] >> (j % 32)) & 1u));

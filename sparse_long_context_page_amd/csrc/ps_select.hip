@@ -37,8 +37,8 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
 // delta; select_unit keeps the forced pages and the best-scoring pages with
 // scale * score >= threshold, at most budget of them in all. The logits are
 // formed in fp64 (every fp32 * bf16 or fp32 * fp32 product is exact there),
-// one (token, head) pair per thread, then reduced per head across the
-// workgroup.
+// one (token, head) pair per thread with the key row in registers and the
+// queries in LDS, then reduced per head across the workgroup.
 template <typename T, int C, int D>
 __global__ __launch_bounds__(kSelThreads) void select_topdelta_kernel(
     const float* __restrict__ q, const T* __restrict__ k_pool,
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topdelta_kernel(
   constexpr int V = L::kVec;
   __shared__ SelectLds<kSelWaves> sh;
   __shared__ double sm_max[kSelWaves][8];
+  __shared__ __align__(16) float sm_q[8][D];
   const int unit = blockIdx.x;  // b * hkv + g
   const int b = unit / hkv;
   const int g = unit % hkv;
@@ -58,14 +59,21 @@ __global__ __launch_bounds__(kSelThreads) void select_topdelta_kernel(
   const int len = seq_lens[b];
   const int n = ceil_div(len, kPage);
 
-  double tau = -INFINITY;
-  if (budget < n && n_sink + n_local > 0) {  // uniform
+  // pseudo-max and threshold, evaluated inside select_unit once the scores
+  // are requested
+  auto threshold = [&]() -> double {
+    if (budget >= n || n_sink + n_local == 0) return -INFINITY;  // uniform
+    // the group's queries, staged once in LDS (fp32; widened per product)
+    const float* qg = q + ((int64_t)b * hkv * group + g * group) * D;
+    for (int i = threadIdx.x; i < group * D / 4; i += kSelThreads)
+      reinterpret_cast<float4*>(sm_q)[i] = reinterpret_cast<const float4*>(qg)[i];
     const int n_s = min(n_sink, n);
     const int l0 = max(n - n_local, n_s);  // local pages [l0, n), after the sink pages
     const int items = (n_s + n - l0) * kPage * group;  // (forced page, token, head)
     double mx[8];
 #pragma unroll
     for (int h = 0; h < 8; ++h) mx[h] = -INFINITY;
+    __syncthreads();  // sm_q complete
     for (int it = threadIdx.x; it < items; it += kSelThreads) {
       const int h = it % group;
       const int tok = it / group;
@@ -74,15 +82,20 @@ __global__ __launch_bounds__(kSelThreads) void select_topdelta_kernel(
       if (p * kPage + t >= len) continue;  // unused slot of a partial page
       const int phys = page_table[(int64_t)b * max_pages + p];
       const T* krow = k_pool + (((int64_t)phys * hkv + g) * kPage + t) * D;
-      const float* qh = q + ((int64_t)b * hkv * group + g * group + h) * D;
-      double acc = 0.0;
-      for (int d = 0; d < D; d += V) {
-        float kf[V];
-        unpack(ld16(krow + d), kf);
+      uint4 kv[D / V];
 #pragma unroll
-        for (int j = 0; j < V; ++j) acc = __builtin_fma((double)qh[d + j], (double)kf[j], acc);
+      for (int i = 0; i < D / V; ++i) kv[i] = ld16(krow + i * V);
+      // four partial sums over interleaved coordinates, then a fixed order
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int i = 0; i < D / V; ++i) {
+        float kf[V];
+        unpack(kv[i], kf);
+#pragma unroll
+        for (int j = 0; j < V; ++j)
+          acc[j % 4] = __builtin_fma((double)sm_q[h][i * V + j], (double)kf[j], acc[j % 4]);
       }
-      const double s = (double)scale * acc;
+      const double s = (double)scale * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
 #pragma unroll
       for (int hh = 0; hh < 8; ++hh) mx[hh] = hh == h ? fmax(mx[hh], s) : mx[hh];
     }
@@ -100,12 +113,12 @@ __global__ __launch_bounds__(kSelThreads) void select_topdelta_kernel(
       for (int w = 0; w < kSelWaves; ++w) m = fmax(m, sm_max[w][hh]);
       m_min = fmin(m_min, m);
     }
-    tau = m_min - (double)delta;
-  }
+    return m_min - (double)delta;
+  };
   int32_t* dst = sel + (int64_t)unit * budget;
   const int kept = select_unit<kSelWaves, C, false, true>(
       scores + (int64_t)unit * max_pages, n, budget, n_sink, n_local, sh, nullptr,
-      [&](int o, int p, int) { dst[o] = p; }, (double)scale, tau);
+      [&](int o, int p, int) { dst[o] = p; }, (double)scale, threshold);
   for (int i = kept + (int)threadIdx.x; i < budget; i += kSelThreads) dst[i] = -1;
   if (threadIdx.x == 0) sel_count[unit] = kept;
 }
