@@ -44,8 +44,11 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   constexpr int V = L::kVec;
   constexpr int LPR = L::kLanesPerRow;
 
+  // Consecutive workgroups go to the 8 XCDs in turn; rotating the chunk
+  // index by the unit spreads the leading chunks of short requests (the only
+  // ones with pages) over every XCD instead of the first few.
   const int unit = blockIdx.x / chunks_per_unit;  // b * hkv + g
-  const int chunk = blockIdx.x % chunks_per_unit;
+  const int chunk = (blockIdx.x % chunks_per_unit + unit) % chunks_per_unit;
   const int b = unit / hkv;
   const int g = unit % hkv;
   const int np = ceil_div(seq_lens[b], kPage);
@@ -173,8 +176,11 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   // holds a request's last page)
   __shared__ __align__(16) uint16_t tail_lds[2][REFRESH ? D : 8];
 
+  // Consecutive workgroups go to the 8 XCDs in turn; rotating the chunk
+  // index by the unit spreads the leading chunks of short requests (the only
+  // ones with pages) over every XCD instead of the first few.
   const int unit = blockIdx.x / chunks_per_unit;  // b * hkv + g
-  const int chunk = blockIdx.x % chunks_per_unit;
+  const int chunk = (blockIdx.x % chunks_per_unit + unit) % chunks_per_unit;
   const int b = unit / hkv;
   const int g = unit % hkv;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
