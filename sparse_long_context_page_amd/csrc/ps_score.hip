@@ -45,10 +45,11 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   constexpr int LPR = L::kLanesPerRow;
 
   // Consecutive workgroups go to the 8 XCDs in turn; rotating the chunk
-  // index by the unit spreads the leading chunks of short requests (the only
-  // ones with pages) over every XCD instead of the first few.
+  // index by the request spreads the leading chunks of short requests (the
+  // only ones with pages) over every XCD instead of the first few, and keeps
+  // a request's KV heads (interleaved in the metadata) on the same XCDs.
   const int unit = blockIdx.x / chunks_per_unit;  // b * hkv + g
-  const int chunk = (blockIdx.x % chunks_per_unit + unit) % chunks_per_unit;
+  const int chunk = (blockIdx.x % chunks_per_unit + unit / hkv) % chunks_per_unit;
   const int b = unit / hkv;
   const int g = unit % hkv;
   const int np = ceil_div(seq_lens[b], kPage);
@@ -177,10 +178,11 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   __shared__ __align__(16) uint16_t tail_lds[2][REFRESH ? D : 8];
 
   // Consecutive workgroups go to the 8 XCDs in turn; rotating the chunk
-  // index by the unit spreads the leading chunks of short requests (the only
-  // ones with pages) over every XCD instead of the first few.
+  // index by the request spreads the leading chunks of short requests (the
+  // only ones with pages) over every XCD instead of the first few, and keeps
+  // a request's KV heads (interleaved in the metadata) on the same XCDs.
   const int unit = blockIdx.x / chunks_per_unit;  // b * hkv + g
-  const int chunk = (blockIdx.x % chunks_per_unit + unit) % chunks_per_unit;
+  const int chunk = (blockIdx.x % chunks_per_unit + unit / hkv) % chunks_per_unit;
   const int b = unit / hkv;
   const int g = unit % hkv;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
