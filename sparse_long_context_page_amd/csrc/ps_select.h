@@ -65,7 +65,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 //
 // The kept candidates are the r best in the order (key descending, page
 // ascending). Radix passes narrow the r-th key's bits; once its bin holds at
-// most 64 keys and more than one pass would still be needed, those keys are
+// most 64 keys and more than two passes would still be needed, those keys are
 // gathered and wavefront 0 ranks them directly, which fixes the cut exactly as
 // (key, page); when every bit is decided first, the bin's keys are equal and
 // the cut is the remaining-th lowest page among them.
@@ -149,8 +149,9 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
   // Radix passes. Invariant: candidates with (k & pmask) > prefix are kept,
   // those with (k & pmask) < prefix are dropped, and `remaining` of the
   // `in_bin` candidates with (k & pmask) == prefix are kept. A pass costs one
-  // barrier and ranking the bin three, so a pass that decides every
-  // remaining bit is taken even when the bin is small enough to rank.
+  // barrier and ranking the bin three, so passes continue while at most two
+  // more would decide every bit, even when the bin is small enough to rank
+  // (one pass usually leaves exactly the keys still needed).
   const uint32_t diff = kmin ^ kmax;
   int top = diff ? 32 - __clz(diff) : 0;  // undecided low bits
   uint32_t pmask = top == 32 ? 0u : ~((1u << top) - 1u);
@@ -160,7 +161,7 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
   int pass = 0;
 #pragma unroll 1
   while (remaining > 0 && in_bin > remaining && top > 0 &&
-         (in_bin > kSelRankMax || top <= kSelDigitBits)) {
+         (in_bin > kSelRankMax || top <= 2 * kSelDigitBits)) {
     const int width = top < kSelDigitBits ? top : kSelDigitBits;
     const int shift = top - width;
     int* h = sh.hist[pass % 3];
