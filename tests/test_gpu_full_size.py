@@ -100,3 +100,30 @@ def test_dense_decode_matches_exact_attention(full):
             o, l = ref.full_decode(hu, 0, i)
             assert rel_l2(out_h[b, h], o) <= gate(w)
             assert abs(lse_h[b, h] - l) <= 1e-4 * max(1.0, abs(l))
+
+
+def test_sampled_units_match_oracle_with_8bit_metadata(full):
+    """The same step with 8-bit metadata bounds, at full size: the codes of
+    the sampled units bit for bit against the oracle's directed rounding,
+    scores against fp64 on the 8-bit values, page lists and outputs."""
+    w, inp, _ = full
+    res = run_step(inp, meta_format="fp8")
+    for b, g in _sample_units(w, k=2):
+        print(f"[full-size fp8] {w.name} unit b={b} g={g}", flush=True)
+        hu = unit_host(inp, b, g, meta_format="fp8")
+        n = int(inp["n_pages_host"][b])
+        phys = inp["page_table"][b, :n].long()
+        dev = res["meta"][phys, g].cpu().numpy()
+        kmax, kmin = ref.unit_page_meta(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
+                                        hu["seq_lens"], 0, 0, hu["page_size"])
+        cmax, cmin = ref.fp8_bounds(kmax, kmin)
+        assert np.array_equal(dev[:, 0], cmax) and np.array_equal(dev[:, 1], cmin)
+        r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local)
+        assert score_rel_err(res["scores"][b, g, :n], r["scores"]) <= SCORE_REL
+        _, differs = check_selection(res["sel"][b, g], res["sel_count"][b, g], r["scores"], n,
+                                     w.budget_pages, w.n_sink, w.n_local)
+        k = int(res["sel_count"][b, g])
+        check_unit_outputs(res, hu, b, g, w, w.budget_pages, w.n_sink, w.n_local,
+                           sel_dev=res["sel"][b, g, :k] if differs else None)
+    del res
+    torch.cuda.empty_cache()

@@ -172,3 +172,36 @@ def test_headline_shape_topdelta_keeps_budget():
     ops.ps_select_topk(g, sc, inp["seq_lens"], w.budget_pages, w.n_sink, w.n_local, sel, cnt)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(a, sel.cpu().numpy())
+
+
+def test_step_with_8bit_metadata():
+    """Top-delta selection on scores of 8-bit metadata bounds: the oracle's
+    top-delta rule on its 8-bit scores, outside the band; outputs in the gate."""
+    w, spread, deltas, _ = CASES[0]
+    inp = _inputs(w, spread)
+    g = geometry(inp, "fp8")
+    step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
+                      inp["scale"], delta=deltas[0])
+    meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+    out, lse = step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
+                           inp["seq_lens"], inp["sink"])
+    torch.cuda.synchronize()
+    res = {"out": out.cpu().numpy().astype(np.float64),
+           "lse": lse.cpu().numpy().astype(np.float64)}
+    sel, cnt = step.sel.cpu().numpy(), step.sel_count.cpu().numpy()
+    fewer = 0
+    for b in range(w.batch):
+        for kv in range(w.num_kv_heads):
+            hu = unit_host(inp, b, kv, meta_format="fp8")
+            r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local, delta=deltas[0])
+            n = r["n"]
+            mt = _oracle_pseudo_max(hu, n, w.n_sink, w.n_local, w.budget_pages)
+            amb = ref.ambiguous_pages_topdelta(r["scores"], n, w.budget_pages, w.n_sink,
+                                               w.n_local, hu["scale"], mt, deltas[0], rel=1e-5)
+            k = int(cnt[b, kv])
+            assert set(int(x) for x in sel[b, kv, :k]) - amb == \
+                set(int(x) for x in r["sel"]) - amb, (b, kv)
+            fewer += k < min(w.budget_pages, n)
+            check_unit_outputs(res, hu, b, kv, w, w.budget_pages, w.n_sink, w.n_local,
+                               sel_dev=sel[b, kv, :k])
+    print(f"8-bit metadata, top-delta: units keeping fewer pages than the budget: {fewer}")
