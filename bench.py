@@ -354,6 +354,30 @@ def main():
     print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr,
           flush=True)
 
+    # -- distribution over replays, and warm steps ------------------------------
+    # per-replay times of the multi-step graph (median, p10, p90 per step), and
+    # the step repeated on ONE input set, whose working set then stays in the
+    # memory-side cache ("warm", reported as such)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(max(args.steps // len(sets), 1))]
+    for a, b in ev:
+        a.record()
+        multi.replay()
+        b.record()
+    torch.cuda.synchronize()
+    per_step = sorted(a.elapsed_time(b) * 1e3 / len(sets) for a, b in ev)
+
+    def pct(p):
+        return per_step[min(len(per_step) - 1, int(round(p * (len(per_step) - 1))))]
+    for _ in range(3):
+        graphs[0].replay()
+    e0.record()
+    for _ in range(args.steps):
+        graphs[0].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    warm_us = e0.elapsed_time(e1) / args.steps * 1e3
+
     # -- the same steps, one graph per step ---------------------------------
     e0.record()
     for i in range(args.steps):
@@ -560,6 +584,8 @@ def main():
         "copy_gbps_read_plus_write": round(copy_gbps, 1),
         "timed_wall_ms": round(wall_ms, 3),
         "eager_us_per_step": round(eager_us, 3),
+        "us_per_step_p10_p50_p90": [round(pct(0.1), 3), round(pct(0.5), 3), round(pct(0.9), 3)],
+        "warm_same_set_us_per_step": round(warm_us, 3),
         "one_step_per_graph_us_per_step": round(one_graph_us, 3),
         "parity": parity,
         "roofline": {"kernel": "ps_refresh_score_pages" if fused else "ps_score_pages",
