@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
 // separated (max(q,0) against kmax, min(q,0) against kmin), so every product
 // is exact; each (sign, 32-coordinate block) has its own accumulator (lo, mid,
 // then hi added), and the 2*D/32 accumulators are summed in a fixed tree.
-// Each wavefront streams a run of tiles of one (request, KV head): it splits
+// Each wavefront streams tiles of one (request, KV head), every w_u-th tile
+// of the request (w_u = the request's wavefronts): it splits
 // its own slice of the queries in registers (no LDS, no barrier), reads its
 // table entries once up front, and keeps the metadata of the next two tiles
 // in flight while the current tile is scored.
@@ -190,7 +191,13 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   const int col = lane % 16;   // page of the tile (B column), head of A (row)
   const int kgrp = lane / 16;  // which 8 of each 32 coordinates
   const bool live = col < G;   // A rows G..15 are zero
-  const int p0 = (chunk * kMfmaWaves + wave) * tiles_per_wave * 16;
+  // The unit's tiles are dealt to its wavefronts round-robin (wavefront wu
+  // takes tiles wu, wu + w_u, wu + 2 w_u, ...), so every wavefront reads
+  // from all over the unit's metadata rather than one contiguous run; the
+  // wavefronts then finish closer together.
+  const int wu = chunk * kMfmaWaves + wave;      // wavefront within the unit
+  const int w_u = chunks_per_unit * kMfmaWaves;  // wavefronts per unit
+  auto tile_page = [&](int t) { return ((int64_t)wu + (int64_t)t * w_u) * 16; };
 
   // 1. Everything that does not depend on the request length is requested at
   // once: the length, the A-operand slice of the queries (8 consecutive
@@ -206,7 +213,8 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   const int32_t* row = page_table + (int64_t)b * max_pages;
   int phys[kMaxTiles];
 #pragma unroll
-  for (int t = 0; t < kMaxTiles; ++t) phys[t] = row[min(p0 + t * 16 + col, max_pages - 1)];
+  for (int t = 0; t < kMaxTiles; ++t)
+    phys[t] = row[min(tile_page(t) + col, (int64_t)max_pages - 1)];
   __builtin_amdgcn_sched_barrier(0);
   const float* qh = q + ((int64_t)b * hkv * G + g * G + min(col, G - 1)) * D;
   float4 qv[KB][2];
@@ -219,13 +227,14 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
 
   const int np = ceil_div(len, kPage);
   // tiles of this wavefront that hold pages of the request
-  const int n_tiles = p0 < np ? min(tiles_per_wave, ceil_div(np - p0, 16)) : 0;
+  const int n_all = ceil_div(np, 16);  // tiles of the request
+  const int n_tiles = wu < n_all ? min(tiles_per_wave, ceil_div(n_all - wu, w_u)) : 0;
   // A page past the request reads the metadata of physical page 0 (shared by
   // all such lanes, so it stays in cache) and its score is not written; an
   // entry of a live page is clamped into the pool.
 #pragma unroll
   for (int t = 0; t < kMaxTiles; ++t)
-    phys[t] = p0 + t * 16 + col < np ? min(max(phys[t], 0), last_phys) : 0;
+    phys[t] = tile_page(t) + col < np ? min(max(phys[t], 0), last_phys) : 0;
   auto load = [&](int t, uint4 (&bx)[ML], uint4 (&bn)[ML]) {
     const uint8_t* src = static_cast<const uint8_t*>(meta) +
                          (((int64_t)phys[t] * hkv + g) * 2 * D + coord(kgrp, 0)) * EB;
@@ -244,14 +253,14 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   // The last page's keys, when this wavefront holds it, behind its first
   // two tiles (waits for the tiles already cover them).
   const int tail = np - 1;
-  const bool has_tail = REFRESH && n_tiles > 0 && tail < p0 + n_tiles * 16;
+  const bool has_tail = REFRESH && n_tiles > 0 && (tail / 16) % w_u == wu;
   const int col_tail = tail % 16;
   PageFold<bf16_t, D> tail_keys;
   int phys_tail = 0;
   if (has_tail) {
     int pt = phys[0];
 #pragma unroll
-    for (int t = 1; t < kMaxTiles; ++t) pt = t == (tail - p0) / 16 ? phys[t] : pt;
+    for (int t = 1; t < kMaxTiles; ++t) pt = t == (tail / 16) / w_u ? phys[t] : pt;
     phys_tail = __builtin_amdgcn_readlane(pt, col_tail);
     tail_keys.load(k_pool + ((int64_t)phys_tail * hkv + g) * kPage * D, lane);
   }
@@ -350,7 +359,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
 #pragma unroll
     for (int i = 0; i < 4; ++i) best = (4 * kgrp + i < G) ? fmax_(best, u[i]) : best;
     best = fmax_(best, __shfl_xor(best, 16));  // heads 0-3 with 4-7
-    const int p = p0 + t * 16 + col;
+    const int64_t p = tile_page(t) + col;
     if (kgrp == 0 && p < np) out[p] = best;
   };
   // Steady state: every iteration scores two tiles and requests the next two,
