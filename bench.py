@@ -54,8 +54,11 @@ def parse():
     ap.add_argument("--sets", type=int, default=4, help="independent input batches cycled")
     ap.add_argument("--dense-steps", type=int, default=20)
     ap.add_argument("--parity-units", type=int, default=6)
-    ap.add_argument("--cpu-units", type=int, default=16,
-                    help="(request, KV head) units of one step the oracle is timed on")
+    ap.add_argument("--cpu-units", type=int, default=0,
+                    help="(request, KV head) units of one step the oracle is timed on "
+                         "(0: all of them)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU work the oracle timing aims for (whole passes, at most 3x)")
     ap.add_argument("--n-splits", type=int, default=None, help="override the sparse split count")
     ap.add_argument("--dense-splits", type=int, default=None,
                     help="override the dense split count")
@@ -203,39 +206,48 @@ def parity_gate(s, w, units, wl):
             "ambiguous_pages": n_amb, "units_differing_inside_band": n_diff}
 
 
-def cpu_baseline(s, w, units, wl):
+def cpu_baseline(s, w, units, wl, seconds):
     """The fp64 oracle's decode step (score, select, attend; metadata given,
-    as on the device) timed on the host for a sample of units, scaled to the
-    whole step."""
+    as on the device) timed on the host, single-threaded: whole steps over
+    the given units, repeated until about `seconds` of CPU work (at most three
+    times that), scaled to the whole step when the units are a sample."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle as ref
 
     inp = s["inp"]
-    per_unit = []
+    prepared = []
+    for b, g in units:
+        hu = unit_host(inp, b, g, wl)
+        kmax, kmin = ref.unit_page_meta(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
+                                        hu["seq_lens"], 0, 0, hu["page_size"])
+        prepared.append((hu, kmax, kmin))
+    passes, total = 0, 0.0
     with threadpool_limits(limits=1):
-        for b, g in units:
-            hu = unit_host(inp, b, g, wl)
-            kmax, kmin = ref.unit_page_meta(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
-                                            hu["seq_lens"], 0, 0, hu["page_size"])
+        while passes == 0 or (total < seconds and total < 3 * seconds - total / passes):
             t0 = time.perf_counter()
-            qg = hu["q"][0].astype(np.float64)
-            _, sc = ref.unit_scores(qg, kmax, kmin)
-            sel, _, _ = ref.select_pages(sc, kmax.shape[0], w.budget_pages, w.n_sink, w.n_local)
-            keys = ref.gather_tokens(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
-                                     hu["seq_lens"], 0, 0, sel, hu["page_size"])
-            vals = ref.gather_tokens(hu["v_pool"], hu["kv_dtype"], hu["page_table"],
-                                     hu["seq_lens"], 0, 0, sel, hu["page_size"])
-            for i in range(w.group):
-                sk = None if hu["sink"] is None else hu["sink"][i]
-                ref.attend(qg[i], keys, vals, hu["scale"], sk)
-            per_unit.append(time.perf_counter() - t0)
+            for hu, kmax, kmin in prepared:
+                qg = hu["q"][0].astype(np.float64)
+                _, sc = ref.unit_scores(qg, kmax, kmin)
+                sel, _, _ = ref.select_pages(sc, kmax.shape[0], w.budget_pages, w.n_sink,
+                                             w.n_local)
+                keys = ref.gather_tokens(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
+                                         hu["seq_lens"], 0, 0, sel, hu["page_size"])
+                vals = ref.gather_tokens(hu["v_pool"], hu["kv_dtype"], hu["page_table"],
+                                         hu["seq_lens"], 0, 0, sel, hu["page_size"])
+                for i in range(w.group):
+                    sk = None if hu["sink"] is None else hu["sink"][i]
+                    ref.attend(qg[i], keys, vals, hu["scale"], sk)
+            total += time.perf_counter() - t0
+            passes += 1
     total_units = w.batch * w.num_kv_heads
-    us = float(np.mean(per_unit)) * total_units * 1e6
+    us = total / passes * total_units / len(units) * 1e6
+    what = (f"all {total_units} (request, KV head) units of one step" if len(units) == total_units
+            else f"{len(units)} of {total_units} (request, KV head) units of one step, "
+                 f"scaled x{total_units}/{len(units)}")
     return {"value": us, "unit": "us/decode-step", "cores": 1, "kind": "oracle",
-            "sample": f"{len(units)} of {total_units} (request, KV head) units of one step, "
-                      f"single-threaded numpy fp64, scaled x{total_units}/{len(units)}; "
+            "sample": f"{what}, {passes} passes ({total:.1f} s), single-threaded numpy fp64; "
                       "metadata precomputed as on the device"}
 
 
@@ -609,7 +621,10 @@ def main():
         result["topdelta_selection"] = topdelta_line(args, w, sets, step_us, torch, wl, ps)
     if not args.no_cpu_baseline:
         print("# cpu baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(s0, w, sample_units(w, args.cpu_units), wl)
+        n_units = w.batch * w.num_kv_heads
+        result["cpu_baseline"] = cpu_baseline(
+            s0, w, sample_units(w, args.cpu_units if args.cpu_units > 0 else n_units), wl,
+            args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
