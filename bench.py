@@ -289,8 +289,10 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode step has no "
-                                   "cross-GPU work (see DESIGN.md for how it would shard)",
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the decode step has "
+                                   "no cross-GPU work: every (request, KV head) is "
+                                   "independent, so requests or KV heads shard over GPUs "
+                                   "without communication",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -30,7 +30,7 @@ Sources (cited by page title and section):
   and proving it against dense" (output equals a reference restricted to the
   selected positions).
 
-Readings taken where the pages are silent (each listed again in the design doc):
+Readings taken where the pages are silent:
 
 1. GQA: one page list per (request, KV head); the group's score for a page
    is the MAX over the group's query heads of the per-head bound. No page says
