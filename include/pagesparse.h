@@ -49,7 +49,7 @@ typedef enum {
   PS_OK = 0,
   PS_ERR_NULL = -1,        /* a required pointer is NULL                          */
   PS_ERR_SHAPE = -2,       /* an inconsistent or out-of-range dimension          */
-  PS_ERR_UNSUPPORTED = -3, /* a valid shape this build does not implement        */
+  PS_ERR_UNSUPPORTED = -3, /* a valid shape the library does not implement       */
   PS_ERR_OVERFLOW = -4,    /* a size computation overflows 64 bits / int32 index */
   PS_ERR_BUDGET = -5,      /* budget, forced-page or split arguments inconsistent */
   PS_ERR_HIP = -6          /* the HIP runtime reported an error at launch        */

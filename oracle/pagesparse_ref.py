@@ -180,7 +180,7 @@ def unit_scores(q_group: np.ndarray, kmax: np.ndarray, kmin: np.ndarray):
 # so the 8-bit box contains the exact one and, for every q, the bound can only
 # grow. The attention itself still reads the full-precision keys and values.
 #
-# Format (this build's reading; the pages name no 8-bit format): the 8-bit
+# Format (a reading: the pages name no 8-bit format): the 8-bit
 # floating point E4M3 of the OCP 8-bit floating point specification, the
 # variant without infinities: 1 sign bit, 4 exponent bits with bias 7, 3
 # mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; the two

@@ -25,7 +25,7 @@ from sparse_long_context_page_amd import DecodeStep
 
 pytestmark = pytest.mark.gpu
 
-FULL = [wl.B8_16K, wl.HEADLINE, wl.SINK, wl.RAGGED]
+FULL = [wl.B8_16K, wl.B32_64K, wl.SINK, wl.RAGGED]
 
 
 def _sample_units(w, k=3):
@@ -85,7 +85,7 @@ def test_sampled_units_match_oracle(full):
 
 def test_dense_decode_matches_exact_attention(full):
     w, inp, _ = full
-    if w.name not in (wl.B8_16K.name, wl.HEADLINE.name):
+    if w.name not in (wl.B8_16K.name, wl.B32_64K.name):
         pytest.skip("the dense check runs on the two uniform-length GQA-6 workloads")
     step = DecodeStep(geometry(inp), w.budget_pages, w.n_sink, w.n_local, w.n_splits,
                       w.dense_splits, inp["scale"])

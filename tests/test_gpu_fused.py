@@ -15,7 +15,7 @@ from test_gpu_parity import SMALL
 
 pytestmark = pytest.mark.gpu
 
-BF16 = [w for w in SMALL if w.kv_dtype == "bf16"] + [wl.HEADLINE]
+BF16 = [w for w in SMALL if w.kv_dtype == "bf16"] + [wl.B32_64K]
 
 
 def _both(inp, budget=None, n_sink=None, n_local=None, n_splits=None):

@@ -97,7 +97,7 @@ def test_selection_and_outputs(cases, w):
     print(f"{w.name}: max rel-L2 {worst:.3e} (gate {gate(w)})")
 
 
-@pytest.mark.parametrize("w", BF16 + [wl.HEADLINE], ids=[w.name for w in BF16 + [wl.HEADLINE]])
+@pytest.mark.parametrize("w", BF16 + [wl.B32_64K], ids=[w.name for w in BF16 + [wl.B32_64K]])
 def test_refresh_score_equals_meta_then_score_bitwise(w):
     inp = wl.make_inputs(w, device="cuda")
     g = geometry(inp, "fp8")

@@ -159,10 +159,10 @@ def test_infinite_delta_and_no_forced_pages_are_topk(case):
         np.testing.assert_array_equal(ca, cnt.cpu().numpy())
 
 
-def test_headline_shape_topdelta_keeps_budget():
+def test_b32_64k_topdelta_keeps_budget():
     """On the 32 x 64k workload (random keys: loose bounds) every page passes
     a threshold of delta = 5, so the selection is the top-k one."""
-    w = wl.HEADLINE
+    w = wl.B32_64K
     inp = wl.make_inputs(w, device="cuda")
     g = geometry(inp)
     sc = _scores(inp, g)

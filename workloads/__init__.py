@@ -76,7 +76,7 @@ TINY_DENSE = TINY.replace(name="tiny_dense", budget_pages=64, n_splits=8)
 B8_16K = Workload("b8_16k_needles_sink_page", batch=8, num_q_heads=12, num_kv_heads=2,
                   head_dim=128, context=16384, budget_pages=128, n_sink=1, needles=4,
                   seed=1002, n_splits=8, dense_splits=32)
-HEADLINE = Workload("b32_64k_needles_local4", batch=32, num_q_heads=12, num_kv_heads=2,
+B32_64K = Workload("b32_64k_needles_local4", batch=32, num_q_heads=12, num_kv_heads=2,
                     head_dim=128, context=65536, budget_pages=128, n_local=4, needles=8,
                     seed=1003, n_splits=4, dense_splits=64)
 SINK = Workload("b16_32k_learned_sink", batch=16, num_q_heads=64, num_kv_heads=8, head_dim=64,
@@ -86,7 +86,7 @@ RAGGED = Workload("b64_ragged_4k_128k_shared_pool", batch=64, num_q_heads=28, nu
                   head_dim=128, ctx_range=(4096, 131072), budget_pages=128, needles=8,
                   permuted_pool=True, max_pages=8192, seed=1005, n_splits=1, dense_splits=64)
 
-WORKLOADS = {w.name: w for w in (TINY, TINY_DENSE, B8_16K, HEADLINE, SINK, RAGGED)}
+WORKLOADS = {w.name: w for w in (TINY, TINY_DENSE, B8_16K, B32_64K, SINK, RAGGED)}
 
 
 def _pages(n_tokens: int, page: int) -> int:
