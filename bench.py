@@ -98,7 +98,7 @@ def run_sparse_step(s):
     refreshed, then score, select, sparse decode and merge."""
     inp, step = s["inp"], s["step"]
     return step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], s["meta"], inp["page_table"],
-                       inp["seq_lens"], inp["sink"], refresh_tail=True, tail_begin=s["tail"])
+                       inp["seq_lens"], inp["sink"], refresh_tail=True)
 
 
 def run_dense_step(s):

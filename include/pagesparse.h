@@ -167,7 +167,7 @@ int ps_score_pages(const ps_geom* geom, const float* q, const void* meta,
  * page summaries are maintained incrementally as tokens append; a decode step
  * appends to each request's last page only.) meta is read for every page and
  * written for page n_b - 1 of every request.
- * Host checks: those of ps_score_pages; bf16 K (else PS_ERR_UNSUPPORTED).
+ * Host checks: those of ps_score_pages.
  * Device preconditions: as ps_build_page_meta and ps_score_pages; no two
  * requests share their last physical page. */
 int ps_refresh_score_pages(const ps_geom* geom, const float* q, const void* k_pool, void* meta,
@@ -256,7 +256,7 @@ int ps_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool, co
  * Host checks: those of ps_select_topk and ps_sparse_decode (same codes);
  * sel and sel_count both NULL or both set, and the partials set when out is
  * NULL (else PS_ERR_NULL); out != NULL with n_splits != 1, or sink or lse
- * set without out (PS_ERR_BUDGET); bf16 K/V, max_pages <= 8192 and
+ * set without out (PS_ERR_BUDGET); max_pages <= 8192 and
  * ceil(budget_pages / n_splits) <= 512 (else PS_ERR_UNSUPPORTED).
  * Device precondition: scores are finite (no NaN). */
 int ps_select_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool,

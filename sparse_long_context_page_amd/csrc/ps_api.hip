@@ -110,7 +110,6 @@ PS_API int ps_refresh_score_pages(const ps_geom* geom, const float* q, const voi
   int rc = check_geom(geom, &s);
   if (rc) return rc;
   if (!q || !k_pool || !meta || !page_table || !seq_lens || !scores) return PS_ERR_NULL;
-  if (!s.kv_bf16) return PS_ERR_UNSUPPORTED;
   if (s.batch == 0) return PS_OK;
   return hip_status(ps::launch_score_pages(s, q, meta, page_table, seq_lens, scores, k_pool, meta,
                                            (hipStream_t)stream));
@@ -196,7 +195,7 @@ PS_API int ps_select_sparse_decode(const ps_geom* geom, const float* q, const vo
   if ((int64_t)n_sink_pages + n_local_pages > budget_pages) return PS_ERR_BUDGET;
   if (n_splits < 1 || n_splits > budget_pages || n_splits > kMaxSplits) return PS_ERR_BUDGET;
   if (out ? n_splits != 1 : (sink || lse)) return PS_ERR_BUDGET;
-  if (!s.kv_bf16 || s.max_pages > ps::kSelectDecodeMaxPages ||
+  if (s.max_pages > ps::kSelectDecodeMaxPages ||
       (budget_pages + n_splits - 1) / n_splits > ps::kMaxSplitPages)
     return PS_ERR_UNSUPPORTED;
   int64_t t;

@@ -114,13 +114,52 @@ __device__ __forceinline__ void merge_weights(float m1, float m2, float& mo, flo
   a2 = m2 == -INFINITY ? 0.0f : exp2_(m2 - mo);
 }
 
-template <typename T, int D, int G, bool SPARSE>
+// Where a workgroup's pages come from: every page of the request (dense), a
+// page list (sparse), or a selection the workgroup makes itself from the page
+// scores (sparse, fused with the selection: every split of a (request, KV
+// head) runs the same selection and keeps its share of the list).
+enum DecodeMode : int { kDense = 0, kList = 1, kSelect = 2 };
+
+// Selection inputs and outputs of the kSelect mode, and the merged output of
+// a launch with one split.
+struct SelectArgs {
+  const float* scores;  // [B, Hkv, max_pages]
+  int n_sink, n_local;
+  int32_t* sel;        // [B, Hkv, budget] or null
+  int32_t* sel_count;  // [B, Hkv] or null
+  const float* sink;   // [Hq] or null; with out
+  float* out;          // [B, Hq, D] or null: one split, merged output written
+  float* lse;          // [B, Hq] or null
+};
+
+// One split: the merge of ps_combine over that single partial (max m_nat in
+// natural-log units, normaliser lsum, accumulator a at coordinate d of query
+// head `row`), with the same operations (sink in the denominator only).
+__device__ __forceinline__ void write_merged(const SelectArgs& sa, int64_t row, int hq_index,
+                                             int d, int dim, float m_nat, float lsum, float a) {
+  const float sig = sa.sink ? sa.sink[hq_index] : -INFINITY;
+  const float mx = fmax_(m_nat, sig);
+  if (mx == -INFINITY) {
+    sa.out[row * dim + d] = 0.0f;
+    if (sa.lse && d == 0) sa.lse[row] = -INFINITY;
+    return;
+  }
+  float l = m_nat != -INFINITY ? __builtin_fmaf(expf(m_nat - mx), lsum, 0.0f) : 0.0f;
+  if (sig != -INFINITY) l += expf(sig - mx);
+  const float inv = 1.0f / l;
+  const float wgt = m_nat == -INFINITY ? 0.0f : expf(m_nat - mx);
+  sa.out[row * dim + d] = __builtin_fmaf(wgt, a, 0.0f) * inv;
+  if (sa.lse && d == 0) sa.lse[row] = mx + logf(l);
+}
+
+template <typename T, int D, int G, int MODE, int C>
 __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(
     const float* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int budget, int hkv,
     int max_pages, int n_splits, float qscale, float* __restrict__ part_acc,
-    float* __restrict__ part_ml) {
+    float* __restrict__ part_ml, SelectArgs sa) {
+  constexpr bool SPARSE = MODE != kDense;
   using L = RowLayout<T, D>;
   using S = DecodeState<T, D, G>;
   constexpr int V = L::kVec;
@@ -129,6 +168,10 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(
   __shared__ float sm_m[kDecWaves][G];
   __shared__ float sm_l[kDecWaves][G];
   __shared__ float sm_acc[kDecWaves][G][D];
+  // kSelect: the selection's workspace and this split's share of the list
+  __shared__ SelectLds<MODE == kSelect ? kDecWaves : 1> ssel;
+  __shared__ int spages[MODE == kSelect ? kMaxSplitPages : 1];
+  __shared__ int sphys[MODE == kSelect ? kMaxSplitPages : 1];
 
   const int split = blockIdx.x % n_splits;
   const int unit = blockIdx.x / n_splits;  // b * hkv + g
@@ -136,8 +179,32 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(
   const int g = unit % hkv;
   const int len = seq_lens[b];
   const int np = ceil_div(len, kPage);
+  const int32_t* row = page_table + (int64_t)b * max_pages;
   int lo, hi;
-  if constexpr (SPARSE) {
+  if constexpr (MODE == kSelect) {
+    // The whole workgroup selects the unit's pages (with their physical
+    // pages); this split keeps list slots [lo, lo + per) in LDS and writes
+    // them (and the padding among them) to the page list output.
+    const int per = ceil_div(budget, n_splits);
+    lo = split * per;
+    int32_t* dst = sa.sel ? sa.sel + (int64_t)unit * budget : nullptr;
+    const int kept = select_unit<kDecWaves, C, true, false>(
+        sa.scores + (int64_t)unit * max_pages, np, budget, sa.n_sink, sa.n_local, ssel, row,
+        [&](int o, int p, int ph) {
+          if (o >= lo && o < lo + per) {
+            spages[o - lo] = p;
+            sphys[o - lo] = ph;
+            if (dst) dst[o] = p;
+          }
+        });
+    __syncthreads();  // spages complete
+    if (dst)
+      for (int o = max(kept, lo) + (int)threadIdx.x; o < min(lo + per, budget);
+           o += kDecWaves * kWave)
+        dst[o] = -1;
+    if (sa.sel_count && split == 0 && threadIdx.x == 0) sa.sel_count[unit] = kept;
+    hi = min(lo + per, kept);
+  } else if constexpr (SPARSE) {
     const int per = ceil_div(budget, n_splits);
     const int cnt = min(sel_count[unit], budget);
     lo = min(split * per, cnt);
@@ -175,17 +242,26 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(
     for (int j = 0; j < V; ++j) st.acc[h][j] = 0.0f;
   }
 
-  const int32_t* list = SPARSE ? sel + (int64_t)unit * budget : nullptr;
-  const int32_t* row = page_table + (int64_t)b * max_pages;
+  const int32_t* list = MODE == kList ? sel + (int64_t)unit * budget : nullptr;
   const int64_t head_off = (int64_t)g * kPage * D + c * V;
+  // logical and physical page of item i of the split (i in [lo, hi))
+  auto logical = [&](int i) {
+    if constexpr (MODE == kSelect) return spages[i - lo];
+    else return MODE == kList ? list[i] : i;
+  };
+  auto physical = [&](int i, int p) {
+    if constexpr (MODE == kSelect) return sphys[i - lo];
+    else return row[p];
+  };
   for (int it = lo + wave; it < hi; it += 2 * kDecWaves) {
-    const int pa = SPARSE ? list[it] : it;
+    const int pa = logical(it);
     const bool has_b = it + kDecWaves < hi;
-    const int pb = has_b ? (SPARSE ? list[it + kDecWaves] : it + kDecWaves) : pa;
+    const int ib = has_b ? it + kDecWaves : it;
+    const int pb = logical(ib);
     const int cnt_a = min(kPage, len - pa * kPage);
     const int cnt_b = has_b ? min(kPage, len - pb * kPage) : 0;
-    const int64_t base_a = (int64_t)row[pa] * hkv * kPage * D + head_off;
-    const int64_t base_b = (int64_t)row[pb] * hkv * kPage * D + head_off;
+    const int64_t base_a = (int64_t)physical(it, pa) * hkv * kPage * D + head_off;
+    const int64_t base_b = (int64_t)physical(ib, pb) * hkv * kPage * D + head_off;
     uint4 ka[NT], va[NT], kb[NT], vb[NT];
     load_page<T, D, G>(k_pool, v_pool, base_a, cnt_a, r0, ka, va);
     load_page<T, D, G>(k_pool, v_pool, base_b, cnt_b, r0, kb, vb);
@@ -251,10 +327,15 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(
       a = __builtin_fmaf(wt, sm_acc[w][h][d], a);
       lsum = __builtin_fmaf(wt, sm_l[w][h], lsum);
     }
+    const float m_nat = mo == -INFINITY ? -INFINITY : mo * kLn2;
+    if (MODE == kSelect && sa.out) {
+      write_merged(sa, (int64_t)b * hq + g * G + h, g * G + h, d, D, m_nat, lsum, a);
+      continue;
+    }
     const int64_t ph = ((int64_t)b * hq + g * G + h) * n_splits + split;
     part_acc[ph * D + d] = a;
     if (d == 0) {
-      part_ml[ph * 2 + 0] = mo == -INFINITY ? -INFINITY : mo * kLn2;
+      part_ml[ph * 2 + 0] = m_nat;
       part_ml[ph * 2 + 1] = lsum;
     }
   }
@@ -289,23 +370,6 @@ struct PageRef {
 };
 
 
-// Where a workgroup's pages come from: every page of the request (dense), a
-// page list (sparse), or a selection the workgroup makes itself from the page
-// scores (sparse, fused with the selection: every split of a (request, KV
-// head) runs the same selection and keeps its share of the list).
-enum DecodeMode : int { kDense = 0, kList = 1, kSelect = 2 };
-
-// Selection inputs and outputs of the kSelect mode, and the merged output of
-// a launch with one split.
-struct SelectArgs {
-  const float* scores;  // [B, Hkv, max_pages]
-  int n_sink, n_local;
-  int32_t* sel;        // [B, Hkv, budget] or null
-  int32_t* sel_count;  // [B, Hkv] or null
-  const float* sink;   // [Hq] or null; with out
-  float* out;          // [B, Hq, D] or null: one split, merged output written
-  float* lse;          // [B, Hq] or null
-};
 
 // Wavefronts per workgroup: 8 when the launch has at most one workgroup per
 // compute unit (256), else 4.
@@ -610,22 +674,7 @@ void decode_mfma_kernel(
     }
     const float m_nat = mo == -INFINITY ? -INFINITY : mo * kLn2;
     if (sa.out) {
-      // One split: the merge of ps_combine over that single partial, with
-      // the same operations (sink in the denominator only).
-      const int64_t row = (int64_t)b * hq + g * G + h;
-      const float sig = sa.sink ? sa.sink[g * G + h] : -INFINITY;
-      const float mx = fmax_(m_nat, sig);
-      if (mx == -INFINITY) {
-        sa.out[row * D + d] = 0.0f;
-        if (sa.lse && d == 0) sa.lse[row] = -INFINITY;
-        continue;
-      }
-      float l = m_nat != -INFINITY ? __builtin_fmaf(expf(m_nat - mx), lsum, 0.0f) : 0.0f;
-      if (sig != -INFINITY) l += expf(sig - mx);
-      const float inv = 1.0f / l;
-      const float wgt = m_nat == -INFINITY ? 0.0f : expf(m_nat - mx);
-      sa.out[row * D + d] = __builtin_fmaf(wgt, a, 0.0f) * inv;
-      if (sa.lse && d == 0) sa.lse[row] = mx + logf(l);
+      write_merged(sa, (int64_t)b * hq + g * G + h, g * G + h, d, D, m_nat, lsum, a);
       continue;
     }
     const int64_t ph = ((int64_t)b * hq + g * G + h) * n_splits + split;
@@ -645,8 +694,8 @@ hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(kDecWaves * kWave);
   const float qscale = scale * 1.44269504088896340736f;  // log2(e)
+  const SelectArgs none{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
   if (s.kv_bf16) {
-    const SelectArgs none{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
     const int waves = decode_waves(blocks);
     const dim3 wblock(waves * kWave);
 #define PS_DECODE_MFMA(DD, MM, WW)                                                             \
@@ -675,15 +724,15 @@ hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void
   PS_WITH_KV(false, s.head_dim, {
     PS_WITH_GROUP(s.group, {
       if (sparse) {
-        hipLaunchKernelGGL((decode_kernel<TElem, kD, kG, true>), grid, block, 0, st, q,
+        hipLaunchKernelGGL((decode_kernel<TElem, kD, kG, kList, 1>), grid, block, 0, st, q,
                            static_cast<const TElem*>(k_pool), static_cast<const TElem*>(v_pool),
                            page_table, seq_lens, sel, sel_count, budget, s.hkv, s.max_pages,
-                           n_splits, qscale, part_acc, part_ml);
+                           n_splits, qscale, part_acc, part_ml, none);
       } else {
-        hipLaunchKernelGGL((decode_kernel<TElem, kD, kG, false>), grid, block, 0, st, q,
+        hipLaunchKernelGGL((decode_kernel<TElem, kD, kG, kDense, 1>), grid, block, 0, st, q,
                            static_cast<const TElem*>(k_pool), static_cast<const TElem*>(v_pool),
                            page_table, seq_lens, nullptr, nullptr, 0, s.hkv, s.max_pages,
-                           n_splits, qscale, part_acc, part_ml);
+                           n_splits, qscale, part_acc, part_ml, none);
       }
     });
   });
@@ -698,13 +747,37 @@ hipError_t launch_select_decode(const Shape& s, const float* q, const void* k_po
                                 const float* sink, float* out, float* lse, hipStream_t st) {
   const int64_t blocks = (int64_t)s.batch * s.hkv * n_splits;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (!s.kv_bf16 || s.max_pages > kSelectDecodeMaxPages ||
+  if (s.max_pages > kSelectDecodeMaxPages ||
       (budget + n_splits - 1) / n_splits > kMaxSplitPages || (out && n_splits != 1))
     return hipErrorInvalidValue;
-  const int waves = decode_waves(blocks);
-  const dim3 grid((unsigned)blocks), block(waves * kWave);
   const float qscale = scale * 1.44269504088896340736f;  // log2(e)
   const SelectArgs sa{scores, n_sink, n_local, sel, sel_count, sink, out, lse};
+  if (!s.kv_bf16) {  // fp32 K/V: the vector-ALU decode, 4 wavefronts
+    const dim3 grid((unsigned)blocks), block(kDecWaves * kWave);
+    const int per_lane = (s.max_pages + kDecWaves * kWave - 1) / (kDecWaves * kWave);
+#define PS_SELECT_DECODE_F32(DD, CC)                                                         \
+  hipLaunchKernelGGL((decode_kernel<float, DD, kG, kSelect, CC>), grid, block, 0, st, q,     \
+                     static_cast<const float*>(k_pool), static_cast<const float*>(v_pool),  \
+                     page_table, seq_lens, nullptr, nullptr, budget, s.hkv, s.max_pages,    \
+                     n_splits, qscale, part_acc, part_ml, sa)
+#define PS_SELECT_DECODE_F32_C(DD)                          \
+  do {                                                      \
+    if (per_lane <= 2) PS_SELECT_DECODE_F32(DD, 2);         \
+    else if (per_lane <= 8) PS_SELECT_DECODE_F32(DD, 8);    \
+    else PS_SELECT_DECODE_F32(DD, 32);                      \
+  } while (0)
+    PS_WITH_GROUP(s.group, {
+      if (s.head_dim == 64)
+        PS_SELECT_DECODE_F32_C(64);
+      else
+        PS_SELECT_DECODE_F32_C(128);
+    });
+#undef PS_SELECT_DECODE_F32_C
+#undef PS_SELECT_DECODE_F32
+    return hipGetLastError();
+  }
+  const int waves = decode_waves(blocks);
+  const dim3 grid((unsigned)blocks), block(waves * kWave);
   const int per_lane = (s.max_pages + waves * kWave - 1) / (waves * kWave);
 #define PS_SELECT_DECODE(DD, CC, WW)                                                          \
   hipLaunchKernelGGL((decode_mfma_kernel<DD, kG, kSelect, CC, WW, 2>), grid,                   \

@@ -14,7 +14,11 @@
 // consecutive logical pages of one (request, KV head); within a wavefront,
 // lane = (page slot, column vector); a page's kmax and kmin rows are read as
 // coalesced 16-byte vectors, several pages per wave-load, and all loads of a
-// wavefront's pages are issued before any arithmetic.
+// wavefront's pages are issued before any arithmetic. In its refresh variant
+// the wavefront holding a request's last page also reads that page's keys,
+// folds them with the lane layout of the scoring (lane = (row, column
+// vector)), writes the page's metadata and scores the page from the folded
+// registers.
 #include <algorithm>
 
 #include "ps_device.h"
@@ -34,11 +38,12 @@ struct ScoreCfg {
   static constexpr int kPagesPerBlock = kPagesPerWave * kScoreWaves;
 };
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool REFRESH>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
     const float* __restrict__ q, const T* __restrict__ meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
-    int max_pages, int chunks_per_unit, float* __restrict__ scores) {
+    int max_pages, int chunks_per_unit, float* __restrict__ scores,
+    const T* __restrict__ k_pool, T* meta_out) {
   using C = ScoreCfg<T, D>;
   using L = typename C::L;
   constexpr int V = L::kVec;
@@ -52,7 +57,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   const int chunk = (blockIdx.x % chunks_per_unit + unit / hkv) % chunks_per_unit;
   const int b = unit / hkv;
   const int g = unit % hkv;
-  const int np = ceil_div(seq_lens[b], kPage);
+  const int len = seq_lens[b];
+  const int np = ceil_div(len, kPage);
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int p0 = chunk * C::kPagesPerBlock + wave * C::kPagesPerWave;
@@ -76,6 +82,16 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
     }
   }
 
+  // The last page's keys, when this wavefront holds it (p0 <= np - 1 here).
+  const int tail = np - 1;
+  const bool has_tail = REFRESH && tail < p0 + C::kPagesPerWave;  // uniform
+  PageFold<T, D> tail_keys;
+  int64_t tail_base = 0;
+  if (has_tail) {
+    tail_base = (int64_t)page_table[(int64_t)b * max_pages + tail] * hkv + g;
+    tail_keys.load(k_pool + tail_base * kPage * D, lane);
+  }
+
   // Split query coordinates by sign: qp = max(q, 0) multiplies kmax,
   // qn = min(q, 0) multiplies kmin.
   float qp[G][V], qn[G][V];
@@ -94,12 +110,29 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
     }
   }
 
+  // The last page's metadata, folded from its keys: lane (row r0, column
+  // vector c) ends with columns c of both bounds, the columns it scores.
+  float tx[V], tn[V];
+  if (has_tail) {
+    tail_keys.fold(len - tail * kPage, lane, tx, tn);
+    if (slot < 2)
+      st16(meta_out + tail_base * 2 * D + slot * D + c * V, slot == 0 ? pack(tx) : pack(tn));
+  }
+
   float* out = scores + (int64_t)unit * max_pages;
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
+    const int p = p0 + it * C::kPagesPerLoad + slot;
     float kx[V], kn[V];
     unpack(vmax[it], kx);
     unpack(vmin[it], kn);
+    if (has_tail && p == tail) {
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        kx[j] = tx[j];
+        kn[j] = tn[j];
+      }
+    }
     float best = -INFINITY;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -112,7 +145,6 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
       acc = group_sum<LPR>(acc);
       best = fmax_(best, acc);
     }
-    const int p = p0 + it * C::kPagesPerLoad + slot;
     if (c == 0 && p < np) out[p] = best;
   }
 }
@@ -424,17 +456,23 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
 #undef PS_SCORE_MFMA
     return hipGetLastError();
   }
-  if (k_pool) return hipErrorInvalidValue;  // the refresh is bf16 only
   PS_WITH_KV(false, s.head_dim, {
     const int per_block = ScoreCfg<TElem, kD>::kPagesPerBlock;
     const int chunks = (s.max_pages + per_block - 1) / per_block;
     const int64_t blocks = (int64_t)chunks * s.batch * s.hkv;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const dim3 grid((unsigned)blocks);
+    const TElem* kp = static_cast<const TElem*>(k_pool);
+    TElem* mo = static_cast<TElem*>(meta_out);
     PS_WITH_GROUP(s.group, {
-      hipLaunchKernelGGL((score_pages_kernel<TElem, kD, kG>), grid, block, 0, st, q,
-                         static_cast<const TElem*>(meta), page_table, seq_lens, s.hkv,
-                         s.max_pages, chunks, scores);
+      if (kp)
+        hipLaunchKernelGGL((score_pages_kernel<TElem, kD, kG, true>), grid, block, 0, st, q,
+                           static_cast<const TElem*>(meta), page_table, seq_lens, s.hkv,
+                           s.max_pages, chunks, scores, kp, mo);
+      else
+        hipLaunchKernelGGL((score_pages_kernel<TElem, kD, kG, false>), grid, block, 0, st, q,
+                           static_cast<const TElem*>(meta), page_table, seq_lens, s.hkv,
+                           s.max_pages, chunks, scores, kp, mo);
     });
   });
   return hipGetLastError();

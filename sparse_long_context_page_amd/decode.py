@@ -65,22 +65,15 @@ class DecodeStep:
         ops.ps_build_page_meta(self.g, k_pool, page_table, seq_lens, tail_begin, 1, meta, stream)
 
     def sparse(self, q, k_pool, v_pool, meta, page_table, seq_lens, sink=None, stream=None,
-               refresh_tail=False, tail_begin=None):
+               refresh_tail=False):
         """Score, select, decode and merge. With refresh_tail the metadata of
-        each request's last page is rebuilt first: inside the score launch on
-        the fused path and for top-delta selection (bf16 pools), else by
-        ps_build_page_meta from tail_begin[b] = n_b - 1 (a device int32
-        tensor the caller provides)."""
+        each request's last page is rebuilt inside the score launch
+        (ps_refresh_score_pages)."""
         g = self.g
-        in_score = self.fused or (self.delta is not None and g.kv_dtype == torch.bfloat16)
-        if refresh_tail and in_score:
+        if refresh_tail:
             ops.ps_refresh_score_pages(g, q, k_pool, meta, page_table, seq_lens, self.scores,
                                        stream)
         else:
-            if refresh_tail:
-                if tail_begin is None:
-                    raise ValueError("the unfused tail refresh needs tail_begin (n_b - 1)")
-                self.refresh_tail_meta(k_pool, page_table, seq_lens, tail_begin, meta, stream)
             ops.ps_score_pages(g, q, meta, page_table, seq_lens, self.scores, stream)
         acc, ml = self.partials(self.n_splits)
         if self.fused and self.n_splits == 1:  # select, decode and merge in one launch

@@ -191,7 +191,7 @@ SELECT_DECODE_MAX_SPLIT_PAGES = 512
 
 
 def select_decode_supported(g: Geometry, budget_pages: int, n_splits: int) -> bool:
-    return (g.kv_dtype == torch.bfloat16 and g.max_pages <= SELECT_DECODE_MAX_PAGES
+    return (g.max_pages <= SELECT_DECODE_MAX_PAGES
             and -(-budget_pages // n_splits) <= SELECT_DECODE_MAX_SPLIT_PAGES)
 
 

@@ -158,8 +158,9 @@ def test_refresh_score_validation():
     g = geom()
     assert lib.ps_refresh_score_pages(g, X, None, X, X, X, X, None) == _lib.PS_ERR_NULL
     assert lib.ps_refresh_score_pages(g, X, X, None, X, X, X, None) == _lib.PS_ERR_NULL
-    assert lib.ps_refresh_score_pages(geom(kv_dtype=_lib.PS_F32), X, X, X, X, X, X, None) == \
-        _lib.PS_ERR_UNSUPPORTED
+    # fp32 pools are accepted (validated, nothing enqueued for an empty batch)
+    assert lib.ps_refresh_score_pages(geom(kv_dtype=_lib.PS_F32, batch=0), X, X, X, X, X, X,
+                                      None) == _lib.PS_OK
     assert lib.ps_refresh_score_pages(geom(batch=0), X, X, X, X, X, X, None) == _lib.PS_OK
 
 
@@ -178,7 +179,8 @@ def test_fused_select_decode_validation():
     assert call(ns=5, nl=4) == _lib.PS_ERR_BUDGET
     assert call(splits=9) == _lib.PS_ERR_BUDGET
     assert call(splits=0) == _lib.PS_ERR_BUDGET
-    assert call(g=geom(kv_dtype=_lib.PS_F32)) == _lib.PS_ERR_UNSUPPORTED
+    assert call(g=geom(kv_dtype=_lib.PS_F32, batch=0)) == _lib.PS_OK
+    assert call(g=geom(kv_dtype=_lib.PS_F32, max_pages=8193)) == _lib.PS_ERR_UNSUPPORTED
     assert call(g=geom(max_pages=8193)) == _lib.PS_ERR_UNSUPPORTED
     assert call(budget=1026, ns=0, nl=0, splits=2) == _lib.PS_ERR_UNSUPPORTED  # 513 per split
     assert call(acc=None) == _lib.PS_ERR_NULL           # partials needed without out

@@ -1,9 +1,11 @@
 """The fused selection + sparse decode (ps_select_sparse_decode) against the
 two launches it replaces (ps_select_topk then ps_sparse_decode): the page
 list, the counts, the split partials and the merged outputs are bitwise
-identical, on the small bf16 workloads (several splits, ragged tails, sink and
-local pages, budgets that cover every page of short requests) and on the
-32 x 64k workload in the benchmark's launch configuration."""
+identical, on the small workloads (bf16 and fp32 pools, several splits,
+ragged tails, sink and local pages, budgets that cover every page of short
+requests), on fp32 pools with longer rows (the selection's larger register
+tiles) and on the 32 x 64k workload in the benchmark's launch
+configuration."""
 
 import pytest
 import torch
@@ -15,7 +17,18 @@ from test_gpu_parity import SMALL
 
 pytestmark = pytest.mark.gpu
 
-BF16 = [w for w in SMALL if w.kv_dtype == "bf16"] + [wl.B32_64K]
+# fp32 pools with rows of 563 and 2500 pages (selection tiles of 8 and 32
+# pages per lane in the 4-wavefront fp32 decode)
+F32_LONG = [
+    wl.Workload("f32_g4_d128_sink_local_rows563", batch=3, num_q_heads=8, num_kv_heads=2,
+                head_dim=128, ctx_range=(2000, 9000), budget_pages=24, n_sink=1, n_local=3,
+                needles=3, sink_logits=True, permuted_pool=True, max_pages=563,
+                kv_dtype="f32", seed=31, n_splits=3, dense_splits=8),
+    wl.Workload("f32_g6_d64_rows2500", batch=2, num_q_heads=12, num_kv_heads=2, head_dim=64,
+                ctx_range=(30000, 40000), budget_pages=40, n_local=2, needles=4,
+                max_pages=2500, kv_dtype="f32", seed=32, n_splits=4, dense_splits=8),
+]
+CASES = SMALL + F32_LONG + [wl.B32_64K]
 
 
 def _both(inp, budget=None, n_sink=None, n_local=None, n_splits=None):
@@ -44,7 +57,7 @@ def _both(inp, budget=None, n_sink=None, n_local=None, n_splits=None):
     return res
 
 
-@pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_fused_equals_unfused_bitwise(w):
     inp = wl.make_inputs(w, device="cuda")
     configs = [dict()]
@@ -76,7 +89,7 @@ def test_fused_without_page_list_output():
     assert torch.equal(acc, a["acc"]) and torch.equal(ml, a["ml"])
 
 
-@pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_fused_one_split_merged_output_bitwise(w):
     """With one split the fused launch also merges (sink in the denominator):
     equal, bit for bit, to the unfused one-split decode followed by
@@ -101,7 +114,7 @@ def test_fused_one_split_merged_output_bitwise(w):
         assert torch.equal(got, want)
 
 
-@pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_refresh_score_equals_meta_then_score_bitwise(w):
     """ps_refresh_score_pages on metadata whose last pages are stale equals
     the full metadata build followed by ps_score_pages, bit for bit (the
@@ -136,8 +149,10 @@ def test_step_with_tail_refresh_fused_equals_unfused():
               enumerate(inp["n_pages_host"])]] = -2.0
         step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
                           inp["scale"], fused=fused)
+        if not fused:  # the tail pages rebuilt by their own launch, then the five launches
+            step.refresh_tail_meta(inp["k_pool"], inp["page_table"], inp["seq_lens"], tail, meta)
         out, lse = step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
-                               inp["seq_lens"], inp["sink"], refresh_tail=True, tail_begin=tail)
+                               inp["seq_lens"], inp["sink"], refresh_tail=fused)
         torch.cuda.synchronize()
         outs.append((meta.clone(), step.sel.clone(), out.clone(), lse.clone()))
     for a, b in zip(*outs):

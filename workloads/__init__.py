@@ -71,7 +71,7 @@ class Workload:
 
 # The five measured workloads. Seeds are 1000 + the workload's ordinal.
 TINY = Workload("tiny", batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, context=1024,
-                budget_pages=8, kv_dtype="f32", seed=1001, n_splits=4, dense_splits=8)
+                budget_pages=8, kv_dtype="f32", seed=1001, n_splits=1, dense_splits=4)
 TINY_DENSE = TINY.replace(name="tiny_dense", budget_pages=64, n_splits=8)
 B8_16K = Workload("b8_16k_needles_sink_page", batch=8, num_q_heads=12, num_kv_heads=2,
                   head_dim=128, context=16384, budget_pages=128, n_sink=1, needles=4,
