@@ -489,8 +489,8 @@ def main():
 
     fused = s0["step"].fused
     kern_us = {}
-    if fused:  # the step's own launches
-        kern_us["refresh_score"] = time_launches(k_refresh_score)
+    kern_us["refresh_score"] = time_launches(k_refresh_score)  # the step's own launches
+    if fused:
         kern_us["select_decode"] = time_launches(k_select_decode)
     kern_us["combine"] = time_launches(k_combine)
     # the unfused entry points, one stage each
@@ -546,14 +546,14 @@ def main():
     dense_b = acc.dense_kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
     step_us = ms_per_step * 1e3
     eff_gbps = touched / (step_us * 1e-6) / 1e9
-    # the dominant kernel: the step's score launch (with the last-page
-    # refresh when fused): metadata of every page read, one fp32 score per
-    # page written, and per (request, KV head) the last page's 16 key rows
-    # read and its metadata written
+    # the dominant kernel: the step's score launch with the last-page
+    # refresh: metadata of every page read, one fp32 score per page written,
+    # and per (request, KV head) the last page's 16 key rows read and its
+    # metadata written
     units = w.batch * w.num_kv_heads
     scores_b = sum(-(-n // w.page_size) for n in lens) * w.num_kv_heads * 4
-    tail_b = (units * (w.page_size * elem + 2 * meta_elem) * w.head_dim) if fused else 0
-    dom_key = "refresh_score" if fused else "score"
+    tail_b = units * (w.page_size * elem + 2 * meta_elem) * w.head_dim
+    dom_key = "refresh_score"
     dom_b = meta_b + scores_b + tail_b
     score_gbps = dom_b / (kern_us[dom_key] * 1e-6) / 1e9
     dec_key = "select_decode" if fused else "sparse_decode"
@@ -587,10 +587,7 @@ def main():
         "touched_bytes": touched,
         "touched_bytes_split": {"metadata": meta_b, "selected_kv": kv_b},
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
-        "step_launches": ((["ps_refresh_score_pages", "ps_select_sparse_decode"] +
-                           ([] if s0["step"].n_splits == 1 else ["ps_combine"]))
-                          if fused else ["ps_build_page_meta", "ps_score_pages",
-                                         "ps_select_topk", "ps_sparse_decode", "ps_combine"]),
+        "step_launches": step_launches(s0["step"]),
         "selection_overhead_us": round(kern_us["select"], 3),
         "selection_in_decode_us": (round(kern_us["select_decode"] - kern_us["sparse_decode"], 3)
                                    if fused else None),
@@ -607,7 +604,7 @@ def main():
         "warm_same_set_us_per_step": round(warm_us, 3),
         "one_step_per_graph_us_per_step": round(one_graph_us, 3),
         "parity": parity,
-        "roofline": {"kernel": "ps_refresh_score_pages" if fused else "ps_score_pages",
+        "roofline": {"kernel": "ps_refresh_score_pages",
                      "bound": "hbm",
                      "achieved": round(score_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
@@ -630,11 +627,22 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def step_launches(step):
+    """The launches of one sparse step (with the tail refresh) in order."""
+    sel = "ps_select_topk" if step.delta is None else "ps_select_topdelta"
+    if step.fused:
+        fused = ("ps_select_sparse_decode" if step.delta is None
+                 else "ps_select_topdelta_sparse_decode")
+        return ["ps_refresh_score_pages", fused] + ([] if step.n_splits == 1 else ["ps_combine"])
+    return ["ps_refresh_score_pages", sel, "ps_sparse_decode", "ps_combine"]
+
+
 def topdelta_line(args, w, sets, step_us_topk, torch, wl, ps):
     """The same inputs with top-delta selection (delta = args.delta): parity
     against the oracle's top-delta rule, the step timed as the main one
-    (refresh+score, top-delta select, sparse decode, merge: four launches),
-    the selection launch on its own, and the pages kept per unit."""
+    (refresh+score, then the top-delta selection fused into the sparse
+    decode, then the merge when there are several splits), the standalone
+    selection launch on its own, and the pages kept per unit."""
     import numpy as np
 
     sets_d = []
@@ -691,8 +699,7 @@ def topdelta_line(args, w, sets, step_us_topk, torch, wl, ps):
             "select_topdelta_us": round(sel_us, 3),
             "kept_pages_per_unit": {"mean": round(float(np.mean(kept)), 2),
                                     "min": int(kept.min()), "max": int(kept.max())},
-            "launches": ["ps_refresh_score_pages", "ps_select_topdelta", "ps_sparse_decode",
-                         "ps_combine"],
+            "launches": step_launches(sets_d[0]["step"]),
             "parity": dict(parity, oracle="top-delta rule")}
 
 
@@ -769,13 +776,9 @@ def profile_only(args, sets, torch, ps):
     for i in range(args.steps):
         s = sets[i % len(sets)]
         inp, step, g = s["inp"], s["step"], s["g"]
-        if args.only_kernel == "score":
-            if step.fused:
-                ps.ps_refresh_score_pages(g, inp["q"], inp["k_pool"], s["meta"],
-                                          inp["page_table"], inp["seq_lens"], step.scores)
-            else:
-                ps.ps_score_pages(g, inp["q"], s["meta"], inp["page_table"], inp["seq_lens"],
-                                  step.scores)
+        if args.only_kernel == "score":  # the step's score launch
+            ps.ps_refresh_score_pages(g, inp["q"], inp["k_pool"], s["meta"], inp["page_table"],
+                                      inp["seq_lens"], step.scores)
         elif args.only_kernel == "step":
             run_sparse_step(s)
         elif args.only_kernel == "copy":

@@ -267,6 +267,28 @@ int ps_select_sparse_decode(const ps_geom* geom, const float* q, const void* k_p
                             float* part_ml, const float* sink, float* out, float* lse,
                             void* stream);
 
+/* 3'+4a. Top-delta selection fused into the sparse decode: one launch does
+ * the work of ps_select_topdelta followed by ps_sparse_decode, with bitwise
+ * the same page list and partials (and, with out, the merge of ps_combine as
+ * in ps_select_sparse_decode). ("Faster Than Flash: Exploiting Attention
+ * Sparsity for Efficient Long-Context Decoding", section "Methodology", item
+ * 2; "Training-free sparse attention for long-context LLM decode", section
+ * "Reusable code": a fused single-launch variant of the sparse decode.)
+ * Every split's workgroup computes the (b, g) threshold from the forced
+ * pages' keys and selects the page list itself.
+ * Arguments as ps_select_sparse_decode, with delta as in ps_select_topdelta.
+ * Host checks: those of ps_select_sparse_decode (same codes), then delta >= 0
+ * and 0 < scale < infinity (else PS_ERR_BUDGET).
+ * Device preconditions: those of ps_select_topdelta and ps_sparse_decode. */
+int ps_select_topdelta_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool,
+                                     const void* v_pool, const int32_t* page_table,
+                                     const int32_t* seq_lens, const float* scores,
+                                     int32_t budget_pages, int32_t n_sink_pages,
+                                     int32_t n_local_pages, float scale, float delta,
+                                     int32_t n_splits, int32_t* sel, int32_t* sel_count,
+                                     float* part_acc, float* part_ml, const float* sink,
+                                     float* out, float* lse, void* stream);
+
 /* 4b. Dense split-KV decode: ps_sparse_decode over every page. Split s of a
  * request covers logical pages [s*c_b, min((s+1)*c_b, n_b)) with
  * c_b = ceil(n_b / n_splits). ("Don't read the haystack", section "Part one:

@@ -16,6 +16,7 @@ from .ops import (  # noqa: F401
     ps_score_pages,
     ps_select_sparse_decode,
     ps_select_topdelta,
+    ps_select_topdelta_sparse_decode,
     ps_select_topk,
     ps_sparse_decode,
     ps_strerror,

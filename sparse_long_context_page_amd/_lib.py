@@ -30,6 +30,7 @@ ENTRY_POINTS = (
     "ps_select_topdelta",
     "ps_sparse_decode",
     "ps_select_sparse_decode",
+    "ps_select_topdelta_sparse_decode",
     "ps_full_decode",
     "ps_combine",
     "ps_strerror",
@@ -80,6 +81,8 @@ _SIGS = {
     "ps_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _P, _I, _F, _I, _P, _P, _P],
     "ps_select_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P, _P, _P,
                                 _P, _P, _P, _P, _P],
+    "ps_select_topdelta_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _F, _I,
+                                         _P, _P, _P, _P, _P, _P, _P, _P],
     "ps_full_decode": [_G, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P],
     "ps_combine": [_G, _P, _P, _I, _P, _P, _P, _P],
     "ps_strerror": [ctypes.c_int],

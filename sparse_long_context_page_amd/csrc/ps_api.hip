@@ -177,6 +177,32 @@ PS_API int ps_sparse_decode(const ps_geom* geom, const float* q, const void* k_p
                                       part_ml, (hipStream_t)stream));
 }
 
+// Host checks shared by the two selecting decodes.
+static int check_select_decode(const ps_geom* geom, ps::Shape* s, const float* q,
+                               const void* k_pool, const void* v_pool,
+                               const int32_t* page_table, const int32_t* seq_lens,
+                               const float* scores, int32_t budget_pages, int32_t n_sink_pages,
+                               int32_t n_local_pages, int32_t n_splits, const int32_t* sel,
+                               const int32_t* sel_count, const float* part_acc,
+                               const float* part_ml, const float* sink, const float* out,
+                               const float* lse) {
+  int rc = check_geom(geom, s);
+  if (rc) return rc;
+  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !scores) return PS_ERR_NULL;
+  if ((sel == nullptr) != (sel_count == nullptr)) return PS_ERR_NULL;
+  if (!out && (!part_acc || !part_ml)) return PS_ERR_NULL;
+  if (budget_pages < 1 || n_sink_pages < 0 || n_local_pages < 0) return PS_ERR_BUDGET;
+  if ((int64_t)n_sink_pages + n_local_pages > budget_pages) return PS_ERR_BUDGET;
+  if (n_splits < 1 || n_splits > budget_pages || n_splits > kMaxSplits) return PS_ERR_BUDGET;
+  if (out ? n_splits != 1 : (sink || lse)) return PS_ERR_BUDGET;
+  if (s->max_pages > ps::kSelectDecodeMaxPages ||
+      (budget_pages + n_splits - 1) / n_splits > ps::kMaxSplitPages)
+    return PS_ERR_UNSUPPORTED;
+  int64_t t;
+  if (!prod_ok({s->batch, s->hkv, budget_pages, 4}, &t)) return PS_ERR_OVERFLOW;
+  return check_partials(*s, n_splits);
+}
+
 PS_API int ps_select_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool,
                                    const void* v_pool, const int32_t* page_table,
                                    const int32_t* seq_lens, const float* scores,
@@ -186,27 +212,37 @@ PS_API int ps_select_sparse_decode(const ps_geom* geom, const float* q, const vo
                                    float* part_ml, const float* sink, float* out, float* lse,
                                    void* stream) {
   ps::Shape s;
-  int rc = check_geom(geom, &s);
-  if (rc) return rc;
-  if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !scores) return PS_ERR_NULL;
-  if ((sel == nullptr) != (sel_count == nullptr)) return PS_ERR_NULL;
-  if (!out && (!part_acc || !part_ml)) return PS_ERR_NULL;
-  if (budget_pages < 1 || n_sink_pages < 0 || n_local_pages < 0) return PS_ERR_BUDGET;
-  if ((int64_t)n_sink_pages + n_local_pages > budget_pages) return PS_ERR_BUDGET;
-  if (n_splits < 1 || n_splits > budget_pages || n_splits > kMaxSplits) return PS_ERR_BUDGET;
-  if (out ? n_splits != 1 : (sink || lse)) return PS_ERR_BUDGET;
-  if (s.max_pages > ps::kSelectDecodeMaxPages ||
-      (budget_pages + n_splits - 1) / n_splits > ps::kMaxSplitPages)
-    return PS_ERR_UNSUPPORTED;
-  int64_t t;
-  if (!prod_ok({s.batch, s.hkv, budget_pages, 4}, &t)) return PS_ERR_OVERFLOW;
-  rc = check_partials(s, n_splits);
+  const int rc = check_select_decode(geom, &s, q, k_pool, v_pool, page_table, seq_lens, scores,
+                                     budget_pages, n_sink_pages, n_local_pages, n_splits, sel,
+                                     sel_count, part_acc, part_ml, sink, out, lse);
   if (rc) return rc;
   if (s.batch == 0) return PS_OK;
   return hip_status(ps::launch_select_decode(s, q, k_pool, v_pool, page_table, seq_lens, scores,
                                              budget_pages, n_sink_pages, n_local_pages, scale,
                                              n_splits, sel, sel_count, part_acc, part_ml, sink,
                                              out, lse, (hipStream_t)stream));
+}
+
+PS_API int ps_select_topdelta_sparse_decode(const ps_geom* geom, const float* q,
+                                            const void* k_pool, const void* v_pool,
+                                            const int32_t* page_table, const int32_t* seq_lens,
+                                            const float* scores, int32_t budget_pages,
+                                            int32_t n_sink_pages, int32_t n_local_pages,
+                                            float scale, float delta, int32_t n_splits,
+                                            int32_t* sel, int32_t* sel_count, float* part_acc,
+                                            float* part_ml, const float* sink, float* out,
+                                            float* lse, void* stream) {
+  ps::Shape s;
+  const int rc = check_select_decode(geom, &s, q, k_pool, v_pool, page_table, seq_lens, scores,
+                                     budget_pages, n_sink_pages, n_local_pages, n_splits, sel,
+                                     sel_count, part_acc, part_ml, sink, out, lse);
+  if (rc) return rc;
+  if (!(delta >= 0.0f) || !(scale > 0.0f) || !(scale < INFINITY)) return PS_ERR_BUDGET;
+  if (s.batch == 0) return PS_OK;
+  return hip_status(ps::launch_select_topdelta_decode(
+      s, q, k_pool, v_pool, page_table, seq_lens, scores, budget_pages, n_sink_pages,
+      n_local_pages, scale, delta, n_splits, sel, sel_count, part_acc, part_ml, sink, out, lse,
+      (hipStream_t)stream));
 }
 
 PS_API int ps_full_decode(const ps_geom* geom, const float* q, const void* k_pool,
@@ -254,4 +290,4 @@ PS_API const char* ps_strerror(int status) {
   }
 }
 
-PS_API int ps_abi_version(void) { return (1 << 16) | 4; }  // 1.4: top-delta selection
+PS_API int ps_abi_version(void) { return (1 << 16) | 5; }  // 1.5: top-delta selecting decode

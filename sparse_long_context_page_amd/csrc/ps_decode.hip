@@ -1,690 +1,8 @@
-// Split-KV decode over a page list (sparse) or over every page (dense):
-// per split, the running max, normaliser and unnormalised accumulator of the
-// softmax of scale*q.k for every query head of one KV head.
-// ("Don't read the haystack", sections "Part one: hitting the wall on
-// purpose" and "Part two: the skipping"; "Attention: Undivided &
-// Uncompressed", section "Traffic", for the rescaling merge.)
-//
-// One workgroup of 4 wavefronts per (request, KV head, split). The split's
-// pages are dealt round-robin to the wavefronts, two pages in flight per
-// wavefront. A page's 16 K rows and 16 V rows are read with coalesced
-// 16-byte loads, lane = (row group, column vector); the page table (and the
-// page list) is read per page, so physical pages may be anywhere and in any
-// order. Each lane keeps a private softmax state over its own tokens (all G
-// heads), rescaling lazily only when a page raises its running max by more
-// than 8 (log2 units), so the common path has no cross-lane max and no
-// rescale; the true max is tracked alongside and restored as the state's
-// reference at the end, so each written max is the split's. States are merged
-// across row groups with shuffles and across wavefronts through LDS, then
-// written as fp32 partials (max in natural-log units).
-#include "ps_device.h"
-#include "ps_launch.h"
-#include "ps_select.h"
+// Launches of the split-KV decode over a page list or over every page
+// (kernels in ps_decode.h).
+#include "ps_decode.h"
 
 namespace ps {
-
-constexpr int kDecWaves = 4;
-constexpr float kLazyRescale = 8.0f;  // log2 headroom before the running max is raised
-constexpr float kLn2 = 0.69314718055994530942f;
-
-template <typename T, int D, int G>
-struct DecodeState {
-  using L = RowLayout<T, D>;
-  static constexpr int V = L::kVec;
-  static constexpr int NT = L::kLoadsPerPage;  // tokens per lane per page
-  // m: reference max of the state (at most kLazyRescale below the true max);
-  // mt: true running max, restored as the reference before the state leaves.
-  float m[G], mt[G], l[G], acc[G][V];
-};
-
-template <typename T, int D, int G>
-__device__ __forceinline__ void load_page(const T* __restrict__ k_pool, const T* __restrict__ v_pool,
-                                          int64_t base, int cnt, int r0,
-                                          uint4 (&kv)[DecodeState<T, D, G>::NT],
-                                          uint4 (&vv)[DecodeState<T, D, G>::NT]) {
-  using L = RowLayout<T, D>;
-#pragma unroll
-  for (int i = 0; i < L::kLoadsPerPage; ++i) {
-    const int t = r0 + i * L::kRowsPerLoad;
-    if (t < cnt) {
-      kv[i] = ld16(k_pool + base + (int64_t)t * D);
-      vv[i] = ld16(v_pool + base + (int64_t)t * D);
-    } else {
-      kv[i] = make_uint4(0, 0, 0, 0);
-      vv[i] = make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-template <typename T, int D, int G>
-__device__ __forceinline__ void attend_page(DecodeState<T, D, G>& st,
-                                            const float (&qs)[G][DecodeState<T, D, G>::V],
-                                            const uint4 (&kv)[DecodeState<T, D, G>::NT],
-                                            const uint4 (&vv)[DecodeState<T, D, G>::NT], int cnt,
-                                            int r0) {
-  using L = RowLayout<T, D>;
-  constexpr int V = L::kVec;
-  constexpr int NT = L::kLoadsPerPage;
-  float x[NT][G];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) {
-    float kf[V];
-    unpack(kv[i], kf);
-    const bool valid = r0 + i * L::kRowsPerLoad < cnt;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float d = 0.0f;
-#pragma unroll
-      for (int j = 0; j < V; ++j) d = __builtin_fmaf(qs[h][j], kf[j], d);
-      d = group_sum<L::kLanesPerRow>(d);
-      x[i][h] = valid ? d : -INFINITY;
-    }
-  }
-  float vf[NT][V];
-#pragma unroll
-  for (int i = 0; i < NT; ++i) unpack(vv[i], vf[i]);
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float mp = x[0][h];
-#pragma unroll
-    for (int i = 1; i < NT; ++i) mp = fmax_(mp, x[i][h]);
-    st.mt[h] = fmax_(st.mt[h], mp);
-    if (mp > st.m[h] + kLazyRescale) {  // also taken when the state is empty (-inf)
-      const float a = exp2_(st.m[h] - mp);
-      st.l[h] *= a;
-#pragma unroll
-      for (int j = 0; j < V; ++j) st.acc[h][j] *= a;
-      st.m[h] = mp;
-    }
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const float pr = x[i][h] == -INFINITY ? 0.0f : exp2_(x[i][h] - st.m[h]);
-      st.l[h] += pr;
-#pragma unroll
-      for (int j = 0; j < V; ++j) st.acc[h][j] = __builtin_fmaf(pr, vf[i][j], st.acc[h][j]);
-    }
-  }
-}
-
-// Merge two softmax states (log2 units); an empty state has m = -inf, l = 0.
-__device__ __forceinline__ void merge_weights(float m1, float m2, float& mo, float& a1,
-                                              float& a2) {
-  mo = fmax_(m1, m2);
-  a1 = m1 == -INFINITY ? 0.0f : exp2_(m1 - mo);
-  a2 = m2 == -INFINITY ? 0.0f : exp2_(m2 - mo);
-}
-
-// Where a workgroup's pages come from: every page of the request (dense), a
-// page list (sparse), or a selection the workgroup makes itself from the page
-// scores (sparse, fused with the selection: every split of a (request, KV
-// head) runs the same selection and keeps its share of the list).
-enum DecodeMode : int { kDense = 0, kList = 1, kSelect = 2 };
-
-// Selection inputs and outputs of the kSelect mode, and the merged output of
-// a launch with one split.
-struct SelectArgs {
-  const float* scores;  // [B, Hkv, max_pages]
-  int n_sink, n_local;
-  int32_t* sel;        // [B, Hkv, budget] or null
-  int32_t* sel_count;  // [B, Hkv] or null
-  const float* sink;   // [Hq] or null; with out
-  float* out;          // [B, Hq, D] or null: one split, merged output written
-  float* lse;          // [B, Hq] or null
-};
-
-// One split: the merge of ps_combine over that single partial (max m_nat in
-// natural-log units, normaliser lsum, accumulator a at coordinate d of query
-// head `row`), with the same operations (sink in the denominator only).
-__device__ __forceinline__ void write_merged(const SelectArgs& sa, int64_t row, int hq_index,
-                                             int d, int dim, float m_nat, float lsum, float a) {
-  const float sig = sa.sink ? sa.sink[hq_index] : -INFINITY;
-  const float mx = fmax_(m_nat, sig);
-  if (mx == -INFINITY) {
-    sa.out[row * dim + d] = 0.0f;
-    if (sa.lse && d == 0) sa.lse[row] = -INFINITY;
-    return;
-  }
-  float l = m_nat != -INFINITY ? __builtin_fmaf(expf(m_nat - mx), lsum, 0.0f) : 0.0f;
-  if (sig != -INFINITY) l += expf(sig - mx);
-  const float inv = 1.0f / l;
-  const float wgt = m_nat == -INFINITY ? 0.0f : expf(m_nat - mx);
-  sa.out[row * dim + d] = __builtin_fmaf(wgt, a, 0.0f) * inv;
-  if (sa.lse && d == 0) sa.lse[row] = mx + logf(l);
-}
-
-template <typename T, int D, int G, int MODE, int C>
-__global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(
-    const float* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
-    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ sel_count, int budget, int hkv,
-    int max_pages, int n_splits, float qscale, float* __restrict__ part_acc,
-    float* __restrict__ part_ml, SelectArgs sa) {
-  constexpr bool SPARSE = MODE != kDense;
-  using L = RowLayout<T, D>;
-  using S = DecodeState<T, D, G>;
-  constexpr int V = L::kVec;
-  constexpr int LPR = L::kLanesPerRow;
-  constexpr int NT = S::NT;
-  __shared__ float sm_m[kDecWaves][G];
-  __shared__ float sm_l[kDecWaves][G];
-  __shared__ float sm_acc[kDecWaves][G][D];
-  // kSelect: the selection's workspace and this split's share of the list
-  __shared__ SelectLds<MODE == kSelect ? kDecWaves : 1> ssel;
-  __shared__ int spages[MODE == kSelect ? kMaxSplitPages : 1];
-  __shared__ int sphys[MODE == kSelect ? kMaxSplitPages : 1];
-
-  const int split = blockIdx.x % n_splits;
-  const int unit = blockIdx.x / n_splits;  // b * hkv + g
-  const int b = unit / hkv;
-  const int g = unit % hkv;
-  const int len = seq_lens[b];
-  const int np = ceil_div(len, kPage);
-  const int32_t* row = page_table + (int64_t)b * max_pages;
-  int lo, hi;
-  if constexpr (MODE == kSelect) {
-    // The whole workgroup selects the unit's pages (with their physical
-    // pages); this split keeps list slots [lo, lo + per) in LDS and writes
-    // them (and the padding among them) to the page list output.
-    const int per = ceil_div(budget, n_splits);
-    lo = split * per;
-    int32_t* dst = sa.sel ? sa.sel + (int64_t)unit * budget : nullptr;
-    const int kept = select_unit<kDecWaves, C, true, false>(
-        sa.scores + (int64_t)unit * max_pages, np, budget, sa.n_sink, sa.n_local, ssel, row,
-        [&](int o, int p, int ph) {
-          if (o >= lo && o < lo + per) {
-            spages[o - lo] = p;
-            sphys[o - lo] = ph;
-            if (dst) dst[o] = p;
-          }
-        });
-    __syncthreads();  // spages complete
-    if (dst)
-      for (int o = max(kept, lo) + (int)threadIdx.x; o < min(lo + per, budget);
-           o += kDecWaves * kWave)
-        dst[o] = -1;
-    if (sa.sel_count && split == 0 && threadIdx.x == 0) sa.sel_count[unit] = kept;
-    hi = min(lo + per, kept);
-  } else if constexpr (SPARSE) {
-    const int per = ceil_div(budget, n_splits);
-    const int cnt = min(sel_count[unit], budget);
-    lo = min(split * per, cnt);
-    hi = min(split * per + per, cnt);
-  } else {
-    const int per = ceil_div(np, n_splits);
-    lo = min(split * per, np);
-    hi = min(split * per + per, np);
-  }
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
-  const int r0 = lane / LPR;
-  const int c = lane % LPR;
-
-  float qs[G][V];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float* qh = q + ((int64_t)b * hkv * G + g * G + h) * D + c * V;
-#pragma unroll
-    for (int j = 0; j < V; j += 4) {
-      const float4 v4 = *reinterpret_cast<const float4*>(qh + j);
-      qs[h][j + 0] = v4.x * qscale;
-      qs[h][j + 1] = v4.y * qscale;
-      qs[h][j + 2] = v4.z * qscale;
-      qs[h][j + 3] = v4.w * qscale;
-    }
-  }
-  S st;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    st.m[h] = -INFINITY;
-    st.mt[h] = -INFINITY;
-    st.l[h] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < V; ++j) st.acc[h][j] = 0.0f;
-  }
-
-  const int32_t* list = MODE == kList ? sel + (int64_t)unit * budget : nullptr;
-  const int64_t head_off = (int64_t)g * kPage * D + c * V;
-  // logical and physical page of item i of the split (i in [lo, hi))
-  auto logical = [&](int i) {
-    if constexpr (MODE == kSelect) return spages[i - lo];
-    else return MODE == kList ? list[i] : i;
-  };
-  auto physical = [&](int i, int p) {
-    if constexpr (MODE == kSelect) return sphys[i - lo];
-    else return row[p];
-  };
-  for (int it = lo + wave; it < hi; it += 2 * kDecWaves) {
-    const int pa = logical(it);
-    const bool has_b = it + kDecWaves < hi;
-    const int ib = has_b ? it + kDecWaves : it;
-    const int pb = logical(ib);
-    const int cnt_a = min(kPage, len - pa * kPage);
-    const int cnt_b = has_b ? min(kPage, len - pb * kPage) : 0;
-    const int64_t base_a = (int64_t)physical(it, pa) * hkv * kPage * D + head_off;
-    const int64_t base_b = (int64_t)physical(ib, pb) * hkv * kPage * D + head_off;
-    uint4 ka[NT], va[NT], kb[NT], vb[NT];
-    load_page<T, D, G>(k_pool, v_pool, base_a, cnt_a, r0, ka, va);
-    load_page<T, D, G>(k_pool, v_pool, base_b, cnt_b, r0, kb, vb);
-    attend_page<T, D, G>(st, qs, ka, va, cnt_a, r0);
-    if (has_b) attend_page<T, D, G>(st, qs, kb, vb, cnt_b, r0);
-  }
-
-  // Re-reference each state to its true max, so the written max is exact.
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    if (st.mt[h] > st.m[h]) {
-      const float a = exp2_(st.m[h] - st.mt[h]);
-      st.l[h] *= a;
-#pragma unroll
-      for (int j = 0; j < V; ++j) st.acc[h][j] *= a;
-      st.m[h] = st.mt[h];
-    }
-  }
-  // Merge the row groups of this wavefront (lanes sharing a column vector).
-#pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float m2 = __shfl_xor(st.m[h], off);
-      const float l2 = __shfl_xor(st.l[h], off);
-      float mo, a1, a2;
-      merge_weights(st.m[h], m2, mo, a1, a2);
-      st.l[h] = st.l[h] * a1 + l2 * a2;
-#pragma unroll
-      for (int j = 0; j < V; ++j) {
-        const float o2 = __shfl_xor(st.acc[h][j], off);
-        st.acc[h][j] = st.acc[h][j] * a1 + o2 * a2;
-      }
-      st.m[h] = mo;
-    }
-  }
-  if (r0 == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int j = 0; j < V; ++j) sm_acc[wave][h][c * V + j] = st.acc[h][j];
-      if (c == 0) {
-        sm_m[wave][h] = st.m[h];
-        sm_l[wave][h] = st.l[h];
-      }
-    }
-  }
-  __syncthreads();
-
-  // Merge the wavefronts and write this split's partials.
-  const int hq = hkv * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecWaves * kWave) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float mo = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) mo = fmax_(mo, sm_m[w][h]);
-    float a = 0.0f, lsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kDecWaves; ++w) {
-      const float mw = sm_m[w][h];
-      const float wt = mw == -INFINITY ? 0.0f : exp2_(mw - mo);
-      a = __builtin_fmaf(wt, sm_acc[w][h][d], a);
-      lsum = __builtin_fmaf(wt, sm_l[w][h], lsum);
-    }
-    const float m_nat = mo == -INFINITY ? -INFINITY : mo * kLn2;
-    if (MODE == kSelect && sa.out) {
-      write_merged(sa, (int64_t)b * hq + g * G + h, g * G + h, d, D, m_nat, lsum, a);
-      continue;
-    }
-    const int64_t ph = ((int64_t)b * hq + g * G + h) * n_splits + split;
-    part_acc[ph * D + d] = a;
-    if (d == 0) {
-      part_ml[ph * 2 + 0] = m_nat;
-      part_ml[ph * 2 + 1] = lsum;
-    }
-  }
-}
-
-// bf16 K/V: q.k on the matrix cores. A page (16 tokens) is one
-// v_mfma_f32_16x16x32_bf16 row block: A = K (row = token, the 8 contraction
-// coordinates of a lane are 8 consecutive d of one 16-byte load straight from
-// the pool), B = the group's queries scaled by scale*log2(e) (column = head,
-// padded to 16 with zeros), split exactly into hi + mid + lo bf16 terms in
-// LDS once per workgroup and read from there as each product is issued. Lane (token group, head) then holds 4 logits of one
-// head; the page max per head is a 3-step shuffle, the running max is uniform
-// per head and raised lazily (by more than 8 in log2 units), and p =
-// 2^(x - m) is handed to the V owners through LDS. P.V runs on the vector
-// ALUs with V in row layout (lane = (row group, 8 columns)), every lane
-// accumulating all G heads for its rows and columns. The queries are
-// requested first; each wavefront resolves its page ids (list entry, then
-// table entry) a block of 4 ahead, keeps the next page's K and V in flight
-// while the current page is attended, and leaves its accumulators unreduced
-// in LDS for the workgroup merge (no cross-row shuffles).
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// A page as the decode sees it: valid token count (0 = none) and its
-// physical page.
-struct PageRef {
-  int cnt;
-  int phys;
-};
-
-
-
-// Wavefronts per workgroup: 8 when the launch has at most one workgroup per
-// compute unit (256), else 4.
-inline int decode_waves(int64_t blocks) { return blocks <= 256 ? 8 : 4; }
-
-// P: pages in flight per wavefront (its K and V rows held in registers).
-template <int D, int G, int MODE, int C, int W, int P>
-__global__ __launch_bounds__(W * kWave, W == 8 ? 1 : ((MODE == kSelect && D == 128) ? 2 : 3))
-void decode_mfma_kernel(
-    const float* __restrict__ q, const bf16_t* __restrict__ k_pool,
-    const bf16_t* __restrict__ v_pool, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ sel,
-    const int32_t* __restrict__ sel_count, int budget, int hkv, int max_pages, int n_splits,
-    float qscale, float* __restrict__ part_acc, float* __restrict__ part_ml, SelectArgs sa) {
-  constexpr bool SPARSE = MODE != kDense;
-  using L = RowLayout<bf16_t, D>;  // V row layout
-  constexpr int KB = D / 32;
-  constexpr int LPR = L::kLanesPerRow;
-  constexpr int RPL = L::kRowsPerLoad;
-  constexpr int NT = L::kLoadsPerPage;  // V rows per lane per page
-  constexpr int NB = D / 16;            // 16-column blocks of the output
-  static_assert(G <= 8, "group size");
-  __shared__ __align__(16) uint16_t qsp[3][8][D];         // split scaled queries
-  __shared__ __align__(16) uint16_t vt[W][16][D];  // V page of each wavefront
-  __shared__ float sm_m[W][G], sm_mt[W][G], sm_l[W][G];
-  __shared__ float sm_acc[W][G][D];
-  // kSelect: the selection's workspace and this split's share of the list
-  __shared__ SelectLds<MODE == kSelect ? W : 1> ssel;
-  __shared__ int spages[MODE == kSelect ? kMaxSplitPages : 1];
-  __shared__ int sphys[MODE == kSelect ? kMaxSplitPages : 1];
-
-  const int split = blockIdx.x % n_splits;
-  const int unit = blockIdx.x / n_splits;  // b * hkv + g
-  const int b = unit / hkv;
-  const int g = unit % hkv;
-  // Uniform per wavefront, so page ids below are scalar loads: they are
-  // counted apart from the vector loads of K and V and never make a wait for
-  // one page's K/V drain the loads of the pages behind it.
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int lane = threadIdx.x % kWave;
-  const int col = lane % 16;   // token row of A / head column of B
-  const int kgrp = lane / 16;  // which 8 of each 32 coordinates; token group of D
-  const int rg = lane / LPR;   // V row group
-  const int vc = lane % LPR;   // V column vector
-
-  // The queries are requested first: their split is the first thing waited
-  // for after the page ids, and vector loads complete in order.
-  const float* qg = q + ((int64_t)b * hkv * G + g * G) * D;
-  constexpr int kQPer = (G * D + W * kWave - 1) / (W * kWave);
-  float qv[kQPer];
-#pragma unroll
-  for (int i = 0; i < kQPer; ++i) {
-    const int e = threadIdx.x + i * W * kWave;
-    qv[i] = e < G * D ? qg[e] : 0.0f;
-  }
-
-  const int32_t* list = MODE == kList ? sel + (int64_t)unit * budget : nullptr;
-  const int32_t* row = page_table + (int64_t)b * max_pages;
-  const int len = seq_lens[b];
-  int first, hi;
-  if constexpr (MODE == kSelect) {
-    // The whole workgroup selects the unit's pages; this split keeps list
-    // slots [first, first + per) in LDS and writes them (and the padding
-    // among them) to the page list output.
-    const int per = ceil_div(budget, n_splits);
-    first = split * per;
-    int32_t* dst = sa.sel ? sa.sel + (int64_t)unit * budget : nullptr;
-    // The physical page of each kept page is read next to its score, so the
-    // pages' K and V can be requested right after the selection.
-    const int kept = select_unit<W, C, true, false>(
-        sa.scores + (int64_t)unit * max_pages, ceil_div(len, kPage), budget, sa.n_sink,
-        sa.n_local, ssel, row, [&](int o, int p, int ph) {
-          if (o >= first && o < first + per) {
-            spages[o - first] = p;
-            sphys[o - first] = ph;
-            if (dst) dst[o] = p;
-          }
-        });
-    __syncthreads();  // spages complete
-    if (dst)
-      for (int o = max(kept, first) + (int)threadIdx.x; o < min(first + per, budget);
-           o += W * kWave)
-        dst[o] = -1;
-    if (sa.sel_count && split == 0 && threadIdx.x == 0) sa.sel_count[unit] = kept;
-    hi = min(first + per, kept);
-  } else if constexpr (MODE == kList) {
-    const int per = ceil_div(budget, n_splits);
-    first = split * per;
-    hi = min(first + per, min(sel_count[unit], budget));
-  } else {
-    const int np = ceil_div(len, kPage);
-    const int per = ceil_div(np, n_splits);
-    first = min(split * per, np);
-    hi = min(split * per + per, np);
-  }
-  // Wavefront `wave` takes the split's items first + wave + W*k.
-  const int n_items = hi > first + wave ? ceil_div(hi - first - wave, W) : 0;
-
-
-  // Page ids of a block of P items (list entry, then table entry). Every
-  // read is in bounds: list slots are clamped to the row, and items past the
-  // wavefront's last one read logical page 0 and get no tokens.
-  auto resolve_block = [&](int blk, PageRef (&refs)[P]) {
-    int pg[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const int item = first + wave + (blk * P + j) * W;
-      if constexpr (MODE == kSelect)
-        pg[j] = spages[min(item - first, kMaxSplitPages - 1)];
-      else
-        pg[j] = MODE == kList ? list[min(item, budget - 1)] : item;
-    }
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      const bool ok = blk * P + j < n_items;
-      const int pc = ok ? pg[j] : 0;
-      if constexpr (MODE == kSelect) {  // physical pages came with the selection
-        const int item = first + wave + (blk * P + j) * W;
-        refs[j].phys = ok ? sphys[min(item - first, kMaxSplitPages - 1)] : 0;
-      } else {
-        refs[j].phys = row[pc];
-      }
-      refs[j].cnt = ok ? min(kPage, len - pc * kPage) : 0;
-    }
-  };
-  // All 16 rows of a (page, KV head) block are read (they are in bounds);
-  // rows past the valid count are zeroed in V and masked in the logits.
-  auto load = [&](const PageRef& r, uint4 (&kf)[KB], uint4 (&vf)[NT]) {
-    const int64_t off = ((int64_t)r.phys * hkv + g) * kPage * D;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) kf[kb] = ld16(k_pool + off + col * D + kb * 32 + kgrp * 8);
-#pragma unroll
-    for (int i = 0; i < NT; ++i) vf[i] = ld16(v_pool + off + (rg + i * RPL) * D + vc * 8);
-  };
-
-  // Page ids are resolved two blocks of P ahead of their use.
-  PageRef ids[P], nxt[P];
-  resolve_block(0, ids);
-  resolve_block(1, nxt);
-
-  // Split of the scaled queries, once per workgroup (the table reads above
-  // are in flight meanwhile).
-#pragma unroll
-  for (int i = 0; i < kQPer; ++i) {
-    const int e = threadIdx.x + i * W * kWave;
-    if (e < G * D) {
-      uint32_t hi_, mid_, lo_;
-      bf16_split3(qv[i] * qscale, hi_, mid_, lo_);
-      const int h = e / D, d = e % D;
-      qsp[0][h][d] = (uint16_t)hi_;
-      qsp[1][h][d] = (uint16_t)mid_;
-      qsp[2][h][d] = (uint16_t)lo_;
-    }
-  }
-
-  // P pages in flight before the barrier.
-  uint4 kbuf[P][KB], vbuf[P][NT];
-#pragma unroll
-  for (int j = 0; j < P; ++j) load(ids[j], kbuf[j], vbuf[j]);
-  __syncthreads();
-  const bool live = col < G;  // lanes of real heads in the B operand
-
-  float m_run = -INFINITY, m_true = -INFINITY, l_part = 0.0f;  // head `col`
-  // P.V accumulators: acc[nb][i] = output of head 4*kgrp+i, column 16*nb+col.
-  f32x4_t acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  const int trow = 4 * kgrp + (col >> 2);  // V row this lane hands to the transposed read
-  const int tcol = 4 * (col & 3);          // and its 4-column offset within a 16-column block
-
-  auto attend = [&](const PageRef& r, const uint4 (&kf)[KB], const uint4 (&vf)[NT]) {
-    f32x4_t s[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int k = 2; k >= 0; --k)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const uint4 bq = live ? *reinterpret_cast<const uint4*>(&qsp[k][col][kb * 32 + kgrp * 8])
-                              : make_uint4(0, 0, 0, 0);
-        s[kb] = mfma_bf16_16x16x32(kf[kb], bq, s[kb]);
-      }
-    float x[4];
-    {
-      f32x4_t t = s[0];
-#pragma unroll
-      for (int kb = 1; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) t[i] += s[kb][i];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[i] = 4 * kgrp + i < r.cnt ? t[i] : -INFINITY;
-    }
-    float mp = fmax_(fmax_(x[0], x[1]), fmax_(x[2], x[3]));
-    mp = fmax_(mp, __shfl_xor(mp, 16));
-    mp = fmax_(mp, __shfl_xor(mp, 32));
-    m_true = fmax_(m_true, mp);
-    const bool resc = mp > m_run + kLazyRescale;
-    float alpha = 1.0f;
-    if (resc) {
-      alpha = exp2_(m_run - mp);
-      m_run = mp;
-      l_part *= alpha;
-    }
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = x[i] == -INFINITY ? 0.0f : exp2_(x[i] - m_run);
-    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
-    // Weights as the A operand of P.V (row = head `col`, k = token 4*kgrp+i),
-    // split into hi + lo bf16 so the product keeps ~16 bits of each weight.
-    uint32_t whi[4], wlo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      whi[i] = bf16_rne_bits(pr[i]);
-      wlo[i] = bf16_rne_bits(pr[i] - bf16_bits_to_float(whi[i]));
-    }
-    const uint2 aph = make_uint2(whi[0] | (whi[1] << 16), whi[2] | (whi[3] << 16));
-    const uint2 apl = make_uint2(wlo[0] | (wlo[1] << 16), wlo[2] | (wlo[3] << 16));
-    if (__any(resc && live)) {
-      // accumulator rows are heads 4*kgrp+i; their factors live in lanes 4*kgrp+i
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ai = __shfl(alpha, 4 * kgrp + i);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[nb][i] *= ai;
-      }
-    }
-    // Stage V (rows past the valid count as zeros), then P.V per 16 columns
-    // with the B operand read transposed from LDS.
-#pragma unroll
-    for (int i = 0; i < NT; ++i) {
-      const int t = rg + i * RPL;
-      *reinterpret_cast<uint4*>(&vt[wave][t][vc * 8]) = t < r.cnt ? vf[i] : make_uint4(0, 0, 0, 0);
-    }
-    wave_sync_lds();
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const uint2 bv = lds_read_tr16(&vt[wave][trow][nb * 16 + tcol]);
-      acc[nb] = mfma_bf16_16x16x16(apl, bv, acc[nb]);
-      acc[nb] = mfma_bf16_16x16x16(aph, bv, acc[nb]);
-    }
-    wave_sync_lds();  // V is read before the next page overwrites it
-  };
-
-  // Pipeline: while page j of a block is attended, the loads of the pages of
-  // the next block are in flight; each buffer is refilled as soon as its
-  // page is attended (every load in the loop unconditional, so the number in
-  // flight is the same on every path). The last block is attended after the
-  // loop and requests nothing more.
-  int base = 0;
-  for (; base + P < n_items; base += P) {
-    PageRef nn[P];
-    resolve_block(base / P + 2, nn);
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      attend(ids[j], kbuf[j], vbuf[j]);
-      load(nxt[j], kbuf[j], vbuf[j]);
-    }
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-      ids[j] = nxt[j];
-      nxt[j] = nn[j];
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < P; ++j)
-    if (base + j < n_items) attend(ids[j], kbuf[j], vbuf[j]);  // uniform per wavefront
-
-  // Per wavefront: normaliser over token groups; each (head, column) of the
-  // accumulators is owned by one lane.
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * kgrp + i;
-    if (h < G) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) sm_acc[wave][h][nb * 16 + col] = acc[nb][i];
-    }
-  }
-  if (kgrp == 0 && live) {
-    sm_m[wave][col] = m_run;
-    sm_mt[wave][col] = m_true;
-    sm_l[wave][col] = l_part;
-  }
-  __syncthreads();
-
-  // Merge against the split's true max; write the partials.
-  const int hq = hkv * G;
-  for (int idx = threadIdx.x; idx < G * D; idx += W * kWave) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float mo = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < W; ++w) mo = fmax_(mo, sm_mt[w][h]);
-    float a = 0.0f, lsum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < W; ++w) {
-      const float mw = sm_m[w][h];
-      const float wt = mw == -INFINITY ? 0.0f : exp2_(mw - mo);
-      a = __builtin_fmaf(wt, sm_acc[w][h][d], a);
-      lsum = __builtin_fmaf(wt, sm_l[w][h], lsum);
-    }
-    const float m_nat = mo == -INFINITY ? -INFINITY : mo * kLn2;
-    if (sa.out) {
-      write_merged(sa, (int64_t)b * hq + g * G + h, g * G + h, d, D, m_nat, lsum, a);
-      continue;
-    }
-    const int64_t ph = ((int64_t)b * hq + g * G + h) * n_splits + split;
-    part_acc[ph * D + d] = a;
-    if (d == 0) {
-      part_ml[ph * 2 + 0] = m_nat;
-      part_ml[ph * 2 + 1] = lsum;
-    }
-  }
-}
 
 hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void* k_pool,
                          const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,
@@ -694,7 +12,7 @@ hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(kDecWaves * kWave);
   const float qscale = scale * 1.44269504088896340736f;  // log2(e)
-  const SelectArgs none{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr};
+  const SelectArgs none{nullptr, 0, 0, nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f, 0.0f};
   if (s.kv_bf16) {
     const int waves = decode_waves(blocks);
     const dim3 wblock(waves * kWave);
@@ -721,88 +39,27 @@ hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void
 #undef PS_DECODE_MFMA
     return hipGetLastError();
   }
-  PS_WITH_KV(false, s.head_dim, {
-    PS_WITH_GROUP(s.group, {
-      if (sparse) {
-        hipLaunchKernelGGL((decode_kernel<TElem, kD, kG, kList, 1>), grid, block, 0, st, q,
-                           static_cast<const TElem*>(k_pool), static_cast<const TElem*>(v_pool),
-                           page_table, seq_lens, sel, sel_count, budget, s.hkv, s.max_pages,
-                           n_splits, qscale, part_acc, part_ml, none);
-      } else {
-        hipLaunchKernelGGL((decode_kernel<TElem, kD, kG, kDense, 1>), grid, block, 0, st, q,
-                           static_cast<const TElem*>(k_pool), static_cast<const TElem*>(v_pool),
-                           page_table, seq_lens, nullptr, nullptr, 0, s.hkv, s.max_pages,
-                           n_splits, qscale, part_acc, part_ml, none);
-      }
-    });
-  });
-  return hipGetLastError();
-}
-
-hipError_t launch_select_decode(const Shape& s, const float* q, const void* k_pool,
-                                const void* v_pool, const int32_t* page_table,
-                                const int32_t* seq_lens, const float* scores, int budget,
-                                int n_sink, int n_local, float scale, int n_splits, int32_t* sel,
-                                int32_t* sel_count, float* part_acc, float* part_ml,
-                                const float* sink, float* out, float* lse, hipStream_t st) {
-  const int64_t blocks = (int64_t)s.batch * s.hkv * n_splits;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (s.max_pages > kSelectDecodeMaxPages ||
-      (budget + n_splits - 1) / n_splits > kMaxSplitPages || (out && n_splits != 1))
-    return hipErrorInvalidValue;
-  const float qscale = scale * 1.44269504088896340736f;  // log2(e)
-  const SelectArgs sa{scores, n_sink, n_local, sel, sel_count, sink, out, lse};
-  if (!s.kv_bf16) {  // fp32 K/V: the vector-ALU decode, 4 wavefronts
-    const dim3 grid((unsigned)blocks), block(kDecWaves * kWave);
-    const int per_lane = (s.max_pages + kDecWaves * kWave - 1) / (kDecWaves * kWave);
-#define PS_SELECT_DECODE_F32(DD, CC)                                                         \
-  hipLaunchKernelGGL((decode_kernel<float, DD, kG, kSelect, CC>), grid, block, 0, st, q,     \
-                     static_cast<const float*>(k_pool), static_cast<const float*>(v_pool),  \
-                     page_table, seq_lens, nullptr, nullptr, budget, s.hkv, s.max_pages,    \
-                     n_splits, qscale, part_acc, part_ml, sa)
-#define PS_SELECT_DECODE_F32_C(DD)                          \
-  do {                                                      \
-    if (per_lane <= 2) PS_SELECT_DECODE_F32(DD, 2);         \
-    else if (per_lane <= 8) PS_SELECT_DECODE_F32(DD, 8);    \
-    else PS_SELECT_DECODE_F32(DD, 32);                      \
+  // fp32 K/V: the vector-ALU decode
+  const float* kp = static_cast<const float*>(k_pool);
+  const float* vp = static_cast<const float*>(v_pool);
+#define PS_DECODE_F32(DD)                                                                     \
+  do {                                                                                        \
+  PS_WITH_GROUP(s.group, {                                                                    \
+    if (sparse)                                                                               \
+      hipLaunchKernelGGL((decode_kernel<float, DD, kG, kList, 1>), grid, block, 0, st, q, kp, \
+                         vp, page_table, seq_lens, sel, sel_count, budget, s.hkv,             \
+                         s.max_pages, n_splits, qscale, part_acc, part_ml, none);             \
+    else                                                                                      \
+      hipLaunchKernelGGL((decode_kernel<float, DD, kG, kDense, 1>), grid, block, 0, st, q,    \
+                         kp, vp, page_table, seq_lens, nullptr, nullptr, 0, s.hkv,            \
+                         s.max_pages, n_splits, qscale, part_acc, part_ml, none);             \
+  });                                                                                         \
   } while (0)
-    PS_WITH_GROUP(s.group, {
-      if (s.head_dim == 64)
-        PS_SELECT_DECODE_F32_C(64);
-      else
-        PS_SELECT_DECODE_F32_C(128);
-    });
-#undef PS_SELECT_DECODE_F32_C
-#undef PS_SELECT_DECODE_F32
-    return hipGetLastError();
-  }
-  const int waves = decode_waves(blocks);
-  const dim3 grid((unsigned)blocks), block(waves * kWave);
-  const int per_lane = (s.max_pages + waves * kWave - 1) / (waves * kWave);
-#define PS_SELECT_DECODE(DD, CC, WW)                                                          \
-  hipLaunchKernelGGL((decode_mfma_kernel<DD, kG, kSelect, CC, WW, 2>), grid,                   \
-                     block, 0, st, q,                                                         \
-                     static_cast<const bf16_t*>(k_pool), static_cast<const bf16_t*>(v_pool),  \
-                     page_table, seq_lens, nullptr, nullptr, budget, s.hkv, s.max_pages,      \
-                     n_splits, qscale, part_acc, part_ml, sa)
-#define PS_SELECT_DECODE_C(DD)                                                   \
-  do {                                                                           \
-    if (waves == 8) {                                                            \
-      if (per_lane <= 8) PS_SELECT_DECODE(DD, 8, 8);                             \
-      else PS_SELECT_DECODE(DD, 16, 8);                                          \
-    } else {                                                                     \
-      if (per_lane <= 16) PS_SELECT_DECODE(DD, 16, 4);                           \
-      else PS_SELECT_DECODE(DD, 32, 4);                                          \
-    }                                                                            \
-  } while (0)
-  PS_WITH_GROUP(s.group, {
-    if (s.head_dim == 64)
-      PS_SELECT_DECODE_C(64);
-    else
-      PS_SELECT_DECODE_C(128);
-  });
-#undef PS_SELECT_DECODE_C
-#undef PS_SELECT_DECODE
+  if (s.head_dim == 64)
+    PS_DECODE_F32(64);
+  else
+    PS_DECODE_F32(128);
+#undef PS_DECODE_F32
   return hipGetLastError();
 }
 

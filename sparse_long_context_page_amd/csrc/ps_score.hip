@@ -456,25 +456,33 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
 #undef PS_SCORE_MFMA
     return hipGetLastError();
   }
-  PS_WITH_KV(false, s.head_dim, {
-    const int per_block = ScoreCfg<TElem, kD>::kPagesPerBlock;
-    const int chunks = (s.max_pages + per_block - 1) / per_block;
-    const int64_t blocks = (int64_t)chunks * s.batch * s.hkv;
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)blocks);
-    const TElem* kp = static_cast<const TElem*>(k_pool);
-    TElem* mo = static_cast<TElem*>(meta_out);
-    PS_WITH_GROUP(s.group, {
-      if (kp)
-        hipLaunchKernelGGL((score_pages_kernel<TElem, kD, kG, true>), grid, block, 0, st, q,
-                           static_cast<const TElem*>(meta), page_table, seq_lens, s.hkv,
-                           s.max_pages, chunks, scores, kp, mo);
-      else
-        hipLaunchKernelGGL((score_pages_kernel<TElem, kD, kG, false>), grid, block, 0, st, q,
-                           static_cast<const TElem*>(meta), page_table, seq_lens, s.hkv,
-                           s.max_pages, chunks, scores, kp, mo);
-    });
-  });
+  // fp32 metadata: the vector-ALU kernel
+  const float* kp = static_cast<const float*>(k_pool);
+  float* mo = static_cast<float*>(meta_out);
+  const float* mt = static_cast<const float*>(meta);
+#define PS_SCORE_F32(DD)                                                                    \
+  do {                                                                                      \
+    const int per_block = ScoreCfg<float, DD>::kPagesPerBlock;                              \
+    const int chunks = (s.max_pages + per_block - 1) / per_block;                           \
+    const int64_t blocks = (int64_t)chunks * s.batch * s.hkv;                               \
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;                           \
+    const dim3 grid((unsigned)blocks);                                                      \
+    PS_WITH_GROUP(s.group, {                                                                \
+      if (kp)                                                                               \
+        hipLaunchKernelGGL((score_pages_kernel<float, DD, kG, true>), grid, block, 0, st, q, \
+                           mt, page_table, seq_lens, s.hkv, s.max_pages, chunks, scores,   \
+                           kp, mo);                                                         \
+      else                                                                                  \
+        hipLaunchKernelGGL((score_pages_kernel<float, DD, kG, false>), grid, block, 0, st,  \
+                           q, mt, page_table, seq_lens, s.hkv, s.max_pages, chunks,        \
+                           scores, kp, mo);                                                 \
+    });                                                                                     \
+  } while (0)
+  if (s.head_dim == 64)
+    PS_SCORE_F32(64);
+  else
+    PS_SCORE_F32(128);
+#undef PS_SCORE_F32
   return hipGetLastError();
 }
 

@@ -60,8 +60,9 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // Sparsity for Efficient Long-Context Decoding", section "Methodology", item
 // 2): only pages with scale * score >= tau (compared in fp64) are candidates,
 // and r = min(budget - |forced|, passing candidates); the others are dropped.
-// tau = tau_fn(), called by every thread once the scores are requested, so
-// the threshold's own work overlaps their loads (it may hold barriers).
+// tau_fn.issue() is called by every thread before the scores are requested
+// (to start the threshold's own loads) and tau = tau_fn() once they are, so
+// the threshold's work overlaps their loads (it may hold barriers).
 //
 // The kept candidates are the r best in the order (key descending, page
 // ascending). Radix passes narrow the r-th key's bits; once its bin holds at
@@ -70,6 +71,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // (key, page); when every bit is decided first, the bin's keys are equal and
 // the cut is the remaining-th lowest page among them.
 struct NoThreshold {
+  __device__ void issue() const {}
   __device__ double operator()() const { return 0.0; }
 };
 
@@ -101,6 +103,7 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
   uint32_t pass_bits[FILTER ? (C + 31) / 32 : 1];
 #pragma unroll
   for (int i = 0; i < (FILTER ? (C + 31) / 32 : 1); ++i) pass_bits[i] = 0u;
+  if constexpr (FILTER) tau_fn.issue();
   float sc[C];
 #pragma unroll
   for (int j = 0; j < C; ++j) {
@@ -311,5 +314,148 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
   }
   return kept_total < budget ? kept_total : budget;
 }
+
+// Top-delta threshold ("Faster Than Flash: Exploiting Attention Sparsity for
+// Efficient Long-Context Decoding", section "Methodology", item 2, eq. (1)-(3)
+// and "Pseudo-Max Robustness as Fail-Safe"): the pseudo-max of each query
+// head is its largest scale * q.k over the valid tokens of the forced pages
+// (sink pages, then local pages after them); the unit's threshold is the
+// smallest of its heads' pseudo-maxima minus delta; -inf when the budget
+// covers the request or no page is forced (every page is then a candidate).
+// The logits are formed in fp64 (every fp32 * bf16 or fp32 * fp32 product is
+// exact there): the queries are widened once into LDS; eight consecutive
+// threads share a forced token, each takes an eighth of the coordinates,
+// widens its key values once and accumulates them in order for one head after
+// another; the eighths are added pairwise, ((e0 + e1) + (e2 + e3)) + ((e4 +
+// e5) + (e6 + e7)). The maximum per head across the workgroup is exact in any
+// order.
+// issue() requests the page-table entries of the first forced tokens and the
+// queries (called before the selection requests its scores); operator()()
+// then requests the key rows, computes, and returns the threshold. Both are
+// called by every thread of the workgroup; operator()() holds two barriers.
+// GL: query rows held (the group size, or 8 when it is known only at run
+// time).
+template <int WAVES, int D, int GL = 8>
+struct TopDeltaLds {
+  double wave_max[WAVES][GL];
+  __align__(16) double q[GL][D];
+};
+
+// G: the group size when known at compile time, else 0 (the group member).
+template <typename T, int D, int WAVES, int G = 0>
+struct TopDeltaThreshold {
+  static constexpr int kG = G ? G : 8;  // heads computed (those past the group skipped)
+  static constexpr int kThreads = WAVES * kWave;
+  static constexpr int kParts = 8;                // threads per forced token
+  static constexpr int kTokens = kThreads / kParts;  // forced tokens per round
+  static constexpr int kCoords = D / kParts;      // coordinates per thread
+  static constexpr int kVec = Elem<T>::kPerVec;
+  static constexpr int kLoads = kCoords / kVec;   // 16-byte key loads per thread
+  static_assert(kLoads >= 1 && kCoords % kVec == 0, "key row split");
+  static_assert(kG * D / 4 <= kThreads, "one float4 of the queries per thread");
+
+  const float* qg;     // the group's queries [group, D]
+  const T* k_pool;
+  const int32_t* table;  // the request's page-table row
+  int g, hkv, len, n, group, budget, n_sink, n_local;
+  float scale, delta;
+  TopDeltaLds<WAVES, D, kG>* sh;
+  int phys0 = 0;  // page of this thread's first-round token
+  float4 qv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+
+  __device__ int ng() const { return G ? G : group; }
+  __device__ bool active() const { return budget < n && n_sink + n_local > 0; }
+  __device__ int n_s() const { return min(n_sink, n); }
+  __device__ int l0() const { return max(n - n_local, n_s()); }  // first local page
+  __device__ int tokens() const { return (n_s() + n - l0()) * kPage; }
+  // logical page of forced token index ft: sink pages, then local pages
+  __device__ int page_of(int ft) const {
+    const int fp = ft / kPage;
+    return fp < n_s() ? fp : l0() + (fp - n_s());
+  }
+
+  __device__ void issue() {
+    if (!active()) return;  // uniform
+    const int t = threadIdx.x;
+    if (t < ng() * D / 4) qv = reinterpret_cast<const float4*>(qg)[t];
+    const int ft = t / kParts;
+    phys0 = ft < tokens() ? table[page_of(ft)] : 0;
+  }
+
+  __device__ double operator()() {
+    if (!active()) return -INFINITY;  // uniform
+    const int t = threadIdx.x;
+    const int lane = t % kWave;
+    const int wave = t / kWave;
+    const int part = t % kParts;
+    const int n_tok = tokens();
+    if (t < ng() * D / 4) {
+      double* dq = &sh->q[0][0] + 4 * t;
+      dq[0] = (double)qv.x;
+      dq[1] = (double)qv.y;
+      dq[2] = (double)qv.z;
+      dq[3] = (double)qv.w;
+    }
+    double mx[kG];
+#pragma unroll
+    for (int h = 0; h < kG; ++h) mx[h] = -INFINITY;
+    for (int base = 0; base < n_tok; base += kTokens) {  // uniform trip count
+      const int ft = base + t / kParts;
+      const int p = ft < n_tok ? page_of(ft) : 0;
+      const int tt = ft % kPage;
+      const bool valid = ft < n_tok && p * kPage + tt < len;
+      const int phys = base == 0 ? phys0 : (ft < n_tok ? table[p] : 0);
+      // rows past the forced tokens read row 0 of physical page 0 (in the
+      // pool) and are not counted
+      const T* krow = k_pool + (((int64_t)phys * hkv + g) * kPage + (ft < n_tok ? tt : 0)) * D +
+                      part * kCoords;
+      uint4 kv[kLoads];
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) kv[i] = ld16(krow + i * kVec);
+      if (base == 0) __syncthreads();  // sh->q complete
+      double k64[kCoords];
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        float kf[kVec];
+        unpack(kv[i], kf);
+#pragma unroll
+        for (int j = 0; j < kVec; ++j) k64[i * kVec + j] = (double)kf[j];
+      }
+      const double* qp = &sh->q[0][0] + part * kCoords;
+#pragma unroll
+      for (int h = 0; h < kG; ++h) {
+        if (!G && h >= group) break;  // uniform
+        __builtin_amdgcn_sched_barrier(0);  // one head's query values live at a time
+        double acc = 0.0;
+#pragma unroll
+        for (int c = 0; c < kCoords; ++c) acc = __builtin_fma(qp[h * D + c], k64[c], acc);
+        // ((e0 + e1) + (e2 + e3)) + ((e4 + e5) + (e6 + e7)) in every lane of the eight
+#pragma unroll
+        for (int m = 1; m < kParts; m <<= 1) {
+          const double o = __shfl_xor(acc, m);
+          acc = (part & m) ? o + acc : acc + o;
+        }
+        const double sv = (double)scale * acc;
+        mx[h] = valid ? fmax(mx[h], sv) : mx[h];
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < kG; ++hh) {
+      if (!G && hh >= group) break;  // uniform
+      double v = mx[hh];
+      for (int off = kWave / 2; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+      if (lane == 0) sh->wave_max[wave][hh] = v;
+    }
+    __syncthreads();
+    double m_min = INFINITY;
+    for (int hh = 0; hh < ng(); ++hh) {
+      double m = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) m = fmax(m, sh->wave_max[w][hh]);
+      m_min = fmin(m_min, m);
+    }
+    return m_min - (double)delta;
+  }
+};
 
 }  // namespace ps

@@ -29,16 +29,9 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
   if (threadIdx.x == 0) sel_count[unit] = kept;
 }
 
-// Top-delta selection ("Faster Than Flash: Exploiting Attention Sparsity for
-// Efficient Long-Context Decoding", section "Methodology", item 2, eq. (1)-(3)
-// and "Pseudo-Max Robustness as Fail-Safe"): the pseudo-max of each query
-// head is its largest scale * q.k over the valid tokens of the forced pages;
-// the unit's threshold is the smallest of its heads' pseudo-maxima minus
-// delta; select_unit keeps the forced pages and the best-scoring pages with
-// scale * score >= threshold, at most budget of them in all. The logits are
-// formed in fp64 (every fp32 * bf16 or fp32 * fp32 product is exact there),
-// one (token, head) pair per thread with the key row in registers and the
-// queries in LDS, then reduced per head across the workgroup.
+// Top-delta selection: select_unit keeps the forced pages and the
+// best-scoring pages with scale * score >= topdelta_threshold (compared in
+// fp64), at most budget of them in all.
 template <typename T, int C, int D>
 __global__ __launch_bounds__(kSelThreads) void select_topdelta_kernel(
     const float* __restrict__ q, const T* __restrict__ k_pool,
@@ -46,75 +39,18 @@ __global__ __launch_bounds__(kSelThreads) void select_topdelta_kernel(
     const int32_t* __restrict__ seq_lens, int hkv, int group, int max_pages, int budget,
     int n_sink, int n_local, float scale, float delta, int32_t* __restrict__ sel,
     int32_t* __restrict__ sel_count) {
-  using L = RowLayout<T, D>;
-  constexpr int V = L::kVec;
   __shared__ SelectLds<kSelWaves> sh;
-  __shared__ double sm_max[kSelWaves][8];
-  __shared__ __align__(16) float sm_q[8][D];
+  __shared__ TopDeltaLds<kSelWaves, D> td;
   const int unit = blockIdx.x;  // b * hkv + g
   const int b = unit / hkv;
   const int g = unit % hkv;
-  const int wave = threadIdx.x / kWave;
-  const int lane = threadIdx.x % kWave;
   const int len = seq_lens[b];
   const int n = ceil_div(len, kPage);
-
-  // pseudo-max and threshold, evaluated inside select_unit once the scores
-  // are requested
-  auto threshold = [&]() -> double {
-    if (budget >= n || n_sink + n_local == 0) return -INFINITY;  // uniform
-    // the group's queries, staged once in LDS (fp32; widened per product)
-    const float* qg = q + ((int64_t)b * hkv * group + g * group) * D;
-    for (int i = threadIdx.x; i < group * D / 4; i += kSelThreads)
-      reinterpret_cast<float4*>(sm_q)[i] = reinterpret_cast<const float4*>(qg)[i];
-    const int n_s = min(n_sink, n);
-    const int l0 = max(n - n_local, n_s);  // local pages [l0, n), after the sink pages
-    const int items = (n_s + n - l0) * kPage * group;  // (forced page, token, head)
-    double mx[8];
-#pragma unroll
-    for (int h = 0; h < 8; ++h) mx[h] = -INFINITY;
-    __syncthreads();  // sm_q complete
-    for (int it = threadIdx.x; it < items; it += kSelThreads) {
-      const int h = it % group;
-      const int tok = it / group;
-      const int fp = tok / kPage, t = tok % kPage;
-      const int p = fp < n_s ? fp : l0 + (fp - n_s);
-      if (p * kPage + t >= len) continue;  // unused slot of a partial page
-      const int phys = page_table[(int64_t)b * max_pages + p];
-      const T* krow = k_pool + (((int64_t)phys * hkv + g) * kPage + t) * D;
-      uint4 kv[D / V];
-#pragma unroll
-      for (int i = 0; i < D / V; ++i) kv[i] = ld16(krow + i * V);
-      // four partial sums over interleaved coordinates, then a fixed order
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-      for (int i = 0; i < D / V; ++i) {
-        float kf[V];
-        unpack(kv[i], kf);
-#pragma unroll
-        for (int j = 0; j < V; ++j)
-          acc[j % 4] = __builtin_fma((double)sm_q[h][i * V + j], (double)kf[j], acc[j % 4]);
-      }
-      const double s = (double)scale * ((acc[0] + acc[1]) + (acc[2] + acc[3]));
-#pragma unroll
-      for (int hh = 0; hh < 8; ++hh) mx[hh] = hh == h ? fmax(mx[hh], s) : mx[hh];
-    }
-#pragma unroll
-    for (int hh = 0; hh < 8; ++hh) {
-      double v = mx[hh];
-      for (int off = kWave / 2; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
-      if (lane == 0) sm_max[wave][hh] = v;
-    }
-    __syncthreads();
-    double m_min = INFINITY;
-    for (int hh = 0; hh < group; ++hh) {
-      double m = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < kSelWaves; ++w) m = fmax(m, sm_max[w][hh]);
-      m_min = fmin(m_min, m);
-    }
-    return m_min - (double)delta;
-  };
+  const int32_t* table = page_table + (int64_t)b * max_pages;
+  // evaluated inside select_unit, its loads issued before the scores'
+  TopDeltaThreshold<T, D, kSelWaves> threshold{
+      q + ((int64_t)b * hkv * group + g * group) * D, k_pool, table, g, hkv, len, n, group,
+      budget, n_sink, n_local, scale, delta, &td};
   int32_t* dst = sel + (int64_t)unit * budget;
   const int kept = select_unit<kSelWaves, C, false, true>(
       scores + (int64_t)unit * max_pages, n, budget, n_sink, n_local, sh, nullptr,

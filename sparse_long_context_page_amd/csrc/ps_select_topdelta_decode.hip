@@ -1,0 +1,22 @@
+// Launch of the decode that selects its own pages by the top-delta threshold
+// (kernels in ps_decode.h).
+#include "ps_decode.h"
+
+namespace ps {
+
+hipError_t launch_select_topdelta_decode(const Shape& s, const float* q, const void* k_pool,
+                                         const void* v_pool, const int32_t* page_table,
+                                         const int32_t* seq_lens, const float* scores,
+                                         int budget, int n_sink, int n_local, float scale,
+                                         float delta, int n_splits, int32_t* sel,
+                                         int32_t* sel_count, float* part_acc, float* part_ml,
+                                         const float* sink, float* out, float* lse,
+                                         hipStream_t st) {
+  if (s.group > 8) return hipErrorInvalidValue;
+  const SelectArgs sa{scores, n_sink, n_local, sel, sel_count, sink, out, lse, scale, delta};
+  return launch_selecting_decode<kSelectDelta>(s, q, k_pool, v_pool, page_table, seq_lens,
+                                               budget, scale, n_splits, part_acc, part_ml, sa,
+                                               st);
+}
+
+}  // namespace ps

@@ -35,8 +35,9 @@ class DecodeStep:
         self.scale = ops.default_scale(geom.head_dim) if scale is None else float(scale)
         # top-delta selection (ps_select_topdelta) instead of top-k when set
         self.delta = None if delta is None else float(delta)
-        # selection fused into the sparse decode (one launch) when supported
-        self.fused = (bool(fused) and self.delta is None and
+        # selection (top-k, or top-delta) fused into the sparse decode (one
+        # launch) when supported
+        self.fused = (bool(fused) and
                       ops.select_decode_supported(geom, self.budget, self.n_splits))
         b, hq, hkv, d = geom.batch, geom.num_q_heads, geom.num_kv_heads, geom.head_dim
         f32 = dict(device=device, dtype=torch.float32)
@@ -76,17 +77,19 @@ class DecodeStep:
         else:
             ops.ps_score_pages(g, q, meta, page_table, seq_lens, self.scores, stream)
         acc, ml = self.partials(self.n_splits)
-        if self.fused and self.n_splits == 1:  # select, decode and merge in one launch
-            ops.ps_select_sparse_decode(g, q, k_pool, v_pool, page_table, seq_lens, self.scores,
-                                        self.budget, self.n_sink, self.n_local, self.scale, 1,
-                                        self.sel, self.sel_count, None, None, sink, self.out,
-                                        self.lse, stream)
-            return self.out, self.lse
         if self.fused:
-            ops.ps_select_sparse_decode(g, q, k_pool, v_pool, page_table, seq_lens, self.scores,
-                                        self.budget, self.n_sink, self.n_local, self.scale,
-                                        self.n_splits, self.sel, self.sel_count, acc, ml,
-                                        stream=stream)
+            head = (g, q, k_pool, v_pool, page_table, seq_lens, self.scores, self.budget,
+                    self.n_sink, self.n_local, self.scale)
+            if self.delta is None:
+                fn = ops.ps_select_sparse_decode
+            else:
+                fn = ops.ps_select_topdelta_sparse_decode
+                head = head + (self.delta,)
+            if self.n_splits == 1:  # select, decode and merge in one launch
+                fn(*head, 1, self.sel, self.sel_count, None, None, sink, self.out, self.lse,
+                   stream)
+                return self.out, self.lse
+            fn(*head, self.n_splits, self.sel, self.sel_count, acc, ml, stream=stream)
         else:
             if self.delta is None:
                 ops.ps_select_topk(g, self.scores, seq_lens, self.budget, self.n_sink,

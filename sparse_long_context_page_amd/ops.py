@@ -195,6 +195,32 @@ def select_decode_supported(g: Geometry, budget_pages: int, n_splits: int) -> bo
             and -(-budget_pages // n_splits) <= SELECT_DECODE_MAX_SPLIT_PAGES)
 
 
+def _select_decode_args(g: Geometry, q, k_pool, v_pool, page_table, seq_lens, scores,
+                        budget_pages: int, n_sink: int, n_local: int, scale: float):
+    return (g.c(), _ptr(q, "q", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
+            _ptr(k_pool, "k_pool", g.kv_dtype, _pool_shape(g)),
+            _ptr(v_pool, "v_pool", g.kv_dtype, _pool_shape(g)),
+            _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
+            _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
+            _ptr(scores, "scores", torch.float32, (g.batch, g.num_kv_heads, g.max_pages)),
+            int(budget_pages), int(n_sink), int(n_local), float(scale))
+
+
+def _select_decode_outputs(g: Geometry, budget_pages: int, ns: int, sel, sel_count, part_acc,
+                           part_ml, sink, out, lse, stream):
+    return (_ptr(sel, "sel", torch.int32, (g.batch, g.num_kv_heads, budget_pages),
+                 optional=True),
+            _ptr(sel_count, "sel_count", torch.int32, (g.batch, g.num_kv_heads), optional=True),
+            _ptr(part_acc, "part_acc", torch.float32, (g.batch, g.num_q_heads, ns, g.head_dim),
+                 optional=True),
+            _ptr(part_ml, "part_ml", torch.float32, (g.batch, g.num_q_heads, ns, 2),
+                 optional=True),
+            _ptr(sink, "sink", torch.float32, (g.num_q_heads,), optional=True),
+            _ptr(out, "out", torch.float32, (g.batch, g.num_q_heads, g.head_dim), optional=True),
+            _ptr(lse, "lse", torch.float32, (g.batch, g.num_q_heads), optional=True),
+            _stream(stream))
+
+
 def ps_select_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens, scores,
                             budget_pages: int, n_sink: int, n_local: int, scale: float,
                             n_splits: int, sel, sel_count, part_acc, part_ml, sink=None,
@@ -204,23 +230,28 @@ def ps_select_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens
     lib = _lib.load()
     ns = int(n_splits)
     rc = lib.ps_select_sparse_decode(
-        g.c(), _ptr(q, "q", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
-        _ptr(k_pool, "k_pool", g.kv_dtype, _pool_shape(g)),
-        _ptr(v_pool, "v_pool", g.kv_dtype, _pool_shape(g)),
-        _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
-        _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
-        _ptr(scores, "scores", torch.float32, (g.batch, g.num_kv_heads, g.max_pages)),
-        int(budget_pages), int(n_sink), int(n_local), float(scale), ns,
-        _ptr(sel, "sel", torch.int32, (g.batch, g.num_kv_heads, budget_pages), optional=True),
-        _ptr(sel_count, "sel_count", torch.int32, (g.batch, g.num_kv_heads), optional=True),
-        _ptr(part_acc, "part_acc", torch.float32, (g.batch, g.num_q_heads, ns, g.head_dim),
-             optional=True),
-        _ptr(part_ml, "part_ml", torch.float32, (g.batch, g.num_q_heads, ns, 2), optional=True),
-        _ptr(sink, "sink", torch.float32, (g.num_q_heads,), optional=True),
-        _ptr(out, "out", torch.float32, (g.batch, g.num_q_heads, g.head_dim), optional=True),
-        _ptr(lse, "lse", torch.float32, (g.batch, g.num_q_heads), optional=True),
-        _stream(stream))
+        *_select_decode_args(g, q, k_pool, v_pool, page_table, seq_lens, scores, budget_pages,
+                             n_sink, n_local, scale), ns,
+        *_select_decode_outputs(g, budget_pages, ns, sel, sel_count, part_acc, part_ml, sink,
+                                out, lse, stream))
     _lib.check("ps_select_sparse_decode", rc)
+
+
+def ps_select_topdelta_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens,
+                                     scores, budget_pages: int, n_sink: int, n_local: int,
+                                     scale: float, delta: float, n_splits: int, sel, sel_count,
+                                     part_acc, part_ml, sink=None, out=None, lse=None,
+                                     stream=None) -> None:
+    """ps_select_topdelta and ps_sparse_decode in one launch (arguments as
+    ps_select_sparse_decode, delta as ps_select_topdelta)."""
+    lib = _lib.load()
+    ns = int(n_splits)
+    rc = lib.ps_select_topdelta_sparse_decode(
+        *_select_decode_args(g, q, k_pool, v_pool, page_table, seq_lens, scores, budget_pages,
+                             n_sink, n_local, scale), float(delta), ns,
+        *_select_decode_outputs(g, budget_pages, ns, sel, sel_count, part_acc, part_ml, sink,
+                                out, lse, stream))
+    _lib.check("ps_select_topdelta_sparse_decode", rc)
 
 
 def ps_full_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens, scale: float,

@@ -192,6 +192,31 @@ def test_fused_select_decode_validation():
         _lib.PS_OK
 
 
+def test_fused_topdelta_decode_validation():
+    lib = _lib.load()
+    g = geom()
+
+    def call(g=g, sel=X, cnt=X, budget=8, ns=1, nl=2, scale=0.1, delta=1.0, splits=2, acc=X,
+             ml=X, sink=None, out=None, lse=None):
+        return lib.ps_select_topdelta_sparse_decode(g, X, X, X, X, X, X, budget, ns, nl, scale,
+                                                    delta, splits, sel, cnt, acc, ml, sink, out,
+                                                    lse, None)
+    assert call(sel=None) == _lib.PS_ERR_NULL
+    assert call(acc=None) == _lib.PS_ERR_NULL
+    assert call(ns=5, nl=4) == _lib.PS_ERR_BUDGET
+    assert call(splits=9) == _lib.PS_ERR_BUDGET
+    assert call(out=X) == _lib.PS_ERR_BUDGET
+    assert call(delta=-1.0) == _lib.PS_ERR_BUDGET
+    assert call(delta=float("nan")) == _lib.PS_ERR_BUDGET
+    assert call(scale=0.0) == _lib.PS_ERR_BUDGET
+    assert call(scale=float("inf")) == _lib.PS_ERR_BUDGET
+    assert call(g=geom(max_pages=8193)) == _lib.PS_ERR_UNSUPPORTED
+    assert call(budget=1026, ns=0, nl=0, splits=2) == _lib.PS_ERR_UNSUPPORTED
+    assert call(g=geom(batch=0), delta=float("inf")) == _lib.PS_OK
+    assert call(g=geom(batch=0, kv_dtype=_lib.PS_F32), splits=1, acc=None, ml=None, sink=X,
+                out=X, lse=X) == _lib.PS_OK
+
+
 def test_partials_overflow():
     lib = _lib.load()
     g = geom(batch=1 << 20, num_q_heads=8, num_kv_heads=8, max_pages=4096)

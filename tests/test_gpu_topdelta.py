@@ -4,7 +4,9 @@ so that the threshold keeps fewer pages than the budget in many units:
 selection identical to the oracle's rule applied to the device's own scores,
 selection identical outside the ambiguity band to the oracle end to end,
 outputs within the rel-L2 gate on the device's page list, and the top-k
-selection at an infinite delta or without forced pages."""
+selection at an infinite delta or without forced pages. The selection fused
+into the decode (ps_select_topdelta_sparse_decode) equals the two launches it
+replaces, bit for bit."""
 
 import math
 
@@ -119,7 +121,7 @@ def test_step_end_to_end(case):
     delta = deltas[0]
     step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
                       inp["scale"], delta=delta)
-    assert not step.fused
+    assert step.fused
     meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
     out, lse = step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
                            inp["seq_lens"], inp["sink"])
@@ -140,6 +142,63 @@ def test_step_end_to_end(case):
             assert got - amb == set(int(x) for x in r["sel"]) - amb, (b, kv)
             check_unit_outputs(res, hu, b, kv, w, w.budget_pages, w.n_sink, w.n_local,
                                sel_dev=sel[b, kv, :k])
+
+
+def _fused_and_unfused(inp, g, meta, budget, n_sink, n_local, n_splits, delta):
+    w = inp["workload"]
+    res = []
+    for fused in (False, True):
+        step = DecodeStep(g, budget, n_sink, n_local, n_splits, w.dense_splits, inp["scale"],
+                          fused=fused, delta=delta)
+        assert step.fused == fused
+        step.sel.fill_(-7)
+        step.sel_count.fill_(-7)
+        out, lse = step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
+                               inp["seq_lens"], inp["sink"])
+        acc, ml = step.partials(step.n_splits)
+        torch.cuda.synchronize()
+        got = dict(sel=step.sel, cnt=step.sel_count, out=out, lse=lse)
+        if step.n_splits > 1:  # with one split the fused launch writes no partials
+            got.update(acc=acc, ml=ml)
+        res.append({k: v.clone() for k, v in got.items()})
+    return res
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0].name for c in CASES])
+def test_fused_equals_unfused_bitwise(case):
+    """ps_select_topdelta_sparse_decode against ps_select_topdelta then
+    ps_sparse_decode (and ps_combine): page lists, counts, partials, merged
+    outputs identical, for every delta of the case, with the case's splits
+    and with one split (merged in the launch)."""
+    w, spread, deltas, binds = case
+    inp = _inputs(w, spread)
+    g = geometry(inp)
+    meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+    fewer = 0
+    for delta in deltas:
+        for ns in (w.n_splits, 1):
+            a, b = _fused_and_unfused(inp, g, meta, w.budget_pages, w.n_sink, w.n_local, ns,
+                                      delta)
+            for k in a:
+                assert torch.equal(a[k], b[k]), (w.name, delta, ns, k)
+            full = torch.tensor([min(w.budget_pages, int(n)) for n in inp["n_pages_host"]],
+                                device="cuda", dtype=torch.int32)[:, None]
+            fewer += int((a["cnt"] < full).sum())
+    print(f"{w.name}: units keeping fewer pages than the budget: {fewer}")
+    assert fewer > 0 or not binds
+
+
+def test_fused_equals_unfused_b32_64k():
+    """The same on the 32 x 64k workload in the benchmark's launch
+    configuration (delta = 5)."""
+    w = wl.B32_64K
+    inp = wl.make_inputs(w, device="cuda")
+    g = geometry(inp)
+    meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+    a, b = _fused_and_unfused(inp, g, meta, w.budget_pages, w.n_sink, w.n_local, w.n_splits,
+                              5.0)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
 
 
 @pytest.mark.parametrize("case", CASES[:2], ids=[c[0].name for c in CASES[:2]])
