@@ -333,6 +333,32 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
 // queries (called before the selection requests its scores); operator()()
 // then requests the key rows, computes, and returns the threshold. Both are
 // called by every thread of the workgroup; operator()() holds two barriers.
+// DPP lane move of a double (both 32-bit halves), and the max over the 64
+// lanes (uniform result; exact in any order).
+template <int CTRL>
+__device__ __forceinline__ double dppd(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dppu<CTRL>((uint32_t)u);
+  const uint64_t hi = dppu<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, lane);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), lane);
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+
+__device__ __forceinline__ double wave_max_f64(double v) {
+  v = fmax(v, dppd<kDppXor1>(v));
+  v = fmax(v, dppd<kDppXor2>(v));
+  v = fmax(v, dppd<kDppHalfMirror>(v));
+  v = fmax(v, dppd<kDppMirror>(v));  // every lane of a row holds the row's max
+  return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)),
+              fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+
 // GL: query rows held (the group size, or 8 when it is known only at run
 // time).
 template <int WAVES, int D, int GL = 8>
@@ -352,6 +378,7 @@ struct TopDeltaThreshold {
   static constexpr int kVec = Elem<T>::kPerVec;
   static constexpr int kLoads = kCoords / kVec;   // 16-byte key loads per thread
   static_assert(kLoads >= 1 && kCoords % kVec == 0, "key row split");
+  static_assert(kWave % kParts == 0, "a token's eight threads are lanes 8i..8i+7 of a wavefront");
   static_assert(kG * D / 4 <= kThreads, "one float4 of the queries per thread");
 
   const float* qg;     // the group's queries [group, D]
@@ -429,11 +456,20 @@ struct TopDeltaThreshold {
         double acc = 0.0;
 #pragma unroll
         for (int c = 0; c < kCoords; ++c) acc = __builtin_fma(qp[h * D + c], k64[c], acc);
-        // ((e0 + e1) + (e2 + e3)) + ((e4 + e5) + (e6 + e7)) in every lane of the eight
-#pragma unroll
-        for (int m = 1; m < kParts; m <<= 1) {
-          const double o = __shfl_xor(acc, m);
-          acc = (part & m) ? o + acc : acc + o;
+        // ((e0 + e1) + (e2 + e3)) + ((e4 + e5) + (e6 + e7)) in every lane of
+        // the eight (DPP: the neighbour, the other pair of the quad, the
+        // mirrored lane of the other quad, which holds that quad's sum)
+        {
+          const double o = dppd<kDppXor1>(acc);
+          acc = (part & 1) ? o + acc : acc + o;
+        }
+        {
+          const double o = dppd<kDppXor2>(acc);
+          acc = (part & 2) ? o + acc : acc + o;
+        }
+        {
+          const double o = dppd<kDppHalfMirror>(acc);
+          acc = (part & 4) ? o + acc : acc + o;
         }
         const double sv = (double)scale * acc;
         mx[h] = valid ? fmax(mx[h], sv) : mx[h];
@@ -442,8 +478,7 @@ struct TopDeltaThreshold {
 #pragma unroll
     for (int hh = 0; hh < kG; ++hh) {
       if (!G && hh >= group) break;  // uniform
-      double v = mx[hh];
-      for (int off = kWave / 2; off > 0; off >>= 1) v = fmax(v, __shfl_xor(v, off));
+      const double v = wave_max_f64(mx[hh]);
       if (lane == 0) sh->wave_max[wave][hh] = v;
     }
     __syncthreads();
