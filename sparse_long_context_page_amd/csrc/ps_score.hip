@@ -190,11 +190,15 @@ __device__ __forceinline__ f32x4_t tree_sum(const f32x4_t (&a)[N]) {
 
 constexpr int kMfmaWaves = 4;
 constexpr int kMaxTiles = 16;  // 16-page tiles one wavefront streams at most
+// tiles in flight per wavefront with 8-bit metadata (bf16 metadata: 2); an
+// 8-bit tile is half the bytes of a bf16 one
+constexpr int kMeta8InFlight = 3;
 
 // REFRESH: the wavefront holding a request's last page first rebuilds that
 // page's metadata from its keys (the page a decode step appends to), writes
-// it to meta_out and scores the page with it.
-template <int D, int G, bool REFRESH, bool META8>
+// it to meta_out and scores the page with it. NF: tiles of metadata in flight
+// per wavefront.
+template <int D, int G, bool REFRESH, bool META8, int NF>
 __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel(
     const float* __restrict__ q, const void* __restrict__ meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
@@ -278,26 +282,31 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
       bn[i] = ld16(src + D * EB + off);
     }
   };
-  // Two tiles of metadata in flight, requested whatever the run's length.
-  uint4 xa[ML], na[ML], xb[ML], nb[ML];
-  load(0, xa, na);
-  load(1, xb, nb);
-  // The last page's keys, when this wavefront holds it, behind its first
-  // two tiles (waits for the tiles already cover them).
+  // The last page's keys: read by every wavefront of a refresh launch, the
+  // one holding the page reading its own, the others page 0 of this KV head
+  // (the same rows for all, so they stay in cache). Requested before the
+  // metadata tiles, so waiting for them waits for no tile, and with no branch
+  // around the loads or the fold (a branch made the first tile wait for every
+  // load in flight: the compiler could not tell whether the key registers,
+  // reused after the fold, still had loads pending).
   const int tail = np - 1;
   const bool has_tail = REFRESH && n_tiles > 0 && (tail / 16) % w_u == wu;
   const int col_tail = tail % 16;
   PageFold<bf16_t, D> tail_keys;
   int phys_tail = 0;
-  if (has_tail) {
+  if constexpr (REFRESH) {
     int pt = phys[0];
 #pragma unroll
     for (int t = 1; t < kMaxTiles; ++t) pt = t == (tail / 16) / w_u ? phys[t] : pt;
-    phys_tail = __builtin_amdgcn_readlane(pt, col_tail);
+    phys_tail = has_tail ? __builtin_amdgcn_readlane(pt, col_tail) : 0;
     tail_keys.load(k_pool + ((int64_t)phys_tail * hkv + g) * kPage * D, lane);
   }
+  // NF tiles of metadata in flight, requested whatever the run's length.
+  static_assert(NF >= 2 && NF <= 8, "tiles in flight");
+  uint4 xs[NF][ML], ns[NF][ML];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) load(f, xs[f], ns[f]);
   __builtin_amdgcn_sched_barrier(0);  // the split below overlaps these loads
-
   // 2. exact split of the queries, by sign, straight into A fragments:
   // a[sign][part][kb], sign 0 = max(q,0), 1 = min(q,0); part 0 = hi, 1 = mid,
   // 2 = lo; 8 bf16 per lane
@@ -326,15 +335,16 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
     }
   }
 
-  // The last page's metadata: folded from its keys, written out, and kept in
-  // LDS for the last tile.
-  if (has_tail) {
+  // The last page's metadata: folded from its keys (by every wavefront of a
+  // refresh launch), written out and kept in LDS for the last tile by the
+  // wavefront holding the page.
+  if constexpr (REFRESH) {
     using LP = RowLayout<bf16_t, D>;
     float mx[8], mn[8];
     tail_keys.fold(len - tail * kPage, lane, mx, mn);
     const int r0 = lane / LP::kLanesPerRow;
     const int c = lane % LP::kLanesPerRow;
-    if (r0 < 2) {
+    if (has_tail && r0 < 2) {
       const int64_t off = ((int64_t)phys_tail * hkv + g) * 2 * D + r0 * D + c * 8;
       if constexpr (META8) {
         const uint2 codes = r0 == 0 ? fp8_pack8(mx, true) : fp8_pack8(mn, false);
@@ -394,25 +404,50 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
     const int64_t p = tile_page(t) + col;
     if (kgrp == 0 && p < np) out[p] = best;
   };
-  // Steady state: every iteration scores two tiles and requests the next two,
+  // Steady state: every iteration scores NF tiles and requests the next NF,
   // so the number of loads in flight is the same on every path.
   // The main loop never scores the run's last tile (the one that can hold
   // the request's last page).
   int t = 0;
-  for (; t + 3 < n_tiles; t += 2) {
-    score_tile(t, xa, na, false);
-    load(t + 2, xa, na);
-    score_tile(t + 1, xb, nb, false);
-    load(t + 3, xb, nb);
-  }
-  if (t + 2 < n_tiles) {  // three tiles left
-    score_tile(t, xa, na, false);
-    load(t + 2, xa, na);
-    score_tile(t + 1, xb, nb, false);
-    score_tile(t + 2, xa, na, true);
+  if constexpr (NF == 2) {
+    auto& xa = xs[0];
+    auto& na = ns[0];
+    auto& xb = xs[1];
+    auto& nb = ns[1];
+    for (; t + 3 < n_tiles; t += 2) {
+      score_tile(t, xa, na, false);
+      load(t + 2, xa, na);
+      score_tile(t + 1, xb, nb, false);
+      load(t + 3, xb, nb);
+    }
+    if (t + 2 < n_tiles) {  // three tiles left
+      score_tile(t, xa, na, false);
+      load(t + 2, xa, na);
+      score_tile(t + 1, xb, nb, false);
+      score_tile(t + 2, xa, na, true);
+    } else {
+      if (t < n_tiles) score_tile(t, xa, na, t + 1 == n_tiles);
+      if (t + 1 < n_tiles) score_tile(t + 1, xb, nb, true);
+    }
   } else {
-    if (t < n_tiles) score_tile(t, xa, na, t + 1 == n_tiles);
-    if (t + 1 < n_tiles) score_tile(t + 1, xb, nb, true);
+    for (; t + 2 * NF - 1 < n_tiles; t += NF) {
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        score_tile(t + f, xs[f], ns[f], false);
+        load(t + f + NF, xs[f], ns[f]);
+      }
+    }
+    // fewer than 2 NF tiles left, the first NF of them in flight
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      if (t + f < n_tiles) {
+        score_tile(t + f, xs[f], ns[f], t + f + 1 == n_tiles);
+        if (t + f + NF < n_tiles) load(t + f + NF, xs[f], ns[f]);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+      if (t + NF + f < n_tiles) score_tile(t + NF + f, xs[f], ns[f], t + NF + f + 1 == n_tiles);
   }
 }
 
@@ -435,7 +470,8 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
     const int last_phys = (int)std::min<int64_t>(s.num_phys_pages - 1, 0x7fffffff);
     const bf16_t* kp = static_cast<const bf16_t*>(k_pool);
 #define PS_SCORE_MFMA(DD, RR, M8)                                                          \
-  hipLaunchKernelGGL((score_pages_mfma_kernel<DD, kG, RR, M8>), grid, block, 0, st, q, meta, \
+  hipLaunchKernelGGL((score_pages_mfma_kernel<DD, kG, RR, M8, M8 ? kMeta8InFlight : 2>),      \
+                     grid, block, 0, st, q, meta,                                            \
                      page_table, seq_lens, s.hkv, s.max_pages, last_phys, chunks, tpw,       \
                      scores, kp, meta_out)
 #define PS_SCORE_MFMA_M(DD, RR)             \
