@@ -38,9 +38,11 @@ struct ScoreCfg {
   static constexpr int kPagesPerBlock = kPagesPerWave * kScoreWaves;
 };
 
+// meta is not restrict-qualified: a refresh writes the last pages' metadata
+// through meta_out, which is the same buffer.
 template <typename T, int D, int G, bool REFRESH>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
-    const float* __restrict__ q, const T* __restrict__ meta,
+    const float* __restrict__ q, const T* meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
     int max_pages, int chunks_per_unit, float* __restrict__ scores,
     const T* __restrict__ k_pool, T* meta_out) {
@@ -198,9 +200,10 @@ constexpr int kMeta8InFlight = 3;
 // page's metadata from its keys (the page a decode step appends to), writes
 // it to meta_out and scores the page with it. NF: tiles of metadata in flight
 // per wavefront.
+// meta is not restrict-qualified: meta_out (a refresh) is the same buffer.
 template <int D, int G, bool REFRESH, bool META8, int NF>
 __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel(
-    const float* __restrict__ q, const void* __restrict__ meta,
+    const float* __restrict__ q, const void* meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
     int max_pages, int last_phys, int chunks_per_unit, int tiles_per_wave,
     float* __restrict__ scores, const bf16_t* __restrict__ k_pool, void* meta_out) {
@@ -407,7 +410,9 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   // Steady state: every iteration scores NF tiles and requests the next NF,
   // so the number of loads in flight is the same on every path.
   // The main loop never scores the run's last tile (the one that can hold
-  // the request's last page).
+  // the request's last page). A scheduling barrier follows each request:
+  // left free, the scheduler moved the next tile's waits above it (register
+  // pressure), which left one tile in flight instead of NF.
   int t = 0;
   if constexpr (NF == 2) {
     auto& xa = xs[0];
@@ -417,12 +422,15 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
     for (; t + 3 < n_tiles; t += 2) {
       score_tile(t, xa, na, false);
       load(t + 2, xa, na);
+      __builtin_amdgcn_sched_barrier(0);
       score_tile(t + 1, xb, nb, false);
       load(t + 3, xb, nb);
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (t + 2 < n_tiles) {  // three tiles left
       score_tile(t, xa, na, false);
       load(t + 2, xa, na);
+      __builtin_amdgcn_sched_barrier(0);
       score_tile(t + 1, xb, nb, false);
       score_tile(t + 2, xa, na, true);
     } else {
@@ -435,6 +443,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
       for (int f = 0; f < NF; ++f) {
         score_tile(t + f, xs[f], ns[f], false);
         load(t + f + NF, xs[f], ns[f]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // fewer than 2 NF tiles left, the first NF of them in flight
@@ -443,6 +452,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
       if (t + f < n_tiles) {
         score_tile(t + f, xs[f], ns[f], t + f + 1 == n_tiles);
         if (t + f + NF < n_tiles) load(t + f + NF, xs[f], ns[f]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 #pragma unroll
