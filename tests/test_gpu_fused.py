@@ -28,7 +28,18 @@ F32_LONG = [
                 ctx_range=(30000, 40000), budget_pages=40, n_local=2, needles=4,
                 max_pages=2500, kv_dtype="f32", seed=32, n_splits=4, dense_splits=8),
 ]
-CASES = SMALL + F32_LONG + [wl.B32_64K]
+# bf16 pools on grids of more than 256 workgroups (4-wavefront decode
+# workgroups), rows of 375 and 5000 pages (selection tiles of 16 and 32 pages
+# per lane)
+WIDE = [
+    wl.Workload("wide_g2_d64_units280", batch=70, num_q_heads=8, num_kv_heads=4, head_dim=64,
+                ctx_range=(500, 6000), budget_pages=24, n_sink=1, n_local=2, needles=2,
+                permuted_pool=True, max_pages=375, seed=33, n_splits=2, dense_splits=4),
+    wl.Workload("wide_g6_d128_rows5000", batch=34, num_q_heads=12, num_kv_heads=2,
+                head_dim=128, ctx_range=(60000, 80000), budget_pages=64, n_local=4, needles=4,
+                max_pages=5000, seed=34, n_splits=4, dense_splits=8),
+]
+CASES = SMALL + F32_LONG + WIDE + [wl.B32_64K]
 
 
 def _both(inp, budget=None, n_sink=None, n_local=None, n_splits=None):

@@ -188,6 +188,32 @@ def test_fused_equals_unfused_bitwise(case):
     assert fewer > 0 or not binds
 
 
+WIDE_TD = [
+    (W("td_wide_g2_d64_units280", batch=70, num_q_heads=8, num_kv_heads=4, head_dim=64,
+       ctx_range=(500, 6000), budget_pages=24, n_sink=1, n_local=2, permuted_pool=True,
+       max_pages=375, seed=45, n_splits=2, dense_splits=4), 2.5, (0.0, 1.0)),
+    (W("td_wide_g1_d128_rows5000", batch=34, num_q_heads=4, num_kv_heads=4, head_dim=128,
+       ctx_range=(60000, 80000), budget_pages=64, n_sink=1, n_local=3, max_pages=5000,
+       seed=46, n_splits=4, dense_splits=8), 2.5, (0.5,)),
+]
+
+
+@pytest.mark.parametrize("case", WIDE_TD, ids=[c[0].name for c in WIDE_TD])
+def test_fused_equals_unfused_wide_grid(case):
+    """The same on grids of more than 256 workgroups (4-wavefront decode
+    workgroups and their larger selection tiles), with tight bounds."""
+    w, spread, deltas = case
+    inp = _inputs(w, spread)
+    g = geometry(inp)
+    meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+    for delta in deltas:
+        for ns in (w.n_splits, 1):
+            a, b = _fused_and_unfused(inp, g, meta, w.budget_pages, w.n_sink, w.n_local, ns,
+                                      delta)
+            for k in a:
+                assert torch.equal(a[k], b[k]), (w.name, delta, ns, k)
+
+
 def test_fused_equals_unfused_b32_64k():
     """The same on the 32 x 64k workload in the benchmark's launch
     configuration (delta = 5)."""
