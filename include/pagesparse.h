@@ -62,7 +62,7 @@ typedef enum {
 
 /* Element type of the metadata pool.
  *   PS_META_KV        kmax and kmin in kv_dtype (exact).
- *   PS_META_FP8_E4M3  8-bit bounds, bf16 pools only: kmax rounded up and
+ *   PS_META_FP8_E4M3  8-bit bounds (bf16 or fp32 pools): kmax rounded up and
  *                     kmin rounded down to OCP E4M3 (no infinities; bias 7;
  *                     largest finite 448), so for every query the bound can
  *                     only grow and stays an upper bound of q.k. The page
@@ -89,9 +89,8 @@ typedef enum {
  *   kv_dtype        element type of K and V
  *   meta_format     element type of the metadata (ps_meta_format); entry
  *                   points that do not read metadata ignore it. A value
- *                   outside ps_meta_format is PS_ERR_SHAPE, and
- *                   PS_META_FP8_E4M3 with fp32 pools PS_ERR_UNSUPPORTED, in
- *                   every entry point                                    */
+ *                   outside ps_meta_format is PS_ERR_SHAPE in every entry
+ *                   point                                                */
 typedef struct {
   int32_t batch;
   int32_t num_q_heads;
@@ -152,7 +151,7 @@ int ps_build_page_meta(const ps_geom* geom, const void* k_pool, const int32_t* p
  * Computed in fp32 as sum_d (max(q,0)*kmax_d + min(q,0)*kmin_d) with exact
  * products and a fixed summation order (bf16 metadata: on the matrix cores,
  * q split exactly into three bf16 terms; fp32 metadata: fma; 8-bit metadata:
- * widened exactly to bf16, then as bf16), so results are bitwise
+ * widened exactly to the pool's dtype, then as that metadata), so results are bitwise
  * reproducible; entries at p >= n_b are not written.
  * Device preconditions: as ps_build_page_meta, with meta built for every
  * page read. */

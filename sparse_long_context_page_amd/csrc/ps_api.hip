@@ -41,7 +41,6 @@ int check_geom(const ps_geom* g, ps::Shape* s) {
   if (g->head_dim != 64 && g->head_dim != 128) return PS_ERR_UNSUPPORTED;
   if (g->page_size != ps::kPage) return PS_ERR_UNSUPPORTED;
   if (g->kv_dtype != PS_F32 && g->kv_dtype != PS_BF16) return PS_ERR_UNSUPPORTED;
-  if (g->meta_format == PS_META_FP8_E4M3 && g->kv_dtype != PS_BF16) return PS_ERR_UNSUPPORTED;
   const int64_t elem = g->kv_dtype == PS_BF16 ? 2 : 4;
   int64_t t;
   // token positions p * page_size and page counts stay inside int32

@@ -101,6 +101,24 @@ __device__ __forceinline__ uint2 fp8_pack8(const float (&f)[8], bool up) {
   return make_uint2(w[0], w[1]);
 }
 
+// Four codes, one word (code j in byte j).
+__device__ __forceinline__ uint32_t fp8_pack4(const float (&f)[4], bool up) {
+  uint32_t w = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w |= fp8_e4m3_directed(f[j], up) << (8 * j);
+  return w;
+}
+
+// Four codes (one word, code j in byte j) widened exactly to fp32.
+__device__ __forceinline__ void fp8x4_to_f32x4(uint32_t w, float (&f)[4]) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);  // codes 0, 1
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);   // codes 2, 3
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
+}
+
 // Four E4M3 codes (one word, code j in byte j) widened to four bf16 (two
 // words, value j in half j): every E4M3 value is a bf16 value, so the
 // hardware conversion to fp32 followed by keeping the high halves is exact.

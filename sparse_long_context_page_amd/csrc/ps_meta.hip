@@ -44,9 +44,12 @@ __global__ __launch_bounds__(kMetaWaves * kWave) void build_page_meta_kernel(
   pf.fold(cnt, lane, mx, mn);
   if (r0 < 2) {
     const int64_t off = ((int64_t)phys * hkv + g) * 2 * D + r0 * D + c * V;
-    if constexpr (META8) {
+    if constexpr (META8 && V == 8) {
       *reinterpret_cast<uint2*>(static_cast<uint8_t*>(meta) + off) =
           r0 == 0 ? fp8_pack8(mx, true) : fp8_pack8(mn, false);
+    } else if constexpr (META8) {
+      *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(meta) + off) =
+          r0 == 0 ? fp8_pack4(mx, true) : fp8_pack4(mn, false);
     } else {
       st16(static_cast<T*>(meta) + off, r0 == 0 ? pack(mx) : pack(mn));
     }
@@ -62,15 +65,12 @@ hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int3
   const int64_t blocks = (waves + kMetaWaves - 1) / kMetaWaves;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   dim3 grid((unsigned)blocks), block(kMetaWaves * kWave);
-  if (s.meta8) {  // bf16 keys only (checked by the caller)
-    if (s.head_dim == 64)
-      hipLaunchKernelGGL((build_page_meta_kernel<bf16_t, 64, true>), grid, block, 0, st,
-                         static_cast<const bf16_t*>(k_pool), page_table, seq_lens, page_begin,
+  if (s.meta8) {
+    PS_WITH_KV(s.kv_bf16, s.head_dim, {
+      hipLaunchKernelGGL((build_page_meta_kernel<TElem, kD, true>), grid, block, 0, st,
+                         static_cast<const TElem*>(k_pool), page_table, seq_lens, page_begin,
                          pages, s.batch, s.hkv, s.max_pages, items_per_req, meta);
-    else
-      hipLaunchKernelGGL((build_page_meta_kernel<bf16_t, 128, true>), grid, block, 0, st,
-                         static_cast<const bf16_t*>(k_pool), page_table, seq_lens, page_begin,
-                         pages, s.batch, s.hkv, s.max_pages, items_per_req, meta);
+    });
     return hipGetLastError();
   }
   PS_WITH_KV(s.kv_bf16, s.head_dim, {

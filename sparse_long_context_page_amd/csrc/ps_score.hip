@@ -20,6 +20,7 @@
 // vector)), writes the page's metadata and scores the page from the folded
 // registers.
 #include <algorithm>
+#include <type_traits>
 
 #include "ps_device.h"
 #include "ps_launch.h"
@@ -38,18 +39,22 @@ struct ScoreCfg {
   static constexpr int kPagesPerBlock = kPagesPerWave * kScoreWaves;
 };
 
-// meta is not restrict-qualified: a refresh writes the last pages' metadata
-// through meta_out, which is the same buffer.
-template <typename T, int D, int G, bool REFRESH>
+// META8: the metadata are 8-bit codes (4 per lane and bound), widened
+// exactly to fp32. meta is not restrict-qualified: a refresh writes the last
+// pages' metadata through meta_out, which is the same buffer.
+template <typename T, int D, int G, bool REFRESH, bool META8>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
-    const float* __restrict__ q, const T* meta,
+    const float* __restrict__ q, const void* meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
     int max_pages, int chunks_per_unit, float* __restrict__ scores,
-    const T* __restrict__ k_pool, T* meta_out) {
+    const T* __restrict__ k_pool, void* meta_out) {
   using C = ScoreCfg<T, D>;
   using L = typename C::L;
   constexpr int V = L::kVec;
   constexpr int LPR = L::kLanesPerRow;
+  static_assert(!META8 || V == 4, "8-bit codes: four per lane and bound");
+  using MV = std::conditional_t<META8, uint32_t, uint4>;  // one lane's bound values
+  constexpr int EB = META8 ? 1 : (int)sizeof(T);          // bytes per metadata element
 
   // Consecutive workgroups go to the 8 XCDs in turn; rotating the chunk
   // index by the request spreads the leading chunks of short requests (the
@@ -69,18 +74,19 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   const int c = lane % LPR;
 
   // Issue every metadata load of this wavefront first.
-  uint4 vmax[kScoreIters], vmin[kScoreIters];
+  MV vmax[kScoreIters], vmin[kScoreIters];
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
     const int p = p0 + it * C::kPagesPerLoad + slot;
     if (p < np) {
       const int phys = page_table[(int64_t)b * max_pages + p];
-      const T* src = meta + ((int64_t)phys * hkv + g) * 2 * D + c * V;
-      vmax[it] = ld16(src);
-      vmin[it] = ld16(src + D);
+      const uint8_t* src =
+          static_cast<const uint8_t*>(meta) + (((int64_t)phys * hkv + g) * 2 * D + c * V) * EB;
+      vmax[it] = *reinterpret_cast<const MV*>(src);
+      vmin[it] = *reinterpret_cast<const MV*>(src + D * EB);
     } else {
-      vmax[it] = make_uint4(0, 0, 0, 0);
-      vmin[it] = make_uint4(0, 0, 0, 0);
+      vmax[it] = MV{};
+      vmin[it] = MV{};
     }
   }
 
@@ -113,12 +119,20 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   }
 
   // The last page's metadata, folded from its keys: lane (row r0, column
-  // vector c) ends with columns c of both bounds, the columns it scores.
+  // vector c) ends with columns c of both bounds, the columns it scores
+  // (8-bit: the codes written, widened back).
   float tx[V], tn[V];
   if (has_tail) {
     tail_keys.fold(len - tail * kPage, lane, tx, tn);
-    if (slot < 2)
-      st16(meta_out + tail_base * 2 * D + slot * D + c * V, slot == 0 ? pack(tx) : pack(tn));
+    uint8_t* dst = static_cast<uint8_t*>(meta_out) + (tail_base * 2 * D + slot * D + c * V) * EB;
+    if constexpr (META8) {
+      const uint32_t cx = fp8_pack4(tx, true), cn = fp8_pack4(tn, false);
+      if (slot < 2) *reinterpret_cast<uint32_t*>(dst) = slot == 0 ? cx : cn;
+      fp8x4_to_f32x4(cx, tx);
+      fp8x4_to_f32x4(cn, tn);
+    } else {
+      if (slot < 2) st16(dst, slot == 0 ? pack(tx) : pack(tn));
+    }
   }
 
   float* out = scores + (int64_t)unit * max_pages;
@@ -126,8 +140,13 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   for (int it = 0; it < kScoreIters; ++it) {
     const int p = p0 + it * C::kPagesPerLoad + slot;
     float kx[V], kn[V];
-    unpack(vmax[it], kx);
-    unpack(vmin[it], kn);
+    if constexpr (META8) {
+      fp8x4_to_f32x4(vmax[it], kx);
+      fp8x4_to_f32x4(vmin[it], kn);
+    } else {
+      unpack(vmax[it], kx);
+      unpack(vmin[it], kn);
+    }
     if (has_tail && p == tail) {
 #pragma unroll
       for (int j = 0; j < V; ++j) {
@@ -502,10 +521,12 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
 #undef PS_SCORE_MFMA
     return hipGetLastError();
   }
-  // fp32 metadata: the vector-ALU kernel
+  // fp32 K: the vector-ALU kernel (fp32 or 8-bit metadata)
   const float* kp = static_cast<const float*>(k_pool);
-  float* mo = static_cast<float*>(meta_out);
-  const float* mt = static_cast<const float*>(meta);
+#define PS_SCORE_F32_LAUNCH(DD, RR, M8)                                                     \
+  hipLaunchKernelGGL((score_pages_kernel<float, DD, kG, RR, M8>), grid, block, 0, st, q,    \
+                     meta, page_table, seq_lens, s.hkv, s.max_pages, chunks, scores, kp,   \
+                     meta_out)
 #define PS_SCORE_F32(DD)                                                                    \
   do {                                                                                      \
     const int per_block = ScoreCfg<float, DD>::kPagesPerBlock;                              \
@@ -514,14 +535,13 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;                           \
     const dim3 grid((unsigned)blocks);                                                      \
     PS_WITH_GROUP(s.group, {                                                                \
-      if (kp)                                                                               \
-        hipLaunchKernelGGL((score_pages_kernel<float, DD, kG, true>), grid, block, 0, st, q, \
-                           mt, page_table, seq_lens, s.hkv, s.max_pages, chunks, scores,   \
-                           kp, mo);                                                         \
-      else                                                                                  \
-        hipLaunchKernelGGL((score_pages_kernel<float, DD, kG, false>), grid, block, 0, st,  \
-                           q, mt, page_table, seq_lens, s.hkv, s.max_pages, chunks,        \
-                           scores, kp, mo);                                                 \
+      if (kp) {                                                                             \
+        if (s.meta8) PS_SCORE_F32_LAUNCH(DD, true, true);                                   \
+        else PS_SCORE_F32_LAUNCH(DD, true, false);                                          \
+      } else {                                                                              \
+        if (s.meta8) PS_SCORE_F32_LAUNCH(DD, false, true);                                  \
+        else PS_SCORE_F32_LAUNCH(DD, false, false);                                         \
+      }                                                                                     \
     });                                                                                     \
   } while (0)
   if (s.head_dim == 64)
@@ -529,6 +549,7 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
   else
     PS_SCORE_F32(128);
 #undef PS_SCORE_F32
+#undef PS_SCORE_F32_LAUNCH
   return hipGetLastError();
 }
 

@@ -64,7 +64,6 @@ def score(g):
 @pytest.mark.parametrize("kw,code", [
     (dict(meta_format=2), _lib.PS_ERR_SHAPE),
     (dict(meta_format=-1), _lib.PS_ERR_SHAPE),
-    (dict(meta_format=_lib.PS_META_FP8_E4M3, kv_dtype=_lib.PS_F32), _lib.PS_ERR_UNSUPPORTED),
     (dict(batch=-1), _lib.PS_ERR_SHAPE),
     (dict(num_q_heads=0), _lib.PS_ERR_SHAPE),
     (dict(num_q_heads=13), _lib.PS_ERR_SHAPE),
@@ -87,10 +86,11 @@ def test_geometry_validation(kw, code):
     assert score(geom(**kw)) == code
 
 
-def test_fp8_metadata_geometry_accepted():
-    """8-bit metadata with bf16 pools passes the geometry checks (a call with
-    batch 0 validates and enqueues nothing)."""
-    g = geom(meta_format=_lib.PS_META_FP8_E4M3, batch=0)
+@pytest.mark.parametrize("kv", [_lib.PS_BF16, _lib.PS_F32])
+def test_fp8_metadata_geometry_accepted(kv):
+    """8-bit metadata with bf16 or fp32 pools passes the geometry checks (a
+    call with batch 0 validates and enqueues nothing)."""
+    g = geom(meta_format=_lib.PS_META_FP8_E4M3, batch=0, kv_dtype=kv)
     lib = _lib.load()
     assert lib.ps_score_pages(g, X, X, X, X, X, None) == _lib.PS_OK
     assert lib.ps_build_page_meta(g, X, X, X, None, 4, X, None) == _lib.PS_OK

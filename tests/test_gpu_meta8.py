@@ -1,5 +1,6 @@
 """8-bit metadata (E4M3 bounds: kmax rounded up, kmin rounded down) through
-the C ABI against the fp64 oracle: every code decodes to its value, the codes
+the C ABI against the fp64 oracle, on bf16 pools (matrix-core score) and fp32
+pools (vector-ALU score): every code decodes to its value, the codes
 equal the oracle's directed rounding bit for bit, scores match the fp64 bound
 on the 8-bit values, selections are identical outside the ambiguity band,
 outputs are within the rel-L2 gate, and the refresh inside the score launch
@@ -18,11 +19,12 @@ from test_gpu_parity import SMALL
 
 pytestmark = pytest.mark.gpu
 
-BF16 = [w for w in SMALL if w.kv_dtype == "bf16"]
+CASES = SMALL
 
 
+@pytest.mark.parametrize("kv", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_every_code_decodes_to_its_value(d):
+def test_every_code_decodes_to_its_value(d, kv):
     """A request per coordinate, its query one-hot on that coordinate, all
     reading the same pages whose kmax rows hold every finite code and whose
     kmin is -448: score[b, p] = value of the code at (p, d=b). This pins the
@@ -33,7 +35,7 @@ def test_every_code_decodes_to_its_value(d):
     meta = np.zeros((n_pages, 1, 2, d), dtype=np.uint8)
     meta[:, 0, 0, :] = codes.reshape(n_pages, d)
     meta[:, 0, 1, :] = 0xFE  # -448
-    g = Geometry(d, 1, 1, d, n_pages, n_pages, torch.bfloat16, 16, "fp8")
+    g = Geometry(d, 1, 1, d, n_pages, n_pages, kv, 16, "fp8")
     q = torch.eye(d, dtype=torch.float32).reshape(d, 1, d).cuda()
     table = torch.arange(n_pages, dtype=torch.int32).repeat(d, 1).cuda()
     lens = torch.full((d,), 16 * n_pages, dtype=torch.int32).cuda()
@@ -48,7 +50,7 @@ def test_every_code_decodes_to_its_value(d):
 @pytest.fixture(scope="module")
 def cases():
     out = {}
-    for w in BF16:
+    for w in CASES:
         inp = wl.make_inputs(w, device="cuda")
         res = run_step(inp, meta_format="fp8")
         units = [(b, g) for b in range(w.batch) for g in range(w.num_kv_heads)]
@@ -56,7 +58,7 @@ def cases():
     return out
 
 
-@pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_codes_bit_exact(cases, w):
     _, inp, res, hosts = cases[w.name]
     for (b, g), hu in hosts.items():
@@ -70,7 +72,7 @@ def test_codes_bit_exact(cases, w):
         np.testing.assert_array_equal(dev[:, 1], cmin, err_msg=f"kmin codes b={b} g={g}")
 
 
-@pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_scores_match_fp64(cases, w):
     _, inp, res, hosts = cases[w.name]
     worst = 0.0
@@ -82,7 +84,7 @@ def test_scores_match_fp64(cases, w):
     assert worst <= SCORE_REL
 
 
-@pytest.mark.parametrize("w", BF16, ids=[w.name for w in BF16])
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
 def test_selection_and_outputs(cases, w):
     _, inp, res, hosts = cases[w.name]
     worst = 0.0
@@ -97,7 +99,7 @@ def test_selection_and_outputs(cases, w):
     print(f"{w.name}: max rel-L2 {worst:.3e} (gate {gate(w)})")
 
 
-@pytest.mark.parametrize("w", BF16 + [wl.B32_64K], ids=[w.name for w in BF16 + [wl.B32_64K]])
+@pytest.mark.parametrize("w", CASES + [wl.B32_64K], ids=[w.name for w in CASES + [wl.B32_64K]])
 def test_refresh_score_equals_meta_then_score_bitwise(w):
     inp = wl.make_inputs(w, device="cuda")
     g = geometry(inp, "fp8")
@@ -117,11 +119,11 @@ def test_refresh_score_equals_meta_then_score_bitwise(w):
         assert torch.equal(got[b, :, :int(n)], want[b, :, :int(n)]), (w.name, b)
 
 
-def test_fp8_scores_bound_the_bf16_scores():
-    """On the same inputs the score on 8-bit metadata is >= the score on bf16
-    metadata for every page (the 8-bit box contains the exact one), and both
-    are finite."""
-    w = wl.B8_16K
+@pytest.mark.parametrize("w", [wl.B8_16K, wl.TINY], ids=["b8_bf16", "tiny_f32"])
+def test_fp8_scores_bound_the_kv_dtype_scores(w):
+    """On the same inputs the score on 8-bit metadata is >= the score on
+    metadata in the pool's dtype for every page (the 8-bit box contains the
+    exact one), and both are finite."""
     inp = wl.make_inputs(w, device="cuda")
     s = {}
     for fmt in ("kv", "fp8"):
