@@ -51,7 +51,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="b32_64k_needles_local4")
-    ap.add_argument("--sets", type=int, default=4, help="independent input batches cycled")
+    ap.add_argument("--sets", type=int, default=None,
+                    help="independent input batches cycled (default: enough that one pass "
+                         "over them touches 3x the 256 MB memory-side cache, 4 to 32)")
     ap.add_argument("--dense-steps", type=int, default=20)
     ap.add_argument("--parity-units", type=int, default=6)
     ap.add_argument("--cpu-units", type=int, default=0,
@@ -79,6 +81,28 @@ def parse():
 
 # ---------------------------------------------------------------------------
 # setup
+
+
+MALL_BYTES = 256 << 20  # memory-side (Infinity) cache of the chip
+
+
+def default_sets(w, meta_format, acc):
+    """Input sets to cycle so that the steps between two uses of one set
+    touch at least three times the memory-side cache: every timed step then
+    reads its bytes from HBM (4 to 32 sets; the smallest workloads are bound
+    by launches, not bytes)."""
+    if w.lengths is not None:
+        lens = list(w.lengths)
+    elif w.context is not None:
+        lens = [w.context] * w.batch
+    else:
+        lens = [(w.ctx_range[0] + w.ctx_range[1]) // 2] * w.batch
+    elem = 2 if w.kv_dtype == "bf16" else 4
+    meta_elem = 1 if meta_format == "fp8" else elem
+    touched = (acc.meta_bytes(lens, w.num_kv_heads, w.head_dim, meta_elem, w.page_size) +
+               acc.selected_kv_bytes_uniform(lens, w.num_kv_heads, w.head_dim, elem,
+                                             w.page_size, w.budget_pages))
+    return int(min(32, max(4, math.ceil(3 * MALL_BYTES / max(touched, 1)))))
 
 
 def make_set(w, seed, torch, wl, ps, meta_format="kv", inp=None):
@@ -312,6 +336,8 @@ def main():
         w = w.replace(n_splits=args.n_splits)
     if args.dense_splits:
         w = w.replace(dense_splits=args.dense_splits)
+    if args.sets is None:
+        args.sets = default_sets(w, args.meta_format, acc)
     print(f"# setup {w.name}: {args.sets} input sets", file=sys.stderr, flush=True)
     sets = [make_set(w, w.seed + 17 * i, torch, wl, ps, args.meta_format)
             for i in range(args.sets)]
