@@ -73,31 +73,39 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   const int slot = lane / LPR;
   const int c = lane % LPR;
 
-  // Issue every metadata load of this wavefront first.
-  MV vmax[kScoreIters], vmin[kScoreIters];
+  // The last page's keys, read (and folded below) by every wavefront of a
+  // refresh launch: the one holding the page (p0 <= np - 1 here) its own,
+  // the others page 0 of this KV head, before the metadata and with no branch
+  // around the loads (a branch made the compiler wait for every load in
+  // flight at the join).
+  const int tail = np - 1;
+  const bool has_tail = REFRESH && tail < p0 + C::kPagesPerWave;  // uniform
+  // page-table entries first (the tail's and this wavefront's pages')
+  int tp = 0;
+  if constexpr (REFRESH) tp = page_table[(int64_t)b * max_pages + tail];
+  int phys_it[kScoreIters];
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
     const int p = p0 + it * C::kPagesPerLoad + slot;
-    if (p < np) {
-      const int phys = page_table[(int64_t)b * max_pages + p];
-      const uint8_t* src =
-          static_cast<const uint8_t*>(meta) + (((int64_t)phys * hkv + g) * 2 * D + c * V) * EB;
-      vmax[it] = *reinterpret_cast<const MV*>(src);
-      vmin[it] = *reinterpret_cast<const MV*>(src + D * EB);
-    } else {
-      vmax[it] = MV{};
-      vmin[it] = MV{};
-    }
+    phys_it[it] = page_table[(int64_t)b * max_pages + min(p, np - 1)];
+  }
+  PageFold<T, D> tail_keys;
+  int64_t tail_base = g;
+  if constexpr (REFRESH) {
+    tail_base = (int64_t)(has_tail ? tp : 0) * hkv + g;
+    tail_keys.load(k_pool + tail_base * kPage * D, lane);
   }
 
-  // The last page's keys, when this wavefront holds it (p0 <= np - 1 here).
-  const int tail = np - 1;
-  const bool has_tail = REFRESH && tail < p0 + C::kPagesPerWave;  // uniform
-  PageFold<T, D> tail_keys;
-  int64_t tail_base = 0;
-  if (has_tail) {
-    tail_base = (int64_t)page_table[(int64_t)b * max_pages + tail] * hkv + g;
-    tail_keys.load(k_pool + tail_base * kPage * D, lane);
+  // Then every metadata load of this wavefront, unconditionally (a slot past
+  // the request re-reads the last page's metadata and its score is not
+  // written): a conditional load made the compiler wait after each one.
+  MV vmax[kScoreIters], vmin[kScoreIters];
+#pragma unroll
+  for (int it = 0; it < kScoreIters; ++it) {
+    const uint8_t* src = static_cast<const uint8_t*>(meta) +
+                         (((int64_t)phys_it[it] * hkv + g) * 2 * D + c * V) * EB;
+    vmax[it] = *reinterpret_cast<const MV*>(src);
+    vmin[it] = *reinterpret_cast<const MV*>(src + D * EB);
   }
 
   // Split query coordinates by sign: qp = max(q, 0) multiplies kmax,
@@ -122,16 +130,16 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   // vector c) ends with columns c of both bounds, the columns it scores
   // (8-bit: the codes written, widened back).
   float tx[V], tn[V];
-  if (has_tail) {
+  if constexpr (REFRESH) {
     tail_keys.fold(len - tail * kPage, lane, tx, tn);
     uint8_t* dst = static_cast<uint8_t*>(meta_out) + (tail_base * 2 * D + slot * D + c * V) * EB;
     if constexpr (META8) {
       const uint32_t cx = fp8_pack4(tx, true), cn = fp8_pack4(tn, false);
-      if (slot < 2) *reinterpret_cast<uint32_t*>(dst) = slot == 0 ? cx : cn;
+      if (has_tail && slot < 2) *reinterpret_cast<uint32_t*>(dst) = slot == 0 ? cx : cn;
       fp8x4_to_f32x4(cx, tx);
       fp8x4_to_f32x4(cn, tn);
     } else {
-      if (slot < 2) st16(dst, slot == 0 ? pack(tx) : pack(tn));
+      if (has_tail && slot < 2) st16(dst, slot == 0 ? pack(tx) : pack(tn));
     }
   }
 
