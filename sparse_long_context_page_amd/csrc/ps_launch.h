@@ -11,7 +11,7 @@ struct Shape {
   int batch, hq, hkv, group, head_dim, max_pages;
   int64_t num_phys_pages;
   int kv_bf16;  // 1: bf16 pools, 0: fp32 pools
-  int meta8;    // 1: 8-bit metadata bounds (bf16 pools only), 0: metadata in the pool dtype
+  int meta8;    // 1: 8-bit metadata bounds, 0: metadata in the pool dtype
 };
 
 hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int32_t* page_table,
@@ -19,7 +19,7 @@ hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int3
                                   int n_pages, void* meta, hipStream_t st);
 
 // k_pool and meta_out non-null: also rebuild each request's last page's
-// metadata from k_pool into meta_out before scoring it (bf16 only).
+// metadata from k_pool into meta_out before scoring it.
 hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
                               const int32_t* page_table, const int32_t* seq_lens, float* scores,
                               const void* k_pool, void* meta_out, hipStream_t st);

@@ -160,7 +160,7 @@ def test_step_with_tail_refresh_fused_equals_unfused():
               enumerate(inp["n_pages_host"])]] = -2.0
         step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
                           inp["scale"], fused=fused)
-        if not fused:  # the tail pages rebuilt by their own launch, then the five launches
+        if not fused:  # the tail pages rebuilt by a launch of their own, then four more
             step.refresh_tail_meta(inp["k_pool"], inp["page_table"], inp["seq_lens"], tail, meta)
         out, lse = step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
                                inp["seq_lens"], inp["sink"], refresh_tail=fused)
