@@ -214,6 +214,40 @@ def test_fused_equals_unfused_wide_grid(case):
                 assert torch.equal(a[k], b[k]), (w.name, delta, ns, k)
 
 
+@pytest.mark.parametrize("rows", [9000, 20000])
+def test_standalone_selection_long_rows(rows):
+    """The standalone top-delta selection on rows past the fused decode's limit
+    (its register tiles of 32 and 128 pages per lane): the oracle's rule on
+    the device's own scores, bit for bit outside 1e-12 of the threshold."""
+    w = W(f"td_rows{rows}", batch=2, num_q_heads=1, num_kv_heads=1, head_dim=64,
+          ctx_range=(16 * rows - 4000, 16 * rows), budget_pages=48, n_sink=1, n_local=3,
+          permuted_pool=True, max_pages=rows, seed=47 + rows % 7)
+    inp = _inputs(w, 2.5)
+    g = geometry(inp)
+    sc = _scores(inp, g)
+    sc_h = sc.cpu().numpy().astype(np.float64)
+    fewer = 0
+    for delta in (0.0, 1.0):
+        sel, cnt = _select(inp, g, sc, w.budget_pages, w.n_sink, w.n_local, delta)
+        for b in range(w.batch):
+            n = int(inp["n_pages_host"][b])
+            hu = unit_host(inp, b, 0)
+            mt = _oracle_pseudo_max(hu, n, w.n_sink, w.n_local, w.budget_pages)
+            want, _, _, tau = ref.select_pages_topdelta(
+                sc_h[b, 0, :n], n, w.budget_pages, w.n_sink, w.n_local,
+                np.float32(inp["scale"]), mt, delta)
+            k = int(cnt[b, 0])
+            got = [int(x) for x in sel[b, 0, :k]]
+            assert all(int(x) == -1 for x in sel[b, 0, k:])
+            near = {p for p in range(n) if tau is not None and
+                    abs(float(np.float32(inp["scale"])) * sc_h[b, 0, p] - tau) <=
+                    1e-12 * max(abs(tau), 1.0)}
+            assert set(got) - near == set(int(x) for x in want) - near, (rows, delta, b)
+            assert got == sorted(got)
+            fewer += k < min(w.budget_pages, n)
+    print(f"rows {rows}: units keeping fewer pages than the budget: {fewer}")
+
+
 def test_fused_equals_unfused_b32_64k():
     """The same on the 32 x 64k workload in the benchmark's launch
     configuration (delta = 5)."""
