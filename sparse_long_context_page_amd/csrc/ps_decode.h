@@ -1,9 +1,12 @@
-// Split-KV decode over a page list (sparse) or over every page (dense):
-// per split, the running max, normaliser and unnormalised accumulator of the
-// softmax of scale*q.k for every query head of one KV head.
-// ("Don't read the haystack", sections "Part one: hitting the wall on
-// purpose" and "Part two: the skipping"; "Attention: Undivided &
-// Uncompressed", section "Traffic", for the rescaling merge.)
+// Split-KV decode over every page (dense), a page list (sparse), or the
+// pages the workgroup selects itself (top-k or top-delta): per split, the
+// running max, normaliser and unnormalised accumulator of the softmax of
+// scale*q.k for every query head of one KV head; with one split, optionally
+// the merged output. ("Don't read the haystack", sections "Part one: hitting
+// the wall on purpose" and "Part two: the skipping"; "Attention: Undivided &
+// Uncompressed", section "Traffic", for the rescaling merge.) Two kernels:
+// decode_kernel (fp32 pools, vector ALUs, described here) and
+// decode_mfma_kernel (bf16 pools, matrix cores, described at its definition).
 //
 // One workgroup of 4 wavefronts per (request, KV head, split). The split's
 // pages are dealt round-robin to the wavefronts, two pages in flight per
