@@ -553,7 +553,18 @@ def main():
     c1.record()
     torch.cuda.synchronize()
     copy_gbps = 2 * src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del src, dst
+    # achievable read stream: row sums of the same 2 GiB (reads only; torch's
+    # reduction, about 6 TB/s on this chip)
+    rows = src.view(4096, -1)
+    for _ in range(2):
+        rows.sum(dim=1)
+    c0.record()
+    for _ in range(5):
+        rows.sum(dim=1)
+    c1.record()
+    torch.cuda.synchronize()
+    read_gbps = src.numel() * 4 * 5 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del src, dst, rows
 
     # -- bytes ---------------------------------------------------------------
     inp0 = s0["inp"]
@@ -622,6 +633,7 @@ def main():
         "dense_hbm_gbps": round(dense_b / (dense_us * 1e-6) / 1e9, 1),
         "speedup_vs_dense": round(dense_us / step_us, 3),
         "copy_gbps_read_plus_write": round(copy_gbps, 1),
+        "read_stream_gbps": round(read_gbps, 1),
         "timed_wall_ms": round(wall_ms, 3),
         "eager_us_per_step": round(eager_us, 3),
         "us_per_step_p10_p50_p90": [round(pct(0.1), 3), round(pct(0.5), 3), round(pct(0.9), 3)],
@@ -634,7 +646,9 @@ def main():
                      "frac": round(score_gbps / PEAK_HBM_GBPS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": dom_b,
-                     "avg_launch_us": round(kern_us[dom_key], 3)},
+                     "avg_launch_us": round(kern_us[dom_key], 3),
+                     "achievable_read_gbps": round(read_gbps, 1),
+                     "frac_of_achievable_read": round(score_gbps / read_gbps, 4)},
     }
     if args.meta_format == "kv" and not args.no_fp8_line:
         print("# 8-bit metadata", file=sys.stderr, flush=True)
