@@ -179,6 +179,42 @@ def sample_units(w, k):
     return [units[int(i * stride)] for i in range(k)]
 
 
+def selection_diagnostics(s, w, sel_h, cnt_h, units, torch):
+    """Diagnostics of what the selection keeps (not gates): needle recall over
+    every (request, KV head) that has needle pages, and, on sampled units, the
+    share of each query head's exact softmax mass (over every valid token of
+    the request, no sink) that lies on the selected tokens. Plain torch ops
+    on the device in fp32."""
+    inp = s["inp"]
+    ps_ = w.page_size
+    rec = []
+    for (b, g), pages in inp["needle_pages"].items():
+        if pages:
+            chosen = set(int(x) for x in sel_h[b, g, :int(cnt_h[b, g])])
+            rec.append(sum(p in chosen for p in pages) / len(pages))
+    masses = []
+    for b, g in units:
+        n_tok = int(inp["seq_lens_host"][b])
+        n = -(-n_tok // ps_)
+        phys = inp["page_table"][b, :n].long()
+        keys = inp["k_pool"][phys, g].reshape(n * ps_, w.head_dim)[:n_tok].float()
+        q = inp["q"][b, g * w.group:(g + 1) * w.group].float()
+        x = (q @ keys.T.contiguous()) * inp["scale"]
+        prob = torch.softmax(x, dim=1)
+        kept = torch.zeros(n, dtype=torch.bool, device=x.device)
+        kept[torch.as_tensor(sel_h[b, g, :int(cnt_h[b, g])], device=x.device).long()] = True
+        on = kept.repeat_interleave(ps_)[:n_tok]
+        masses += prob[:, on].sum(dim=1).tolist()
+    out = {"kind": "diagnostic, not a gate", "mass_units": len(units)}
+    if rec:
+        out.update(needle_recall_mean=round(float(sum(rec) / len(rec)), 4),
+                   needle_recall_min=round(float(min(rec)), 4))
+    if masses:
+        out.update(captured_mass_mean=round(float(sum(masses) / len(masses)), 4),
+                   captured_mass_min=round(float(min(masses)), 4))
+    return out
+
+
 def parity_gate(s, w, units, wl):
     """Selection identical to the oracle outside the ambiguity band; output
     rel-L2 within the gate. Returns a summary dict; raises on failure."""
@@ -640,6 +676,9 @@ def main():
         "warm_same_set_us_per_step": round(warm_us, 3),
         "one_step_per_graph_us_per_step": round(one_graph_us, 3),
         "parity": parity,
+        "selection": selection_diagnostics(
+            s0, w, sel_h, s0["step"].sel_count.cpu().numpy(),
+            sample_units(w, args.parity_units), torch),
         "roofline": {"kernel": "ps_refresh_score_pages",
                      "bound": "hbm",
                      "achieved": round(score_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
