@@ -237,7 +237,7 @@ def parity_gate(s, w, units, wl):
             if k != min(w.budget_pages, r["n"]):
                 raise AssertionError(f"parity: sel_count {k} at unit {(b, g)}")
             amb, _ = ref.ambiguous_pages(r["scores"], r["n"], w.budget_pages, w.n_sink,
-                                         w.n_local)
+                                         w.n_local, mag=r["mag"])
         else:  # threshold band: the device compares its fp32 scores
             n = r["n"]
             forced = sorted(set(range(min(w.n_sink, n))) | set(range(max(0, n - w.n_local), n)))
@@ -246,7 +246,8 @@ def parity_gate(s, w, units, wl):
                                    hu["page_size"])
             mt = ref.pseudo_max(hu["q"][0].astype(np.float64), kf, hu["scale"])
             amb = ref.ambiguous_pages_topdelta(r["scores"], n, w.budget_pages, w.n_sink,
-                                               w.n_local, hu["scale"], mt, delta, rel=1e-5)
+                                               w.n_local, hu["scale"], mt, delta, rel=1e-5,
+                                               mag=r["mag"])
         got = set(int(x) for x in sel[b, g, :k])
         want = set(int(x) for x in r["sel"])
         if got - amb != want - amb:

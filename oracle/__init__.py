@@ -16,6 +16,7 @@ from .pagesparse_ref import (  # noqa: F401
     unit_page_meta,
     page_meta_pool,
     unit_scores,
+    score_magnitudes,
     FP8_E4M3,
     FP8_MAX,
     fp8_e4m3_value,

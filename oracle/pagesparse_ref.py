@@ -63,6 +63,11 @@ F32 = "f32"
 
 #: Relative band around the k-th selected score inside which the choice
 #: between pages is reported as ambiguous instead of being required to match.
+#: Relative to the score itself, or, when the page magnitudes are given
+#: (score_magnitudes), to the larger magnitude of the two pages compared: a
+#: sum of D terms rounded in fp32 is off by at most about D * 2^-24 times the
+#: sum of the terms' absolute values (the forward error bound of recursive
+#: summation), which is far above the result when the terms cancel.
 AMBIGUITY_REL = 1e-6
 
 
@@ -165,6 +170,15 @@ def unit_scores(q_group: np.ndarray, kmax: np.ndarray, kmin: np.ndarray):
     prod_max = q[:, None, :] * kmax[None, :, :]
     u = np.maximum(prod_min, prod_max).sum(axis=-1)  # [G, n]
     return u, u.max(axis=0)
+
+
+def score_magnitudes(q_group: np.ndarray, kmax: np.ndarray, kmin: np.ndarray) -> np.ndarray:
+    """Per page, the largest over the group's heads of the sum of the absolute
+    values of the D terms of U[h, p]: the scale of the rounding error of any
+    fp32 evaluation of the score (never below |S[p]|)."""
+    q = np.asarray(q_group, dtype=np.float64)
+    terms = np.maximum(q[:, None, :] * kmin[None, :, :], q[:, None, :] * kmax[None, :, :])
+    return np.abs(terms).sum(axis=-1).max(axis=0)
 
 
 # ---------------------------------------------------------------------------
@@ -287,8 +301,18 @@ def select_pages(scores: np.ndarray, n: int, budget: int, n_sink: int, n_local: 
     return sel, forced, taken
 
 
-def ambiguous_pages(scores, n, budget, n_sink, n_local, rel=AMBIGUITY_REL):
-    """Scored pages whose score lies within rel*|s_k| of the k-th taken score.
+def _band(s, k, mag, rel):
+    """Per page, the half-width of the band around page k's score: rel*|s_k|,
+    or rel*max(mag[p], mag[k]) with the page magnitudes."""
+    if mag is None:
+        return np.full(len(s), rel * abs(float(s[k])))
+    m = np.asarray(mag, dtype=np.float64)
+    return rel * np.maximum(m[:len(s)], m[k])
+
+
+def ambiguous_pages(scores, n, budget, n_sink, n_local, rel=AMBIGUITY_REL, mag=None):
+    """Scored pages whose score lies within the band (rel*|s_k|, or relative
+    to the page magnitudes mag when given) of the k-th taken score s_k.
 
     A page choice inside this set may legitimately differ between an fp32
     device and this fp64 reference. Returns (set, s_k or None).
@@ -297,9 +321,11 @@ def ambiguous_pages(scores, n, budget, n_sink, n_local, rel=AMBIGUITY_REL):
     if not taken:
         return set(), None
     s = np.asarray(scores, dtype=np.float64)
-    s_k = float(s[taken[-1]])
+    k = taken[-1]
+    s_k = float(s[k])
+    band = _band(s, k, mag, rel)
     fset = set(forced)
-    amb = {p for p in range(n) if p not in fset and abs(s[p] - s_k) <= rel * abs(s_k)}
+    amb = {p for p in range(n) if p not in fset and abs(s[p] - s_k) <= band[p]}
     return amb, s_k
 
 
@@ -360,10 +386,12 @@ def select_pages_topdelta(scores, n, budget, n_sink, n_local, scale, m_tilde, de
 
 
 def ambiguous_pages_topdelta(scores, n, budget, n_sink, n_local, scale, m_tilde, delta,
-                             rel=AMBIGUITY_REL):
+                             rel=AMBIGUITY_REL, mag=None):
     """Pages an fp32 device may decide differently: scaled scores within
-    rel of the threshold (it is itself an fp32 result on the device), and,
-    when the cap binds, scores within rel of the last taken one."""
+    rel of the threshold (it is itself an fp32 result on the device; with the
+    page magnitudes mag, within rel times the larger of |tau|, 1 and the
+    page's scaled magnitude), and, when the cap binds, scores within the band
+    of ambiguous_pages around the last taken one."""
     sel, forced, taken, tau = select_pages_topdelta(scores, n, budget, n_sink, n_local, scale,
                                                     m_tilde, delta)
     if tau is None:
@@ -372,12 +400,14 @@ def ambiguous_pages_topdelta(scores, n, budget, n_sink, n_local, scale, m_tilde,
     fset = set(forced)
     amb = set()
     if math.isfinite(tau):
+        m = np.zeros(n) if mag is None else float(scale) * np.asarray(mag, dtype=np.float64)
         amb |= {p for p in range(n) if p not in fset and
-                abs(float(scale) * s[p] - tau) <= rel * max(abs(tau), 1.0)}
+                abs(float(scale) * s[p] - tau) <= rel * max(abs(tau), 1.0, m[p])}
     r = budget - len(forced)
     if taken and len(taken) == r:
-        s_k = float(s[taken[-1]])
-        amb |= {p for p in range(n) if p not in fset and abs(s[p] - s_k) <= rel * abs(s_k)}
+        k = taken[-1]
+        band = _band(s, k, mag, rel)
+        amb |= {p for p in range(n) if p not in fset and abs(s[p] - s[k]) <= band[p]}
     return amb
 
 
@@ -479,7 +509,8 @@ def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None, delta=None)
     (FP8_E4M3: pages are scored on the 8-bit bounds).
     sel_override: attend over this page list instead of the selected one.
     delta: select by the top-delta criterion with this delta (None: top-k).
-    Returns a dict with u, scores, sel, forced, taken, out [G,D], lse [G].
+    Returns a dict with u, scores, mag (score_magnitudes), sel, forced, taken,
+    out [G,D], lse [G].
     """
     q = inp["q"]
     hq, hkv = q.shape[1], inp["k_pool"].shape[1]
@@ -493,6 +524,7 @@ def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None, delta=None)
         kmax, kmin = widen_fp8(cmax), widen_fp8(cmin)
     qg = q[b, g * grp:(g + 1) * grp].astype(np.float64)
     u, s = unit_scores(qg, kmax, kmin)
+    mag = score_magnitudes(qg, kmax, kmin)
     tau = None
     if delta is None:
         sel, forced, taken = select_pages(s, n, budget, n_sink, n_local)
@@ -515,7 +547,7 @@ def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None, delta=None)
         o, l = attend(qg[i], keys, vals, inp["scale"], sk)
         outs.append(o)
         lses.append(l)
-    return {"u": u, "scores": s, "sel": sel, "forced": forced, "taken": taken,
+    return {"u": u, "scores": s, "mag": mag, "sel": sel, "forced": forced, "taken": taken,
             "out": np.stack(outs), "lse": np.array(lses), "n": n, "tau": tau}
 
 

@@ -79,7 +79,7 @@ def test_scores_match_fp64(cases, w):
     for (b, g), hu in hosts.items():
         r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local)
         worst = max(worst, score_rel_err(res["scores"][b, g, :r["n"]].astype(np.float64),
-                                         r["scores"]))
+                                         r["scores"], mag=r["mag"]))
     print(f"{w.name}: max score rel err {worst:.3e}")
     assert worst <= SCORE_REL
 
@@ -91,7 +91,7 @@ def test_selection_and_outputs(cases, w):
     for (b, g), hu in hosts.items():
         r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local)
         check_selection(res["sel"][b, g], res["sel_count"][b, g], r["scores"], r["n"],
-                        w.budget_pages, w.n_sink, w.n_local)
+                        w.budget_pages, w.n_sink, w.n_local, mag=r["mag"])
         k = int(res["sel_count"][b, g])
         e, _ = check_unit_outputs(res, hu, b, g, w, w.budget_pages, w.n_sink, w.n_local,
                                   sel_dev=res["sel"][b, g, :k])

@@ -80,7 +80,7 @@ def test_scores_match_fp64(cases, w):
         r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local)
         n = r["n"]
         worst = max(worst, score_rel_err(res["scores"][b, g, :n].astype(np.float64),
-                                         r["scores"]))
+                                         r["scores"], mag=r["mag"]))
     print(f"{w.name}: max score rel err {worst:.3e}")
     assert worst <= SCORE_REL
 
@@ -92,7 +92,7 @@ def test_selection_end_to_end(cases, w):
     for (b, g), hu in hosts.items():
         r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local)
         a, _ = check_selection(res["sel"][b, g], res["sel_count"][b, g], r["scores"], r["n"],
-                               w.budget_pages, w.n_sink, w.n_local)
+                               w.budget_pages, w.n_sink, w.n_local, mag=r["mag"])
         n_amb += a
     print(f"{w.name}: ambiguous pages {n_amb}")
 
@@ -283,7 +283,7 @@ def test_select_large_candidate_count():
     r = ref.unit_step(hu, 0, 0, w.budget_pages, w.n_sink, w.n_local)
     assert r["n"] > 16384 + 4
     check_selection(res["sel"][0, 0], res["sel_count"][0, 0], r["scores"], r["n"],
-                    w.budget_pages, w.n_sink, w.n_local)
+                    w.budget_pages, w.n_sink, w.n_local, mag=r["mag"])
     k = int(res["sel_count"][0, 0])
     check_unit_outputs(res, hu, 0, 0, w, w.budget_pages, w.n_sink, w.n_local,
                        sel_dev=res["sel"][0, 0, :k])

@@ -172,6 +172,79 @@ def test_ambiguity_band():
     assert amb == {1}
 
 
+def test_score_magnitudes_hand_example():
+    """Two heads, two coordinates, one page: kmax = (2, 3), kmin = (1, 2).
+    Head 0, q = (1, -1): terms max(1, 2) = 2 and max(-2, -3) = -2, so the
+    bound is 0 and the magnitude 4. Head 1, q = (0.5, 0.5): terms 1 and 1.5,
+    bound 2.5, magnitude 2.5. The group takes the larger of each: score 2.5,
+    magnitude 4 (from the head whose terms cancel)."""
+    q = np.array([[1.0, -1.0], [0.5, 0.5]])
+    kmax = np.array([[2.0, 3.0]])
+    kmin = np.array([[1.0, 2.0]])
+    u, s = ref.unit_scores(q, kmax, kmin)
+    assert u.tolist() == [[0.0], [2.5]] and s.tolist() == [2.5]
+    assert ref.score_magnitudes(q, kmax, kmin).tolist() == [4.0]
+
+
+def test_score_magnitudes_without_cancellation_equal_the_score():
+    """With q >= 0 and kmin >= 0 every term is non-negative, so the magnitude
+    is the score itself; in general it is at least |score| (triangle
+    inequality) for every page."""
+    rng = np.random.default_rng(3)
+    q = np.abs(rng.standard_normal((3, 64)))
+    lo = np.abs(rng.standard_normal((20, 64)))
+    hi = lo + np.abs(rng.standard_normal((20, 64)))
+    _, s = ref.unit_scores(q, hi, lo)
+    np.testing.assert_allclose(ref.score_magnitudes(q, hi, lo), s, rtol=1e-15)
+    q = rng.standard_normal((4, 128))
+    lo = rng.standard_normal((50, 128))
+    hi = lo + np.abs(rng.standard_normal((50, 128)))
+    _, s = ref.unit_scores(q, hi, lo)
+    assert np.all(ref.score_magnitudes(q, hi, lo) >= np.abs(s) * (1 - 1e-15))
+
+
+def test_fp32_score_error_is_bounded_by_the_magnitude():
+    """A left-to-right fp32 sum of the D exact terms stays within
+    D * 2^-24 * magnitude of the fp64 score (the forward error bound of
+    recursive summation) on pages whose terms cancel almost completely, while
+    its error relative to the score itself is far larger there."""
+    rng = np.random.default_rng(4)
+    d = 128
+    centre = rng.standard_normal((200, d)) * 2.5
+    lo = (centre - 0.05).astype(np.float32).astype(np.float64)
+    hi = (centre + 0.05).astype(np.float32).astype(np.float64)
+    q = rng.standard_normal((1, d)).astype(np.float32).astype(np.float64)
+    _, s = ref.unit_scores(q, hi, lo)
+    mag = ref.score_magnitudes(q, hi, lo)
+    terms = np.maximum(q * lo, q * hi).astype(np.float32)
+    acc = np.zeros(len(s), dtype=np.float32)
+    for j in range(d):
+        acc = (acc + terms[:, j]).astype(np.float32)
+    err = np.abs(acc.astype(np.float64) - s)
+    assert np.all(err <= d * 2.0 ** -24 * mag)
+    assert np.max(err / np.abs(s)) > 10 * np.max(err / mag)
+
+
+def test_ambiguity_band_with_magnitudes():
+    """Scores near zero with large magnitudes: the band is relative to the
+    larger magnitude of the two pages, not to the k-th score."""
+    s = np.array([10.0, 9.0, 1e-4, 0.0, -5.0])
+    mag = np.array([10.0, 9.0, 200.0, 200.0, 5.0])
+    amb, s_k = ref.ambiguous_pages(s, 5, 3, 0, 0)
+    assert s_k == 1e-4 and amb == {2}
+    amb, _ = ref.ambiguous_pages(s, 5, 3, 0, 0, mag=mag)
+    assert amb == {2, 3}  # |0 - 1e-4| <= 1e-6 * 200
+    amb, _ = ref.ambiguous_pages(s, 5, 3, 0, 0, rel=1e-7, mag=mag)
+    assert amb == {2}
+    # threshold band of the top-delta rule: scaled score 1e-4 against tau = 0
+    # is decided either way only with the magnitude
+    m = np.array([0.0])
+    amb = ref.ambiguous_pages_topdelta(s, 5, 4, 1, 0, 1.0, m, 0.0)
+    assert 2 not in amb
+    amb = ref.ambiguous_pages_topdelta(s, 5, 4, 1, 0, 1.0, m, 0.0, mag=mag)
+    assert 2 in amb and 3 in amb and 4 not in amb
+
+
 def test_dense_is_exact_attention(small, tiny):
     check_dense_is_exact_attention(ref, small[2])
     check_dense_is_exact_attention(ref, tiny[1])
