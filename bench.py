@@ -506,7 +506,7 @@ def main():
         ps.ps_refresh_score_pages(s["g"], inp["q"], inp["k_pool"], s["meta"], inp["page_table"],
                                   inp["seq_lens"], step.scores)
 
-    def k_select_decode(s):
+    def k_select_decode(s, merge=True):
         inp, step = s["inp"], s["step"]
         acc_t, ml_t = step.partials(step.n_splits)
         if step.n_splits == 1:  # the merge is in the same launch
@@ -515,6 +515,13 @@ def main():
                                        step.budget, step.n_sink, step.n_local, step.scale, 1,
                                        step.sel, step.sel_count, None, None, inp["sink"],
                                        step.out, step.lse)
+        elif merge and step.merge_in_launch:  # the last split of each unit merges
+            ps.ps_select_sparse_decode(s["g"], inp["q"], inp["k_pool"], inp["v_pool"],
+                                       inp["page_table"], inp["seq_lens"], step.scores,
+                                       step.budget, step.n_sink, step.n_local, step.scale,
+                                       step.n_splits, step.sel, step.sel_count, acc_t, ml_t,
+                                       inp["sink"], step.out, step.lse,
+                                       arrivals=step.arrivals)
         else:
             ps.ps_select_sparse_decode(s["g"], inp["q"], inp["k_pool"], inp["v_pool"],
                                        inp["page_table"], inp["seq_lens"], step.scores,
@@ -553,6 +560,9 @@ def main():
     kern_us["refresh_score"] = time_launches(k_refresh_score)  # the step's own launches
     if fused:
         kern_us["select_decode"] = time_launches(k_select_decode)
+        if s0["step"].merge_in_launch and s0["step"].n_splits > 1:
+            kern_us["select_decode_partials_only"] = time_launches(
+                lambda s: k_select_decode(s, merge=False))
     kern_us["combine"] = time_launches(k_combine)
     # the unfused entry points, one stage each
     kern_us["tail_meta"] = time_launches(k_tail_meta)
@@ -661,8 +671,9 @@ def main():
         "kernels_us": {k: round(v, 3) for k, v in kern_us.items()},
         "step_launches": step_launches(s0["step"]),
         "selection_overhead_us": round(kern_us["select"], 3),
-        "selection_in_decode_us": (round(kern_us["select_decode"] - kern_us["sparse_decode"], 3)
-                                   if fused else None),
+        "selection_in_decode_us": (round(kern_us.get("select_decode_partials_only",
+                                                     kern_us["select_decode"])
+                                         - kern_us["sparse_decode"], 3) if fused else None),
         "score_plus_select_us": round(kern_us["score"] + kern_us["select"], 3),
         "sparse_decode_gbps": round(decode_gbps, 1),
         "dense_us_per_step": round(dense_us, 3),
@@ -711,7 +722,8 @@ def step_launches(step):
     if step.fused:
         fused = ("ps_select_sparse_decode" if step.delta is None
                  else "ps_select_topdelta_sparse_decode")
-        return ["ps_refresh_score_pages", fused] + ([] if step.n_splits == 1 else ["ps_combine"])
+        merged = step.n_splits == 1 or step.merge_in_launch
+        return ["ps_refresh_score_pages", fused] + ([] if merged else ["ps_combine"])
     return ["ps_refresh_score_pages", sel, "ps_sparse_decode", "ps_combine"]
 
 

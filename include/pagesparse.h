@@ -247,29 +247,37 @@ int ps_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool, co
  * Every split's workgroup selects the (b, g) page list from scores itself
  * and attends the list slots of its split, so no page list is read back.
  * sel and sel_count, when not NULL, receive what ps_select_topk writes.
- * With out != NULL (one split only) the single partial is merged in the same
- * launch: out and lse (when not NULL) receive what ps_combine writes for
- * n_splits = 1 with the given sink (NULL = none), bitwise; part_acc and
- * part_ml are then not used (may be NULL). Otherwise the partials are
- * written as by ps_sparse_decode and sink and lse must be NULL.
+ * The partials are written as by ps_sparse_decode. With out != NULL the
+ * merge happens in the same launch: out and lse (when not NULL) receive what
+ * ps_combine writes for these partials with the given sink (NULL = none),
+ * bitwise. With one split the single partial is merged directly (part_acc
+ * and part_ml are then not used and may be NULL). With more splits,
+ * arrivals [B, Hkv] int32 counts the splits of each (b, g) that have
+ * written their partials, and the last one to finish merges them ("Attention:
+ * Undivided & Uncompressed", section "Traffic": the split-KV merge; here it
+ * saves the merge launch). arrivals is device memory owned by the caller:
+ * all zero when the launch starts, all zero again when it ends (allocate it
+ * zeroed once and reuse it; launches that overlap in time must not share
+ * it). Without out, sink, lse and arrivals must be NULL.
  * Host checks: those of ps_select_topk and ps_sparse_decode (same codes);
- * sel and sel_count both NULL or both set, and the partials set when out is
- * NULL (else PS_ERR_NULL); out != NULL with n_splits != 1, or sink or lse
- * set without out (PS_ERR_BUDGET); max_pages <= 8192 and
- * ceil(budget_pages / n_splits) <= 512 (else PS_ERR_UNSUPPORTED).
- * Device precondition: scores are finite (no NaN). */
+ * sel and sel_count both NULL or both set, and the partials set unless out
+ * is set with one split (else PS_ERR_NULL); out != NULL with n_splits != 1
+ * and no arrivals, or sink, lse or arrivals set without out (PS_ERR_BUDGET);
+ * max_pages <= 8192 and ceil(budget_pages / n_splits) <= 512 (else
+ * PS_ERR_UNSUPPORTED).
+ * Device preconditions: scores are finite (no NaN); arrivals as above. */
 int ps_select_sparse_decode(const ps_geom* geom, const float* q, const void* k_pool,
                             const void* v_pool, const int32_t* page_table,
                             const int32_t* seq_lens, const float* scores, int32_t budget_pages,
                             int32_t n_sink_pages, int32_t n_local_pages, float scale,
                             int32_t n_splits, int32_t* sel, int32_t* sel_count, float* part_acc,
                             float* part_ml, const float* sink, float* out, float* lse,
-                            void* stream);
+                            int32_t* arrivals, void* stream);
 
 /* 3'+4a. Top-delta selection fused into the sparse decode: one launch does
  * the work of ps_select_topdelta followed by ps_sparse_decode, with bitwise
  * the same page list and partials (and, with out, the merge of ps_combine as
- * in ps_select_sparse_decode). ("Faster Than Flash: Exploiting Attention
+ * in ps_select_sparse_decode, with arrivals as there). ("Faster Than Flash: Exploiting Attention
  * Sparsity for Efficient Long-Context Decoding", section "Methodology", item
  * 2; "Training-free sparse attention for long-context LLM decode", section
  * "Reusable code": a fused single-launch variant of the sparse decode.)
@@ -286,7 +294,7 @@ int ps_select_topdelta_sparse_decode(const ps_geom* geom, const float* q, const 
                                      int32_t n_local_pages, float scale, float delta,
                                      int32_t n_splits, int32_t* sel, int32_t* sel_count,
                                      float* part_acc, float* part_ml, const float* sink,
-                                     float* out, float* lse, void* stream);
+                                     float* out, float* lse, int32_t* arrivals, void* stream);
 
 /* 4b. Dense split-KV decode: ps_sparse_decode over every page. Split s of a
  * request covers logical pages [s*c_b, min((s+1)*c_b, n_b)) with

@@ -80,9 +80,9 @@ _SIGS = {
     "ps_select_topdelta": [_G, _P, _P, _P, _P, _P, _I, _I, _I, _F, _F, _P, _P, _P],
     "ps_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _P, _I, _F, _I, _P, _P, _P],
     "ps_select_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P, _P, _P,
-                                _P, _P, _P, _P, _P],
+                                _P, _P, _P, _P, _P, _P],
     "ps_select_topdelta_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _F, _I,
-                                         _P, _P, _P, _P, _P, _P, _P, _P],
+                                         _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "ps_full_decode": [_G, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P],
     "ps_combine": [_G, _P, _P, _I, _P, _P, _P, _P],
     "ps_strerror": [ctypes.c_int],

@@ -184,16 +184,16 @@ static int check_select_decode(const ps_geom* geom, ps::Shape* s, const float* q
                                int32_t n_local_pages, int32_t n_splits, const int32_t* sel,
                                const int32_t* sel_count, const float* part_acc,
                                const float* part_ml, const float* sink, const float* out,
-                               const float* lse) {
+                               const float* lse, const int32_t* arrivals) {
   int rc = check_geom(geom, s);
   if (rc) return rc;
   if (!q || !k_pool || !v_pool || !page_table || !seq_lens || !scores) return PS_ERR_NULL;
   if ((sel == nullptr) != (sel_count == nullptr)) return PS_ERR_NULL;
-  if (!out && (!part_acc || !part_ml)) return PS_ERR_NULL;
+  if ((!out || n_splits > 1) && (!part_acc || !part_ml)) return PS_ERR_NULL;
   if (budget_pages < 1 || n_sink_pages < 0 || n_local_pages < 0) return PS_ERR_BUDGET;
   if ((int64_t)n_sink_pages + n_local_pages > budget_pages) return PS_ERR_BUDGET;
   if (n_splits < 1 || n_splits > budget_pages || n_splits > kMaxSplits) return PS_ERR_BUDGET;
-  if (out ? n_splits != 1 : (sink || lse)) return PS_ERR_BUDGET;
+  if (out ? (n_splits != 1 && !arrivals) : (sink || lse || arrivals)) return PS_ERR_BUDGET;
   if (s->max_pages > ps::kSelectDecodeMaxPages ||
       (budget_pages + n_splits - 1) / n_splits > ps::kMaxSplitPages)
     return PS_ERR_UNSUPPORTED;
@@ -209,17 +209,17 @@ PS_API int ps_select_sparse_decode(const ps_geom* geom, const float* q, const vo
                                    int32_t n_local_pages, float scale, int32_t n_splits,
                                    int32_t* sel, int32_t* sel_count, float* part_acc,
                                    float* part_ml, const float* sink, float* out, float* lse,
-                                   void* stream) {
+                                   int32_t* arrivals, void* stream) {
   ps::Shape s;
   const int rc = check_select_decode(geom, &s, q, k_pool, v_pool, page_table, seq_lens, scores,
                                      budget_pages, n_sink_pages, n_local_pages, n_splits, sel,
-                                     sel_count, part_acc, part_ml, sink, out, lse);
+                                     sel_count, part_acc, part_ml, sink, out, lse, arrivals);
   if (rc) return rc;
   if (s.batch == 0) return PS_OK;
   return hip_status(ps::launch_select_decode(s, q, k_pool, v_pool, page_table, seq_lens, scores,
                                              budget_pages, n_sink_pages, n_local_pages, scale,
                                              n_splits, sel, sel_count, part_acc, part_ml, sink,
-                                             out, lse, (hipStream_t)stream));
+                                             out, lse, arrivals, (hipStream_t)stream));
 }
 
 PS_API int ps_select_topdelta_sparse_decode(const ps_geom* geom, const float* q,
@@ -230,18 +230,18 @@ PS_API int ps_select_topdelta_sparse_decode(const ps_geom* geom, const float* q,
                                             float scale, float delta, int32_t n_splits,
                                             int32_t* sel, int32_t* sel_count, float* part_acc,
                                             float* part_ml, const float* sink, float* out,
-                                            float* lse, void* stream) {
+                                            float* lse, int32_t* arrivals, void* stream) {
   ps::Shape s;
   const int rc = check_select_decode(geom, &s, q, k_pool, v_pool, page_table, seq_lens, scores,
                                      budget_pages, n_sink_pages, n_local_pages, n_splits, sel,
-                                     sel_count, part_acc, part_ml, sink, out, lse);
+                                     sel_count, part_acc, part_ml, sink, out, lse, arrivals);
   if (rc) return rc;
   if (!(delta >= 0.0f) || !(scale > 0.0f) || !(scale < INFINITY)) return PS_ERR_BUDGET;
   if (s.batch == 0) return PS_OK;
   return hip_status(ps::launch_select_topdelta_decode(
       s, q, k_pool, v_pool, page_table, seq_lens, scores, budget_pages, n_sink_pages,
       n_local_pages, scale, delta, n_splits, sel, sel_count, part_acc, part_ml, sink, out, lse,
-      (hipStream_t)stream));
+      arrivals, (hipStream_t)stream));
 }
 
 PS_API int ps_full_decode(const ps_geom* geom, const float* q, const void* k_pool,
@@ -289,4 +289,4 @@ PS_API const char* ps_strerror(int status) {
   }
 }
 
-PS_API int ps_abi_version(void) { return (1 << 16) | 5; }  // 1.5: top-delta selecting decode
+PS_API int ps_abi_version(void) { return (1 << 16) | 6; }  // 1.6: in-launch merge of several splits

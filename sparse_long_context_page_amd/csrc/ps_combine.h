@@ -22,17 +22,30 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return v;
 }
 
+// A partial's value; COHERENT: an agent-scope load, which reads past any
+// chiplet cache (partials written by workgroups of the same launch).
+template <bool COHERENT>
+__device__ __forceinline__ float load_partial(const float* p) {
+  if constexpr (COHERENT)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
 // Lanes stride over the splits for the max and the normaliser (wave
 // reductions); each lane computes the weight of one split, and the weighted
 // sum of accumulators runs over the head dimension with the weights
 // broadcast by shuffles, splits in order. ml = [n_splits, 2] (max in natural
 // log units, normaliser), acc = [n_splits, d_], sig = the sink logit or -inf.
+// COHERENT selects the loads only; the arithmetic is the same.
+template <bool COHERENT = false>
 __device__ __forceinline__ void combine_row(const float* __restrict__ acc,
                                             const float* __restrict__ ml, int n_splits, int d_,
                                             float sig, float* __restrict__ o, float* lse_out) {
+  auto ld = [](const float* p) { return load_partial<COHERENT>(p); };
   const int lane = threadIdx.x % kWave;
   float mx = -INFINITY;
-  for (int s = lane; s < n_splits; s += kWave) mx = fmax_(mx, ml[2 * s]);
+  for (int s = lane; s < n_splits; s += kWave) mx = fmax_(mx, ld(ml + 2 * s));
   mx = fmax_(wave_max_f32(mx), sig);
   if (mx == -INFINITY) {
     for (int d = lane; d < d_; d += kWave) o[d] = 0.0f;
@@ -41,8 +54,8 @@ __device__ __forceinline__ void combine_row(const float* __restrict__ acc,
   }
   float l = 0.0f;
   for (int s = lane; s < n_splits; s += kWave) {
-    const float ms = ml[2 * s];
-    if (ms != -INFINITY) l = __builtin_fmaf(expf(ms - mx), ml[2 * s + 1], l);
+    const float ms = ld(ml + 2 * s);
+    if (ms != -INFINITY) l = __builtin_fmaf(expf(ms - mx), ld(ml + 2 * s + 1), l);
   }
   l = wave_sum_f32(l);
   if (sig != -INFINITY) l += expf(sig - mx);
@@ -57,7 +70,7 @@ __device__ __forceinline__ void combine_row(const float* __restrict__ acc,
     const int sl = s0 + lane;
     float w = 0.0f;
     if (sl < n_splits) {
-      const float ms = ml[2 * sl];
+      const float ms = ld(ml + 2 * sl);
       w = ms == -INFINITY ? 0.0f : expf(ms - mx);
     }
     const int cnt = min(kWave, n_splits - s0);
@@ -69,7 +82,7 @@ __device__ __forceinline__ void combine_row(const float* __restrict__ acc,
 #pragma unroll
         for (int k = 0; k < kDPerLane; ++k) {
           const int d = lane + k * kWave;
-          v[j][k] = (j0 + j < cnt && d < d_) ? src[d] : 0.0f;
+          v[j][k] = (j0 + j < cnt && d < d_) ? ld(src + d) : 0.0f;
         }
       }
 #pragma unroll

@@ -22,6 +22,7 @@
 // written as fp32 partials (max in natural-log units).
 #pragma once
 
+#include "ps_combine.h"
 #include "ps_device.h"
 #include "ps_launch.h"
 #include "ps_select.h"
@@ -127,16 +128,18 @@ __device__ __forceinline__ void merge_weights(float m1, float m2, float& mo, flo
 enum DecodeMode : int { kDense = 0, kList = 1, kSelect = 2, kSelectDelta = 3 };
 
 // Selection inputs and outputs of the selecting modes, and the merged output
-// of a launch with one split.
+// (with one split, or with more and the arrival counters).
 struct SelectArgs {
   const float* scores;  // [B, Hkv, max_pages]
   int n_sink, n_local;
   int32_t* sel;        // [B, Hkv, budget] or null
   int32_t* sel_count;  // [B, Hkv] or null
   const float* sink;   // [Hq] or null; with out
-  float* out;          // [B, Hq, D] or null: one split, merged output written
+  float* out;          // [B, Hq, D] or null: merged output written
   float* lse;          // [B, Hq] or null
   float scale, delta;  // kSelectDelta: the softmax scale and delta
+  int32_t* arrivals;   // [B, Hkv], all zero, or null: with out and more than one
+                       // split, the last split of a unit to finish merges
 };
 
 // The selection of a selecting workgroup (W wavefronts): every split of a
@@ -199,6 +202,48 @@ __device__ __forceinline__ void write_merged(const SelectArgs& sa, int64_t row, 
   const float wgt = m_nat == -INFINITY ? 0.0f : expf(m_nat - mx);
   sa.out[row * dim + d] = __builtin_fmaf(wgt, a, 0.0f) * inv;
   if (sa.lse && d == 0) sa.lse[row] = mx + logf(l);
+}
+
+// More than one split and a merged output: after writing its partials a
+// split counts itself in at its (request, KV head), and the split that
+// arrives last merges every split's partials of the group's query heads with
+// the merge kernel's row merge (so bitwise as ps_combine), then re-arms the
+// counter to zero for the next launch. No workgroup waits for another.
+// An agent-scope fence writes back or invalidates a whole chiplet cache, so
+// none is used: the partials are written with agent-scope stores (through
+// the chiplet cache), every wavefront waits until its stores are
+// acknowledged before the count is taken, and the merging workgroup reads
+// the partials with agent-scope loads (past the chiplet cache). These are
+// the instructions of the agent-scope release and acquire without their
+// whole-cache write-back and invalidation, which only ordinary stores and
+// loads need.
+__device__ __forceinline__ void store_partial(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int W, int G>
+__device__ __forceinline__ void merge_if_last(const SelectArgs& sa, int b, int g, int hkv,
+                                              int unit, int n_splits, int dim,
+                                              const float* part_acc, const float* part_ml) {
+  __shared__ int last;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(sa.arrivals + unit, 1, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+    last = prev == n_splits - 1;
+    if (last) __hip_atomic_store(sa.arrivals + unit, 0, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  const int hq = hkv * G;
+  for (int h = (int)(threadIdx.x / kWave); h < G; h += W) {
+    const int64_t row = (int64_t)b * hq + g * G + h;
+    combine_row<true>(part_acc + row * n_splits * dim, part_ml + row * n_splits * 2, n_splits,
+                      dim, sa.sink ? sa.sink[g * G + h] : -INFINITY, sa.out + row * dim,
+                      sa.lse ? sa.lse + row : nullptr);
+  }
 }
 
 template <typename T, int D, int G, int MODE, int C>
@@ -365,16 +410,28 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(
       lsum = __builtin_fmaf(wt, sm_l[w][h], lsum);
     }
     const float m_nat = mo == -INFINITY ? -INFINITY : mo * kLn2;
-    if (SEL && sa.out) {
+    if (SEL && sa.out && n_splits == 1) {
       write_merged(sa, (int64_t)b * hq + g * G + h, g * G + h, d, D, m_nat, lsum, a);
       continue;
     }
     const int64_t ph = ((int64_t)b * hq + g * G + h) * n_splits + split;
+    if (SEL && sa.out) {  // merged in this launch: through the chiplet cache
+      store_partial(part_acc + ph * D + d, a);
+      if (d == 0) {
+        store_partial(part_ml + ph * 2 + 0, m_nat);
+        store_partial(part_ml + ph * 2 + 1, lsum);
+      }
+      continue;
+    }
     part_acc[ph * D + d] = a;
     if (d == 0) {
       part_ml[ph * 2 + 0] = m_nat;
       part_ml[ph * 2 + 1] = lsum;
     }
+  }
+  if constexpr (SEL) {
+    if (sa.out && n_splits > 1)
+      merge_if_last<kDecWaves, G>(sa, b, g, hkv, unit, n_splits, D, part_acc, part_ml);
   }
 }
 
@@ -702,16 +759,28 @@ void decode_mfma_kernel(
       lsum = __builtin_fmaf(wt, sm_l[w][h], lsum);
     }
     const float m_nat = mo == -INFINITY ? -INFINITY : mo * kLn2;
-    if (sa.out) {
+    if (sa.out && n_splits == 1) {
       write_merged(sa, (int64_t)b * hq + g * G + h, g * G + h, d, D, m_nat, lsum, a);
       continue;
     }
     const int64_t ph = ((int64_t)b * hq + g * G + h) * n_splits + split;
+    if (SEL && sa.out) {  // merged in this launch: through the chiplet cache
+      store_partial(part_acc + ph * D + d, a);
+      if (d == 0) {
+        store_partial(part_ml + ph * 2 + 0, m_nat);
+        store_partial(part_ml + ph * 2 + 1, lsum);
+      }
+      continue;
+    }
     part_acc[ph * D + d] = a;
     if (d == 0) {
       part_ml[ph * 2 + 0] = m_nat;
       part_ml[ph * 2 + 1] = lsum;
     }
+  }
+  if constexpr (SEL) {
+    if (sa.out && n_splits > 1)
+      merge_if_last<W, G>(sa, b, g, hkv, unit, n_splits, D, part_acc, part_ml);
   }
 }
 
@@ -726,7 +795,8 @@ hipError_t launch_selecting_decode(const Shape& s, const float* q, const void* k
   const int64_t blocks = (int64_t)s.batch * s.hkv * n_splits;
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (s.max_pages > kSelectDecodeMaxPages ||
-      (budget + n_splits - 1) / n_splits > kMaxSplitPages || (sa.out && n_splits != 1))
+      (budget + n_splits - 1) / n_splits > kMaxSplitPages ||
+      (sa.out && n_splits != 1 && !sa.arrivals))
     return hipErrorInvalidValue;
   const float qscale = scale * 1.44269504088896340736f;  // log2(e)
   if (!s.kv_bf16) {  // fp32 K/V: the vector-ALU decode, 4 wavefronts

@@ -47,7 +47,8 @@ hipError_t launch_select_decode(const Shape& s, const float* q, const void* k_po
                                 const int32_t* seq_lens, const float* scores, int budget,
                                 int n_sink, int n_local, float scale, int n_splits, int32_t* sel,
                                 int32_t* sel_count, float* part_acc, float* part_ml,
-                                const float* sink, float* out, float* lse, hipStream_t st);
+                                const float* sink, float* out, float* lse, int32_t* arrivals,
+                                hipStream_t st);
 
 hipError_t launch_select_topdelta_decode(const Shape& s, const float* q, const void* k_pool,
                                          const void* v_pool, const int32_t* page_table,
@@ -56,7 +57,7 @@ hipError_t launch_select_topdelta_decode(const Shape& s, const float* q, const v
                                          float delta, int n_splits, int32_t* sel,
                                          int32_t* sel_count, float* part_acc, float* part_ml,
                                          const float* sink, float* out, float* lse,
-                                         hipStream_t st);
+                                         int32_t* arrivals, hipStream_t st);
 
 hipError_t launch_decode(const Shape& s, bool sparse, const float* q, const void* k_pool,
                          const void* v_pool, const int32_t* page_table, const int32_t* seq_lens,

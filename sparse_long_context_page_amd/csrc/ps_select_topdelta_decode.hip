@@ -11,9 +11,10 @@ hipError_t launch_select_topdelta_decode(const Shape& s, const float* q, const v
                                          float delta, int n_splits, int32_t* sel,
                                          int32_t* sel_count, float* part_acc, float* part_ml,
                                          const float* sink, float* out, float* lse,
-                                         hipStream_t st) {
+                                         int32_t* arrivals, hipStream_t st) {
   if (s.group > 8) return hipErrorInvalidValue;
-  const SelectArgs sa{scores, n_sink, n_local, sel, sel_count, sink, out, lse, scale, delta};
+  const SelectArgs sa{scores, n_sink, n_local, sel, sel_count, sink, out, lse, scale, delta,
+                      arrivals};
   return launch_selecting_decode<kSelectDelta>(s, q, k_pool, v_pool, page_table, seq_lens,
                                                budget, scale, n_splits, part_acc, part_ml, sa,
                                                st);

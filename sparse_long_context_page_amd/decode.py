@@ -25,7 +25,8 @@ from .ops import Geometry
 class DecodeStep:
     def __init__(self, geom: Geometry, budget_pages: int, n_sink: int = 0, n_local: int = 0,
                  n_splits: int = 8, dense_splits: int = 32, scale: Optional[float] = None,
-                 device="cuda", fused: bool = True, delta: Optional[float] = None):
+                 device="cuda", fused: bool = True, delta: Optional[float] = None,
+                 merge_in_launch: bool = True):
         self.g = geom
         self.budget = int(budget_pages)
         self.n_sink = int(n_sink)
@@ -39,6 +40,12 @@ class DecodeStep:
         # launch) when supported
         self.fused = (bool(fused) and
                       ops.select_decode_supported(geom, self.budget, self.n_splits))
+        # with several splits, the fused launch also merges them (the last
+        # split of each (request, KV head) to finish), counting arrivals in a
+        # zeroed [B, Hkv] buffer that every launch leaves zeroed
+        self.merge_in_launch = self.fused and bool(merge_in_launch)
+        self.arrivals = (torch.zeros((geom.batch, geom.num_kv_heads), device=device,
+                                     dtype=torch.int32) if self.merge_in_launch else None)
         b, hq, hkv, d = geom.batch, geom.num_q_heads, geom.num_kv_heads, geom.head_dim
         f32 = dict(device=device, dtype=torch.float32)
         self.scores = torch.empty((b, hkv, geom.max_pages), **f32)
@@ -88,6 +95,10 @@ class DecodeStep:
             if self.n_splits == 1:  # select, decode and merge in one launch
                 fn(*head, 1, self.sel, self.sel_count, None, None, sink, self.out, self.lse,
                    stream)
+                return self.out, self.lse
+            if self.merge_in_launch:  # the last split to finish merges
+                fn(*head, self.n_splits, self.sel, self.sel_count, acc, ml, sink, self.out,
+                   self.lse, stream, arrivals=self.arrivals)
                 return self.out, self.lse
             fn(*head, self.n_splits, self.sel, self.sel_count, acc, ml, stream=stream)
         else:

@@ -207,7 +207,7 @@ def _select_decode_args(g: Geometry, q, k_pool, v_pool, page_table, seq_lens, sc
 
 
 def _select_decode_outputs(g: Geometry, budget_pages: int, ns: int, sel, sel_count, part_acc,
-                           part_ml, sink, out, lse, stream):
+                           part_ml, sink, out, lse, arrivals, stream):
     return (_ptr(sel, "sel", torch.int32, (g.batch, g.num_kv_heads, budget_pages),
                  optional=True),
             _ptr(sel_count, "sel_count", torch.int32, (g.batch, g.num_kv_heads), optional=True),
@@ -218,22 +218,24 @@ def _select_decode_outputs(g: Geometry, budget_pages: int, ns: int, sel, sel_cou
             _ptr(sink, "sink", torch.float32, (g.num_q_heads,), optional=True),
             _ptr(out, "out", torch.float32, (g.batch, g.num_q_heads, g.head_dim), optional=True),
             _ptr(lse, "lse", torch.float32, (g.batch, g.num_q_heads), optional=True),
+            _ptr(arrivals, "arrivals", torch.int32, (g.batch, g.num_kv_heads), optional=True),
             _stream(stream))
 
 
 def ps_select_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens, scores,
                             budget_pages: int, n_sink: int, n_local: int, scale: float,
                             n_splits: int, sel, sel_count, part_acc, part_ml, sink=None,
-                            out=None, lse=None, stream=None) -> None:
+                            out=None, lse=None, stream=None, arrivals=None) -> None:
     """ps_select_topk and ps_sparse_decode in one launch (sel and sel_count
-    may both be None); with out (one split) also the merge of ps_combine."""
+    may both be None); with out also the merge of ps_combine (with more than
+    one split: arrivals, [B, Hkv] int32 on the device, zero before and after)."""
     lib = _lib.load()
     ns = int(n_splits)
     rc = lib.ps_select_sparse_decode(
         *_select_decode_args(g, q, k_pool, v_pool, page_table, seq_lens, scores, budget_pages,
                              n_sink, n_local, scale), ns,
         *_select_decode_outputs(g, budget_pages, ns, sel, sel_count, part_acc, part_ml, sink,
-                                out, lse, stream))
+                                out, lse, arrivals, stream))
     _lib.check("ps_select_sparse_decode", rc)
 
 
@@ -241,7 +243,7 @@ def ps_select_topdelta_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table,
                                      scores, budget_pages: int, n_sink: int, n_local: int,
                                      scale: float, delta: float, n_splits: int, sel, sel_count,
                                      part_acc, part_ml, sink=None, out=None, lse=None,
-                                     stream=None) -> None:
+                                     stream=None, arrivals=None) -> None:
     """ps_select_topdelta and ps_sparse_decode in one launch (arguments as
     ps_select_sparse_decode, delta as ps_select_topdelta)."""
     lib = _lib.load()
@@ -250,7 +252,7 @@ def ps_select_topdelta_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table,
         *_select_decode_args(g, q, k_pool, v_pool, page_table, seq_lens, scores, budget_pages,
                              n_sink, n_local, scale), float(delta), ns,
         *_select_decode_outputs(g, budget_pages, ns, sel, sel_count, part_acc, part_ml, sink,
-                                out, lse, stream))
+                                out, lse, arrivals, stream))
     _lib.check("ps_select_topdelta_sparse_decode", rc)
 
 

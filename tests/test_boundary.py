@@ -169,9 +169,9 @@ def test_fused_select_decode_validation():
     g = geom()
 
     def call(g=g, sel=X, cnt=X, budget=8, ns=1, nl=2, splits=2, scores=X, acc=X, ml=X,
-             sink=None, out=None, lse=None):
+             sink=None, out=None, lse=None, arr=None):
         return lib.ps_select_sparse_decode(g, X, X, X, X, X, scores, budget, ns, nl, 0.1, splits,
-                                           sel, cnt, acc, ml, sink, out, lse, None)
+                                           sel, cnt, acc, ml, sink, out, lse, arr, None)
     assert call(scores=None) == _lib.PS_ERR_NULL
     assert call(sel=None) == _lib.PS_ERR_NULL           # one of the pair
     assert call(cnt=None) == _lib.PS_ERR_NULL
@@ -184,12 +184,17 @@ def test_fused_select_decode_validation():
     assert call(g=geom(max_pages=8193)) == _lib.PS_ERR_UNSUPPORTED
     assert call(budget=1026, ns=0, nl=0, splits=2) == _lib.PS_ERR_UNSUPPORTED  # 513 per split
     assert call(acc=None) == _lib.PS_ERR_NULL           # partials needed without out
-    assert call(out=X) == _lib.PS_ERR_BUDGET            # merged output needs one split
-    assert call(sink=X) == _lib.PS_ERR_BUDGET           # sink and lse only with out
+    assert call(out=X) == _lib.PS_ERR_BUDGET            # several splits merge with arrivals
+    assert call(sink=X) == _lib.PS_ERR_BUDGET           # sink, lse, arrivals only with out
     assert call(lse=X) == _lib.PS_ERR_BUDGET
+    assert call(arr=X) == _lib.PS_ERR_BUDGET
+    assert call(out=X, arr=X, acc=None) == _lib.PS_ERR_NULL  # several splits write partials
+    assert call(out=X, arr=X, ml=None) == _lib.PS_ERR_NULL
     assert call(g=geom(batch=0), sel=None, cnt=None) == _lib.PS_OK
     assert call(g=geom(batch=0), splits=1, acc=None, ml=None, sink=X, out=X, lse=X) == \
         _lib.PS_OK
+    assert call(g=geom(batch=0), splits=4, sink=X, out=X, lse=X, arr=X) == _lib.PS_OK
+    assert call(g=geom(batch=0, kv_dtype=_lib.PS_F32), splits=4, out=X, arr=X) == _lib.PS_OK
 
 
 def test_fused_topdelta_decode_validation():
@@ -197,15 +202,18 @@ def test_fused_topdelta_decode_validation():
     g = geom()
 
     def call(g=g, sel=X, cnt=X, budget=8, ns=1, nl=2, scale=0.1, delta=1.0, splits=2, acc=X,
-             ml=X, sink=None, out=None, lse=None):
+             ml=X, sink=None, out=None, lse=None, arr=None):
         return lib.ps_select_topdelta_sparse_decode(g, X, X, X, X, X, X, budget, ns, nl, scale,
                                                     delta, splits, sel, cnt, acc, ml, sink, out,
-                                                    lse, None)
+                                                    lse, arr, None)
     assert call(sel=None) == _lib.PS_ERR_NULL
     assert call(acc=None) == _lib.PS_ERR_NULL
     assert call(ns=5, nl=4) == _lib.PS_ERR_BUDGET
     assert call(splits=9) == _lib.PS_ERR_BUDGET
     assert call(out=X) == _lib.PS_ERR_BUDGET
+    assert call(arr=X) == _lib.PS_ERR_BUDGET
+    assert call(out=X, arr=X, acc=None) == _lib.PS_ERR_NULL
+    assert call(out=X, arr=X, delta=-1.0) == _lib.PS_ERR_BUDGET
     assert call(delta=-1.0) == _lib.PS_ERR_BUDGET
     assert call(delta=float("nan")) == _lib.PS_ERR_BUDGET
     assert call(scale=0.0) == _lib.PS_ERR_BUDGET
@@ -215,6 +223,7 @@ def test_fused_topdelta_decode_validation():
     assert call(g=geom(batch=0), delta=float("inf")) == _lib.PS_OK
     assert call(g=geom(batch=0, kv_dtype=_lib.PS_F32), splits=1, acc=None, ml=None, sink=X,
                 out=X, lse=X) == _lib.PS_OK
+    assert call(g=geom(batch=0), splits=3, out=X, lse=X, arr=X) == _lib.PS_OK
 
 
 def test_partials_overflow():

@@ -5,7 +5,8 @@ identical, on the small workloads (bf16 and fp32 pools, several splits,
 ragged tails, sink and local pages, budgets that cover every page of short
 requests), on fp32 pools with longer rows (the selection's larger register
 tiles) and on the 32 x 64k workload in the benchmark's launch
-configuration."""
+configuration; with several splits the merge made in the launch by the last
+split of each (request, KV head) equals ps_combine's, bit for bit."""
 
 import pytest
 import torch
@@ -123,6 +124,54 @@ def test_fused_one_split_merged_output_bitwise(w):
                               inp["seq_lens"], None)
         torch.cuda.synchronize()
         assert torch.equal(got, want)
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_in_launch_merge_of_several_splits_bitwise(w):
+    """With several splits and a merged output, the last split of each
+    (request, KV head) to finish merges them in the launch: outputs and lse
+    equal, bit for bit, to ps_combine over the same partials (with and
+    without the sink, and without lse); page lists and partials unchanged;
+    the arrival counters are zero after every launch, and the next launches,
+    on other queries, reuse them and are exact again."""
+    if w.budget_pages < 2:
+        pytest.skip("one page: one split only")
+    inp = wl.make_inputs(w, device="cuda")
+    g = geometry(inp)
+    meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+    ns = max(2, min(w.n_splits, w.budget_pages))
+    mk = dict(budget_pages=w.budget_pages, n_sink=w.n_sink, n_local=w.n_local, n_splits=ns,
+              dense_splits=w.dense_splits, scale=inp["scale"])
+    merged = DecodeStep(g, **mk)
+    plain = DecodeStep(g, **mk, merge_in_launch=False)
+    assert merged.merge_in_launch and plain.fused and not plain.merge_in_launch
+    queries = [inp["q"], -inp["q"], inp["q"] * 0.5]
+    sinks = [inp["sink"], None, inp["sink"]]
+    for i, (q, sink) in enumerate(zip(queries, sinks)):
+        merged.out.fill_(float("nan"))
+        merged.lse.fill_(float("nan"))
+        got = merged.sparse(q, inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
+                            inp["seq_lens"], sink)
+        want = plain.sparse(q, inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
+                            inp["seq_lens"], sink)
+        torch.cuda.synchronize()
+        for a, b, k in zip(got, want, ("out", "lse")):
+            assert torch.equal(a, b), (w.name, i, k)
+        for a, b in zip(merged.partials(ns), plain.partials(ns)):
+            assert torch.equal(a, b), (w.name, i)
+        assert torch.equal(merged.sel, plain.sel) and torch.equal(merged.sel_count,
+                                                                   plain.sel_count)
+        assert int(merged.arrivals.abs().sum()) == 0, (w.name, i)
+    # without lse: the same output
+    out = torch.full_like(merged.out, float("nan"))
+    acc, ml = merged.partials(ns)
+    ops.ps_select_sparse_decode(g, queries[-1], inp["k_pool"], inp["v_pool"], inp["page_table"],
+                                inp["seq_lens"], merged.scores, w.budget_pages, w.n_sink,
+                                w.n_local, inp["scale"], ns, None, None, acc, ml, sinks[-1],
+                                out, None, arrivals=merged.arrivals)
+    torch.cuda.synchronize()
+    assert torch.equal(out, plain.out)
+    assert int(merged.arrivals.abs().sum()) == 0
 
 
 @pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
