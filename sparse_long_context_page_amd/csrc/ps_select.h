@@ -32,7 +32,6 @@ struct SelectLds {
   int hist[3][kSelBins];
   uint32_t wave_min[WAVES], wave_max[WAVES];
   int wave_cnt[WAVES];
-  int wave_pass[WAVES];  // FILTER: candidates passing the threshold, per wavefront
   uint64_t bin_val[kSelRankMax];  // the threshold bin as (key, ~page) values
   uint64_t cut;  // kept: every candidate at or above this value
 };
@@ -41,6 +40,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The score of a key (a negative zero comes back as +0, which compares the
+// same).
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -58,11 +63,15 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 //
 // FILTER (top-delta selection, "Faster Than Flash: Exploiting Attention
 // Sparsity for Efficient Long-Context Decoding", section "Methodology", item
-// 2): only pages with scale * score >= tau (compared in fp64) are candidates,
-// and r = min(budget - |forced|, passing candidates); the others are dropped.
-// tau_fn.issue() is called by every thread before the scores are requested
-// (to start the threshold's own loads) and tau = tau_fn() once they are, so
-// the threshold's work overlaps their loads (it may hold barriers).
+// 2): only pages with scale * score >= tau (compared in fp64) are kept, at
+// most budget - |forced| of them, the best. The passing pages are a prefix
+// of the (score descending, page ascending) order, so these are the best
+// budget - |forced| candidates of all with the failing ones dropped: the
+// radix passes run on every candidate and tau is applied at the end. Every
+// thread calls tau_fn.issue() before the scores are requested and
+// tau_fn.prefetch() after (the threshold's loads: table entries, then key
+// rows), and tau = tau_fn() once the cut is known, so the threshold's round
+// trips overlap the passes (it may hold barriers).
 //
 // The kept candidates are the r best in the order (key descending, page
 // ascending). Radix passes narrow the r-th key's bits; once its bin holds at
@@ -72,6 +81,7 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // the cut is the remaining-th lowest page among them.
 struct NoThreshold {
   __device__ void issue() const {}
+  __device__ void prefetch() const {}
   __device__ double operator()() const { return 0.0; }
 };
 
@@ -99,10 +109,6 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
   // Keys (pages past the request re-read its last score and never count).
   uint32_t key[C];
   int phys[PHYS ? C : 1];
-  // FILTER: bit j % 32 of word j / 32 set when page(j) passes the threshold
-  uint32_t pass_bits[FILTER ? (C + 31) / 32 : 1];
-#pragma unroll
-  for (int i = 0; i < (FILTER ? (C + 31) / 32 : 1); ++i) pass_bits[i] = 0u;
   if constexpr (FILTER) tau_fn.issue();
   float sc[C];
 #pragma unroll
@@ -110,42 +116,30 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
     sc[j] = row[min(page(j), n - 1)];
     if constexpr (PHYS) phys[j] = table[min(page(j), n - 1)];
   }
-  double tau = 0.0;
-  if constexpr (FILTER) tau = tau_fn();
+  if constexpr (FILTER) tau_fn.prefetch();
 #pragma unroll
-  for (int j = 0; j < C; ++j) {
-    key[j] = order_key(sc[j]);
-    if constexpr (FILTER)
-      pass_bits[j / 32] |= (scale * (double)sc[j] >= tau ? 1u : 0u) << (j % 32);
-  }
-  auto cand_j = [&](int j) {
-    return in_range(page(j)) && (!FILTER || ((pass_bits[FILTER ? j / 32 : 0] >> (j % 32)) & 1u));
-  };
+  for (int j = 0; j < C; ++j) key[j] = order_key(sc[j]);
+  auto cand_j = [&](int j) { return in_range(page(j)); };
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  int n_pass = 0;
 #pragma unroll
   for (int j = 0; j < C; ++j) {
     const bool c = cand_j(j);
     kmin = c ? min(kmin, key[j]) : kmin;
     kmax = c ? max(kmax, key[j]) : kmax;
-    if constexpr (FILTER) n_pass += __popcll(__ballot(c));
   }
   kmin = wave_min_u32(kmin);
   kmax = wave_max_u32(kmax);
   if (lane == 0) {
     sh.wave_min[wave] = kmin;
     sh.wave_max[wave] = kmax;
-    if constexpr (FILTER) sh.wave_pass[wave] = n_pass;
   }
   for (int i = tid; i < 2 * kSelBins; i += kThreads) sh.hist[i / kSelBins][i % kSelBins] = 0;
   __syncthreads();
-  int cands = hi - lo;  // candidates (all scored pages, or those passing the threshold)
-  if constexpr (FILTER) cands = 0;
+  const int cands = hi - lo;  // candidates: every scored page that is not forced
 #pragma unroll
   for (int w = 0; w < WAVES; ++w) {
     kmin = min(kmin, sh.wave_min[w]);
     kmax = max(kmax, sh.wave_max[w]);
-    if constexpr (FILTER) cands += sh.wave_pass[w];
   }
   const int r = min(budget - n_sink - n_local, cands);  // candidates to keep
 
@@ -255,6 +249,12 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
     cut = sh.cut;
   }
 
+  // FILTER: kept candidates below the threshold are dropped (ties in the bin
+  // have equal scores and pass or fail together)
+  double tau = 0.0;
+  if constexpr (FILTER) tau = tau_fn();
+  auto passes = [&](uint32_t k) { return !FILTER || scale * (double)key_value(k) >= tau; };
+
   // Class of each page, 2 bits per page: 2 = kept, 1 = tie in the bin (the
   // lowest `remaining` of them are kept), 0 = dropped or past the request.
   uint32_t cls[(C + 15) / 16];
@@ -270,7 +270,7 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
     const bool tie = !ranked && km == prefix;
     const int cc = above ? 2 : (tie ? 1 : 0);
     // out of range = forced (kept); in range but below the threshold: dropped
-    const int c = p >= n ? 0 : (!in_range(p) ? 2 : (!cand_j(j) || remaining == 0 ? 0 : cc));
+    const int c = p >= n ? 0 : (!in_range(p) ? 2 : (remaining == 0 || !passes(k) ? 0 : cc));
     cls[j / 16] |= (uint32_t)c << (2 * (j % 16));
     cnt_keep += c == 2 ? 1 : 0;
     cnt_tie += c == 1 ? 1 : 0;
@@ -389,6 +389,7 @@ struct TopDeltaThreshold {
   TopDeltaLds<WAVES, D, kG>* sh;
   int phys0 = 0;  // page of this thread's first-round token
   float4 qv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  uint4 kv0[kLoads];  // this thread's share of its first-round key row
 
   __device__ int ng() const { return G ? G : group; }
   __device__ bool active() const { return budget < n && n_sink + n_local > 0; }
@@ -407,6 +408,18 @@ struct TopDeltaThreshold {
     if (t < ng() * D / 4) qv = reinterpret_cast<const float4*>(qg)[t];
     const int ft = t / kParts;
     phys0 = ft < tokens() ? table[page_of(ft)] : 0;
+  }
+
+  // The first round's key rows, requested as soon as their table entries
+  // (issue) have arrived; later loads need not complete first.
+  __device__ void prefetch() {
+    if (!active()) return;  // uniform
+    const int t = threadIdx.x;
+    const int ft = t / kParts;
+    const int tt = ft < tokens() ? ft % kPage : 0;
+    const T* krow = k_pool + (((int64_t)phys0 * hkv + g) * kPage + tt) * D + (t % kParts) * kCoords;
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) kv0[i] = ld16(krow + i * kVec);
   }
 
   __device__ double operator()() {
@@ -431,14 +444,19 @@ struct TopDeltaThreshold {
       const int p = ft < n_tok ? page_of(ft) : 0;
       const int tt = ft % kPage;
       const bool valid = ft < n_tok && p * kPage + tt < len;
-      const int phys = base == 0 ? phys0 : (ft < n_tok ? table[p] : 0);
       // rows past the forced tokens read row 0 of physical page 0 (in the
-      // pool) and are not counted
-      const T* krow = k_pool + (((int64_t)phys * hkv + g) * kPage + (ft < n_tok ? tt : 0)) * D +
-                      part * kCoords;
+      // pool) and are not counted; the first round's rows were prefetched
       uint4 kv[kLoads];
+      if (base == 0) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) kv[i] = ld16(krow + i * kVec);
+        for (int i = 0; i < kLoads; ++i) kv[i] = kv0[i];
+      } else {
+        const int phys = ft < n_tok ? table[p] : 0;
+        const T* krow = k_pool + (((int64_t)phys * hkv + g) * kPage + (ft < n_tok ? tt : 0)) * D +
+                        part * kCoords;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) kv[i] = ld16(krow + i * kVec);
+      }
       if (base == 0) __syncthreads();  // sh->q complete
       double k64[kCoords];
 #pragma unroll
