@@ -37,6 +37,5 @@ from .pagesparse_ref import (  # noqa: F401
     sparse_split_slots,
     dense_split_pages,
     unit_step,
-    decode_step,
     full_decode,
 )

@@ -118,18 +118,26 @@ def unit_page_meta(k_pool, kv_dtype, page_table, seq_lens, b, g, page_size):
     """Elementwise max and min of the valid keys of each logical page.
 
     Returns (kmax, kmin), each float64 [n_pages(b), D], for request b and KV
-    head g. Slots past the sequence end on the last page are ignored.
+    head g. Slots past the sequence end on the last page are ignored. The
+    full pages are reduced together (their token axis is whole); the last
+    page, which may be partial, is reduced over its valid tokens only.
     """
-    n = num_pages(int(seq_lens[b]), page_size)
+    seq_len = int(seq_lens[b])
+    n = num_pages(seq_len, page_size)
     d = k_pool.shape[-1]
     kmax = np.empty((n, d), dtype=np.float64)
     kmin = np.empty((n, d), dtype=np.float64)
-    for p in range(n):
-        phys = int(page_table[b, p])
-        cnt = page_token_count(int(seq_lens[b]), p, page_size)
-        keys = widen(k_pool[phys, g, :cnt, :], kv_dtype)  # [cnt, D]
-        kmax[p] = keys.max(axis=0)
-        kmin[p] = keys.min(axis=0)
+    if n == 0:
+        return kmax, kmin
+    phys = np.asarray(page_table[b, :n], dtype=np.int64)
+    if n > 1:  # pages 0 .. n-2 hold page_size valid tokens each
+        keys = widen(np.asarray(k_pool[phys[:-1], g]), kv_dtype)  # [n-1, page, D]
+        kmax[:-1] = keys.max(axis=1)
+        kmin[:-1] = keys.min(axis=1)
+    cnt = page_token_count(seq_len, n - 1, page_size)
+    last = widen(np.asarray(k_pool[phys[-1], g, :cnt, :]), kv_dtype)  # [cnt, D]
+    kmax[-1] = last.max(axis=0)
+    kmin[-1] = last.min(axis=0)
     return kmax, kmin
 
 
@@ -549,13 +557,6 @@ def unit_step(inp, b, g, budget, n_sink, n_local, sel_override=None, delta=None)
         lses.append(l)
     return {"u": u, "scores": s, "mag": mag, "sel": sel, "forced": forced, "taken": taken,
             "out": np.stack(outs), "lse": np.array(lses), "n": n, "tau": tau}
-
-
-def decode_step(inp, budget, n_sink, n_local, units=None):
-    """unit_step over every (b, g) (or the given list of units)."""
-    b_, hkv = inp["q"].shape[0], inp["k_pool"].shape[1]
-    units = [(b, g) for b in range(b_) for g in range(hkv)] if units is None else units
-    return {(b, g): unit_step(inp, b, g, budget, n_sink, n_local) for b, g in units}
 
 
 def full_decode(inp, b, h):

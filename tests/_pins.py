@@ -49,6 +49,102 @@ def check_meta_bounds(ref, h):
     assert np.all(kmax == 0.375) and np.all(kmin == 0.375)
 
 
+def _append_tokens(h, extra, seed=5):
+    """A copy of host inputs h with extra[b] more tokens in request b: new key
+    rows (N(0,1), fp32 or bf16 bits) written into the free slots of the last
+    page and, past it, into pages mapped to fresh physical pages appended to
+    the pool. Input drawing only."""
+    rng = np.random.default_rng(seed)
+    ps = h["page_size"]
+    k = h["k_pool"]
+    table = h["page_table"].copy()
+    lens = h["seq_lens"].astype(np.int64).copy()
+    need = []
+    for b in range(table.shape[0]):
+        n_old = ref_num_pages(int(lens[b]), ps)
+        n_new = ref_num_pages(int(lens[b]) + int(extra[b]), ps)
+        need.append((b, n_old, n_new))
+    fresh = sum(n_new - n_old for _, n_old, n_new in need)
+    pool = np.concatenate([k, np.zeros((fresh,) + k.shape[1:], dtype=k.dtype)], axis=0)
+    width = max(n_new for _, _, n_new in need)
+    if table.shape[1] < width:  # widen the table rows (entries past n_b are ignored)
+        table = np.concatenate(
+            [table, np.zeros((table.shape[0], width - table.shape[1]), dtype=table.dtype)], axis=1)
+    nxt = k.shape[0]
+    for b, n_old, n_new in need:
+        for p in range(n_old, n_new):
+            table[b, p] = nxt
+            nxt += 1
+        for t in range(int(lens[b]), int(lens[b]) + int(extra[b])):
+            row = rng.standard_normal((pool.shape[1], pool.shape[3])).astype(np.float32)  # [Hkv, D]
+            if h["kv_dtype"] == "bf16":
+                row = (row.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+            pool[table[b, t // ps], :, t % ps, :] = row
+        lens[b] += int(extra[b])
+    out = dict(h)
+    out.update(k_pool=pool, page_table=table, seq_lens=lens.astype(np.int32))
+    return out
+
+
+def ref_num_pages(seq_len, page):
+    return -(-int(seq_len) // int(page))
+
+
+def check_meta_pool(ref, h):
+    """The pool-wide metadata build: every mapped (physical page, KV head)
+    entry bounds the page's valid keys and attains both bounds (the
+    definition of an elementwise max and min), unmapped pages are absent,
+    and an incremental build of only the pages that appended tokens touch,
+    merged into the previous pool, equals the full build of the new state
+    bit for bit ("Don't read the haystack", "Part two: the skipping": the
+    summaries are maintained as tokens append)."""
+    ps = h["page_size"]
+    hkv = h["k_pool"].shape[1]
+    pool = ref.page_meta_pool(h["k_pool"], h["kv_dtype"], h["page_table"], h["seq_lens"], ps)
+    mapped = set()
+    for b in range(h["page_table"].shape[0]):
+        n = ref.num_pages(int(h["seq_lens"][b]), ps)
+        for p in range(n):
+            phys = int(h["page_table"][b, p])
+            cnt = ref.page_token_count(int(h["seq_lens"][b]), p, ps)
+            for g in range(hkv):
+                mapped.add((phys, g))
+                keys = ref.widen(h["k_pool"][phys, g, :cnt], h["kv_dtype"])
+                kmax, kmin = pool[(phys, g)]
+                assert np.all(keys <= kmax) and np.all(keys >= kmin)
+                assert np.all(np.any(keys == kmax, axis=0))
+                assert np.all(np.any(keys == kmin, axis=0))
+    assert set(pool) == mapped
+    # append 1, 16 and 17 tokens (within the page, exactly one page, across
+    # a page boundary) and rebuild only the touched pages
+    extra = [(1, 16, 17)[b % 3] for b in range(h["page_table"].shape[0])]
+    h2 = _append_tokens(h, extra)
+    touched = {}
+    for b in range(h["page_table"].shape[0]):
+        n_old = ref.num_pages(int(h["seq_lens"][b]), ps)
+        n_new = ref.num_pages(int(h2["seq_lens"][b]), ps)
+        touched[b] = list(range(n_old - 1, n_new))
+    inc = ref.page_meta_pool(h2["k_pool"], h2["kv_dtype"], h2["page_table"], h2["seq_lens"], ps,
+                             pages_of=touched)
+    assert set(inc) == {(int(h2["page_table"][b, p]), g) for b, ps_ in touched.items()
+                        for p in ps_ for g in range(hkv)}
+    merged = dict(pool)
+    merged.update(inc)
+    full = ref.page_meta_pool(h2["k_pool"], h2["kv_dtype"], h2["page_table"], h2["seq_lens"], ps)
+    assert set(merged) == set(full)
+    for key, (kmax, kmin) in full.items():
+        assert np.array_equal(merged[key][0], kmax) and np.array_equal(merged[key][1], kmin)
+    # the per-unit build agrees with the pool build on every mapped page
+    for b in range(h2["page_table"].shape[0]):
+        for g in range(hkv):
+            kmax, kmin = ref.unit_page_meta(h2["k_pool"], h2["kv_dtype"], h2["page_table"],
+                                            h2["seq_lens"], b, g, ps)
+            n = ref.num_pages(int(h2["seq_lens"][b]), ps)
+            for p in range(n):
+                e = full[(int(h2["page_table"][b, p]), g)]
+                assert np.array_equal(e[0], kmax[p]) and np.array_equal(e[1], kmin[p])
+
+
 def check_score_admissible(ref, h):
     """The per-page bound is >= every q.k in the page for every query head of
     the group ("Don't read the haystack", "Part two: the skipping")."""

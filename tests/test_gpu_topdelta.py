@@ -136,7 +136,7 @@ def test_step_end_to_end(case):
             n = r["n"]
             mt = _oracle_pseudo_max(hu, n, w.n_sink, w.n_local, w.budget_pages)
             amb = ref.ambiguous_pages_topdelta(r["scores"], n, w.budget_pages, w.n_sink,
-                                               w.n_local, hu["scale"], mt, delta, rel=1e-5,
+                                               w.n_local, hu["scale"], mt, delta,
                                                mag=r["mag"])
             k = int(cnt[b, kv])
             got = set(int(x) for x in sel[b, kv, :k])
@@ -317,7 +317,7 @@ def test_step_with_8bit_metadata():
             n = r["n"]
             mt = _oracle_pseudo_max(hu, n, w.n_sink, w.n_local, w.budget_pages)
             amb = ref.ambiguous_pages_topdelta(r["scores"], n, w.budget_pages, w.n_sink,
-                                               w.n_local, hu["scale"], mt, deltas[0], rel=1e-5,
+                                               w.n_local, hu["scale"], mt, deltas[0],
                                                mag=r["mag"])
             k = int(cnt[b, kv])
             assert set(int(x) for x in sel[b, kv, :k]) - amb == \

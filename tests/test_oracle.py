@@ -17,7 +17,7 @@ import oracle as ref
 import workloads as wl
 from _pins import (check_dense_is_exact_attention, check_fp8_bound_admissible, check_fp8_decode,
                    check_topdelta, check_topdelta_no_forced_is_topk, tight_small_inputs,
-                   check_fp8_directed_rounding, check_meta_bounds, check_restricted_reference,
+                   check_fp8_directed_rounding, check_meta_bounds, check_meta_pool, check_restricted_reference,
                    check_score_admissible, check_score_closed_forms, check_selection_bruteforce,
                    check_selection_rank_count, check_sink, check_split_invariance,
                    check_split_ranges, small_inputs)
@@ -56,6 +56,11 @@ def test_page_counts():
 def test_meta_bounds(small):
     _, _, h = small
     check_meta_bounds(ref, h)
+
+
+def test_meta_pool_and_incremental_update(small, tiny):
+    check_meta_pool(ref.pagesparse_ref, small[2])
+    check_meta_pool(ref.pagesparse_ref, tiny[1])
 
 
 def test_meta_bounds_fp32(tiny):
@@ -374,6 +379,28 @@ def test_mutation_meta_ignores_valid_mask(monkeypatch, small):
         return keys.max(1), keys.min(1)
     monkeypatch.setattr(ref.pagesparse_ref, "unit_page_meta", bad)
     _expect_fail(check_meta_bounds, ref.pagesparse_ref, small[2])
+
+
+def test_mutation_meta_pool_ignores_valid_mask(monkeypatch, small):
+    def bad(k_pool, kv_dtype, page_table, seq_lens, page_size, pages_of=None):
+        out = {}
+        for b in range(page_table.shape[0]):
+            n = ref.num_pages(int(seq_lens[b]), page_size)
+            pages = range(n) if pages_of is None else [p for p in pages_of[b] if 0 <= p < n]
+            for p in pages:
+                for g in range(k_pool.shape[1]):
+                    keys = ref.widen(k_pool[int(page_table[b, p]), g], kv_dtype)
+                    out[(int(page_table[b, p]), g)] = (keys.max(0), keys.min(0))
+        return out
+    monkeypatch.setattr(ref.pagesparse_ref, "page_meta_pool", bad)
+    _expect_fail(check_meta_pool, ref.pagesparse_ref, small[2])
+
+
+def test_mutation_meta_pool_ignores_pages_of(monkeypatch, small):
+    orig = ref.pagesparse_ref.page_meta_pool
+    monkeypatch.setattr(ref.pagesparse_ref, "page_meta_pool",
+                        lambda k, dt, t, sl, ps, pages_of=None: orig(k, dt, t, sl, ps))
+    _expect_fail(check_meta_pool, ref.pagesparse_ref, small[2])
 
 
 def test_mutation_tie_to_higher_index(monkeypatch):
