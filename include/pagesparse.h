@@ -16,9 +16,11 @@
  * ---------------------------------------
  * - Every pointer except `geom` is a DEVICE pointer owned by the caller, to a
  *   contiguous row-major array laid out as documented. The library allocates
- *   nothing, keeps no state between calls, never synchronises and enqueues
- *   work only on `stream` (a hipStream_t; NULL means the null stream). The
- *   calls are therefore safe to capture into a HIP graph.
+ *   nothing, never synchronises and enqueues work only on `stream` (a
+ *   hipStream_t; NULL means the null stream). The calls are therefore safe
+ *   to capture into a HIP graph. No call keeps state between calls except
+ *   ps_select_sparse_decode_noalloc, whose workspace is one fixed device
+ *   array of the library per GPU (see there).
  * - The return value is a ps_status. PS_OK means the work was enqueued.
  *   Arguments are validated on the host BEFORE any HIP call; a failed
  *   validation returns its code and enqueues nothing. Device-resident values
@@ -52,7 +54,8 @@ typedef enum {
   PS_ERR_UNSUPPORTED = -3, /* a valid shape the library does not implement       */
   PS_ERR_OVERFLOW = -4,    /* a size computation overflows 64 bits / int32 index */
   PS_ERR_BUDGET = -5,      /* budget, forced-page or split arguments inconsistent */
-  PS_ERR_HIP = -6          /* the HIP runtime reported an error at launch        */
+  PS_ERR_HIP = -6,         /* the HIP runtime reported an error at launch        */
+  PS_ERR_WORKSPACE = -7    /* needs more than the library's fixed workspace       */
 } ps_status;
 
 typedef enum {
@@ -273,6 +276,35 @@ int ps_select_sparse_decode(const ps_geom* geom, const float* q, const void* k_p
                             int32_t n_splits, int32_t* sel, int32_t* sel_count, float* part_acc,
                             float* part_ml, const float* sink, float* out, float* lse,
                             int32_t* arrivals, void* stream);
+
+/* 3+4a+5 without allocation: ps_select_sparse_decode with out, with the
+ * split partials and the arrival counters in a fixed-size device array of
+ * the library instead of caller buffers. For callers that cannot allocate
+ * or pass workspace: code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc. The caller passes inputs and outputs only;
+ * nothing is allocated (no hipMalloc, hipFree or allocating library call).
+ * Results are bitwise those of ps_select_sparse_decode with out (sel,
+ * sel_count when not NULL, out, lse when not NULL).
+ * Workspace: one array of 8 MiB per GPU, held from the library's first use
+ * on that GPU until the process ends; its device address is looked up once
+ * per device. A call needs 256-byte-aligned room for B*Hkv int32 counters
+ * plus B*Hq*n_splits*(D+2) floats of partials (none of the partials with one
+ * split); a call needing more returns PS_ERR_WORKSPACE and enqueues nothing.
+ * Each call first clears the counters (a small kernel on `stream`, so a
+ * captured graph replays it), then launches the decode. Every call on one
+ * GPU uses the same array: calls that overlap in time on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.
+ * Arguments as ps_select_sparse_decode; out is required.
+ * Host checks: those of ps_select_sparse_decode with out set (same codes;
+ * out NULL is PS_ERR_NULL), then PS_ERR_WORKSPACE as above.
+ * Device preconditions: those of ps_select_sparse_decode. */
+int ps_select_sparse_decode_noalloc(const ps_geom* geom, const float* q, const void* k_pool,
+                                    const void* v_pool, const int32_t* page_table,
+                                    const int32_t* seq_lens, const float* scores,
+                                    int32_t budget_pages, int32_t n_sink_pages,
+                                    int32_t n_local_pages, float scale, int32_t n_splits,
+                                    int32_t* sel, int32_t* sel_count, const float* sink,
+                                    float* out, float* lse, void* stream);
 
 /* 3'+4a. Top-delta selection fused into the sparse decode: one launch does
  * the work of ps_select_topdelta followed by ps_sparse_decode, with bitwise

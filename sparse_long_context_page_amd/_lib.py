@@ -17,6 +17,7 @@ PS_ERR_UNSUPPORTED = -3
 PS_ERR_OVERFLOW = -4
 PS_ERR_BUDGET = -5
 PS_ERR_HIP = -6
+PS_ERR_WORKSPACE = -7
 
 PS_F32 = 0
 PS_BF16 = 1
@@ -30,6 +31,7 @@ ENTRY_POINTS = (
     "ps_select_topdelta",
     "ps_sparse_decode",
     "ps_select_sparse_decode",
+    "ps_select_sparse_decode_noalloc",
     "ps_select_topdelta_sparse_decode",
     "ps_full_decode",
     "ps_combine",
@@ -81,6 +83,8 @@ _SIGS = {
     "ps_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _P, _I, _F, _I, _P, _P, _P],
     "ps_select_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P, _P, _P,
                                 _P, _P, _P, _P, _P, _P],
+    "ps_select_sparse_decode_noalloc": [_G, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _I, _P,
+                                        _P, _P, _P, _P, _P],
     "ps_select_topdelta_sparse_decode": [_G, _P, _P, _P, _P, _P, _P, _I, _I, _I, _F, _F, _I,
                                          _P, _P, _P, _P, _P, _P, _P, _P, _P],
     "ps_full_decode": [_G, _P, _P, _P, _P, _P, _F, _I, _P, _P, _P],

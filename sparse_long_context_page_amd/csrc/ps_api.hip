@@ -222,6 +222,32 @@ PS_API int ps_select_sparse_decode(const ps_geom* geom, const float* q, const vo
                                              out, lse, arrivals, (hipStream_t)stream));
 }
 
+PS_API int ps_select_sparse_decode_noalloc(const ps_geom* geom, const float* q,
+                                           const void* k_pool, const void* v_pool,
+                                           const int32_t* page_table, const int32_t* seq_lens,
+                                           const float* scores, int32_t budget_pages,
+                                           int32_t n_sink_pages, int32_t n_local_pages,
+                                           float scale, int32_t n_splits, int32_t* sel,
+                                           int32_t* sel_count, const float* sink, float* out,
+                                           float* lse, void* stream) {
+  ps::Shape s;
+  // the workspace stands in for the caller's partials and counters in the
+  // checks they share with ps_select_sparse_decode
+  const float* ws = reinterpret_cast<const float*>(out);
+  int rc = check_select_decode(geom, &s, q, k_pool, v_pool, page_table, seq_lens, scores,
+                               budget_pages, n_sink_pages, n_local_pages, n_splits, sel,
+                               sel_count, ws, ws, sink, out, lse,
+                               reinterpret_cast<const int32_t*>(out));
+  if (rc) return rc;
+  if (!out) return PS_ERR_NULL;
+  const int64_t need = ps::noalloc_scratch_bytes(s, n_splits);
+  if (need < 0 || need > ps::kNoAllocScratchBytes) return PS_ERR_WORKSPACE;
+  if (s.batch == 0) return PS_OK;
+  return hip_status(ps::launch_select_decode_noalloc(
+      s, q, k_pool, v_pool, page_table, seq_lens, scores, budget_pages, n_sink_pages,
+      n_local_pages, scale, n_splits, sel, sel_count, sink, out, lse, (hipStream_t)stream));
+}
+
 PS_API int ps_select_topdelta_sparse_decode(const ps_geom* geom, const float* q,
                                             const void* k_pool, const void* v_pool,
                                             const int32_t* page_table, const int32_t* seq_lens,
@@ -285,8 +311,10 @@ PS_API const char* ps_strerror(int status) {
     case PS_ERR_OVERFLOW: return "PS_ERR_OVERFLOW: a size computation overflows";
     case PS_ERR_BUDGET: return "PS_ERR_BUDGET: budget, forced-page or split arguments invalid";
     case PS_ERR_HIP: return "PS_ERR_HIP: the HIP runtime reported a launch error";
+    case PS_ERR_WORKSPACE:
+      return "PS_ERR_WORKSPACE: the call needs more than the library's fixed workspace";
     default: return "unknown ps_status";
   }
 }
 
-PS_API int ps_abi_version(void) { return (1 << 16) | 6; }  // 1.6: in-launch merge of several splits
+PS_API int ps_abi_version(void) { return (1 << 16) | 7; }  // 1.7: decode without allocation

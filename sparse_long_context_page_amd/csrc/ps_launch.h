@@ -50,6 +50,21 @@ hipError_t launch_select_decode(const Shape& s, const float* q, const void* k_po
                                 const float* sink, float* out, float* lse, int32_t* arrivals,
                                 hipStream_t st);
 
+// Fixed size of the library's own workspace array (ps_noalloc.hip), and the
+// bytes a scratch-backed selecting decode of this shape needs in it.
+constexpr int64_t kNoAllocScratchBytes = int64_t(8) << 20;
+int64_t noalloc_scratch_bytes(const Shape& s, int n_splits);
+
+// launch_select_decode with the partials and arrival counters in that array
+// (the merged output is always written).
+hipError_t launch_select_decode_noalloc(const Shape& s, const float* q, const void* k_pool,
+                                        const void* v_pool, const int32_t* page_table,
+                                        const int32_t* seq_lens, const float* scores,
+                                        int budget, int n_sink, int n_local, float scale,
+                                        int n_splits, int32_t* sel, int32_t* sel_count,
+                                        const float* sink, float* out, float* lse,
+                                        hipStream_t st);
+
 hipError_t launch_select_topdelta_decode(const Shape& s, const float* q, const void* k_pool,
                                          const void* v_pool, const int32_t* page_table,
                                          const int32_t* seq_lens, const float* scores,

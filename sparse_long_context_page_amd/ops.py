@@ -239,6 +239,27 @@ def ps_select_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens
     _lib.check("ps_select_sparse_decode", rc)
 
 
+def ps_select_sparse_decode_noalloc(g: Geometry, q, k_pool, v_pool, page_table, seq_lens,
+                                    scores, budget_pages: int, n_sink: int, n_local: int,
+                                    scale: float, n_splits: int, sel, sel_count, sink, out,
+                                    lse=None, stream=None) -> None:
+    """ps_select_sparse_decode with out, its split partials and arrival
+    counters in the library's fixed workspace (nothing allocated; calls that
+    overlap on one GPU race)."""
+    lib = _lib.load()
+    ns = int(n_splits)
+    rc = lib.ps_select_sparse_decode_noalloc(
+        *_select_decode_args(g, q, k_pool, v_pool, page_table, seq_lens, scores, budget_pages,
+                             n_sink, n_local, scale), ns,
+        _ptr(sel, "sel", torch.int32, (g.batch, g.num_kv_heads, budget_pages), optional=True),
+        _ptr(sel_count, "sel_count", torch.int32, (g.batch, g.num_kv_heads), optional=True),
+        _ptr(sink, "sink", torch.float32, (g.num_q_heads,), optional=True),
+        _ptr(out, "out", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
+        _ptr(lse, "lse", torch.float32, (g.batch, g.num_q_heads), optional=True),
+        _stream(stream))
+    _lib.check("ps_select_sparse_decode_noalloc", rc)
+
+
 def ps_select_topdelta_sparse_decode(g: Geometry, q, k_pool, v_pool, page_table, seq_lens,
                                      scores, budget_pages: int, n_sink: int, n_local: int,
                                      scale: float, delta: float, n_splits: int, sel, sel_count,

@@ -41,7 +41,7 @@ def test_library_exports_exactly_the_header():
 
 def test_abi_version_and_strerror():
     assert ops.ps_abi_version() >> 16 == 1
-    for code in range(0, -7, -1):
+    for code in range(0, -8, -1):
         assert ops.ps_strerror(code).startswith("PS_")
     assert "unknown" in ops.ps_strerror(17)
 
@@ -195,6 +195,35 @@ def test_fused_select_decode_validation():
         _lib.PS_OK
     assert call(g=geom(batch=0), splits=4, sink=X, out=X, lse=X, arr=X) == _lib.PS_OK
     assert call(g=geom(batch=0, kv_dtype=_lib.PS_F32), splits=4, out=X, arr=X) == _lib.PS_OK
+
+
+def test_noalloc_select_decode_validation():
+    """The entry point without allocation: the checks of the fused decode with
+    out set, out required, and PS_ERR_WORKSPACE (before any HIP call) when the
+    partials and counters would not fit in the library's 8 MiB array."""
+    lib = _lib.load()
+
+    def call(g=None, sel=X, cnt=X, budget=8, ns=1, nl=2, splits=2, scores=X, sink=None, out=X,
+             lse=None):
+        g = geom() if g is None else g
+        return lib.ps_select_sparse_decode_noalloc(g, X, X, X, X, X, scores, budget, ns, nl, 0.1,
+                                                   splits, sel, cnt, sink, out, lse, None)
+    assert call(out=None) == _lib.PS_ERR_NULL
+    assert call(scores=None) == _lib.PS_ERR_NULL
+    assert call(sel=None) == _lib.PS_ERR_NULL
+    assert call(budget=0) == _lib.PS_ERR_BUDGET
+    assert call(splits=9) == _lib.PS_ERR_BUDGET
+    assert call(g=geom(max_pages=8193)) == _lib.PS_ERR_UNSUPPORTED
+    assert call(g=geom(batch=0)) == _lib.PS_OK
+    assert call(g=geom(batch=0), sel=None, cnt=None, sink=X, lse=X) == _lib.PS_OK
+    # B*Hq*S*(D+2)*4 bytes of partials: 64 x 64 heads x 8 splits x 130 x 4 = 17 MB
+    big = geom(batch=64, num_q_heads=64, num_kv_heads=8, max_pages=64)
+    assert call(g=big, budget=64, splits=8) == _lib.PS_ERR_WORKSPACE
+    # one split needs no partials, only the counters
+    assert call(g=geom(batch=0, num_q_heads=64, num_kv_heads=8), budget=64, splits=1) == \
+        _lib.PS_OK
+    assert call(g=geom(batch=0, num_q_heads=64, num_kv_heads=8), budget=64, splits=4) == \
+        _lib.PS_OK
 
 
 def test_fused_topdelta_decode_validation():
