@@ -1,29 +1,30 @@
 """Decode-step benchmark of page-selected sparse decode on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--sets R]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--configs all|none|a,b]
 
 One step = one decode step of the whole hot path over one batch: refresh of
 each request's tail-page metadata, page scores, selection, sparse split-KV
-decode and merge (three launches: refresh+score, select+decode, merge). R
+decode and merge (two launches: refresh+score, then select+decode+merge). R
 independent input batches are drawn and the timed steps cycle through them,
 so each step reads data that the previous steps evicted from the 256 MB
 memory-side cache (the working set of one step is about 204 MB at the
-b32/64k workload). The timed steps are replays of one HIP graph holding one
-step per input set; one-graph-per-step and eager (uncaptured) step times are
-reported beside it. Before timing, one step is checked against the fp64
-oracle on sampled (request, KV head) units; no timing is printed if that
-check fails.
+b32/64k workload). The K timed steps are replays of one HIP graph holding
+one step per input set (K // R replays, plus K % R one-step graphs), each
+replay between its own HIP events: `value` is the median per-step time over
+those replays, `ms_per_step` the mean over the whole timed region. Before
+timing, one step is checked against the fp64 oracle on sampled (request, KV
+head) units; no timing is printed if that check fails.
 
-Printed: one JSON line with the step time (us per decode step), effective
-HBM bandwidth on algorithmic bytes, the score kernel's roofline (the kernel
-that moves the most bytes), per-kernel times, the in-house dense decode's
-step time and the speedup over it, and the oracle timed on host cores.
-With the default bf16 metadata the same inputs are also run with 8-bit
-metadata bounds (--meta-format fp8 makes that the timed step): its step
-time, score-launch time and parity against the oracle on the 8-bit bounds
-are reported under "metadata_fp8". They are also run with top-delta
-selection (--delta, default 5): step time, selection-launch time, pages kept
-and parity against the oracle's top-delta rule, under "topdelta_selection".
+Printed: one JSON line with the headline workload's step time (us per
+decode step), effective HBM bandwidth on algorithmic bytes, the score
+kernel's roofline (the kernel that moves the most bytes), per-kernel times,
+the in-house dense decode's step time and the speedup over it, the oracle
+timed on the host's cores (all of them, and one) and, under "configs", the
+same figures for every workload (each with its own parity gate). With the
+default bf16 metadata the headline inputs are also run with 8-bit metadata
+bounds (--meta-format fp8 makes that the timed step; "metadata_fp8") and
+with top-delta selection ("topdelta_selection"); "topdelta_binds" times
+top-delta selection on a workload where the threshold removes pages.
 """
 
 from __future__ import annotations
@@ -45,22 +46,37 @@ PEAK_HBM_GBPS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
+HEADLINE = "b32_64k_needles_local4"
+# every workload of the configuration list, in its order (the tiny workload is
+# measured at budget 8 and, as "tiny_dense", at budget 64 = every page)
+CONFIGS = ("tiny", "tiny_dense", "b8_16k_needles_sink_page", HEADLINE, "b16_32k_learned_sink",
+           "b64_ragged_4k_128k_shared_pool")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="b32_64k_needles_local4")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--configs", default="all",
+                    help="workloads measured besides the headline under 'configs': all, none, "
+                         "or a comma-separated list of names")
+    ap.add_argument("--config-steps", type=int, default=100,
+                    help="timed steps of each workload under 'configs'")
     ap.add_argument("--sets", type=int, default=None,
                     help="independent input batches cycled (default: enough that one pass "
                          "over them touches 3x the 256 MB memory-side cache, 4 to 32)")
     ap.add_argument("--dense-steps", type=int, default=20)
     ap.add_argument("--parity-units", type=int, default=6)
     ap.add_argument("--cpu-units", type=int, default=0,
-                    help="(request, KV head) units of one step the oracle is timed on "
-                         "(0: all of them)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
-                    help="CPU work the oracle timing aims for (whole passes, at most 3x)")
+                    help="(request, KV head) units of one headline step the oracle is timed "
+                         "on (0: all of them)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="wall time the headline oracle timing aims for (whole passes)")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="oracle worker processes (0: the host cores this process may use, "
+                         "at most 16)")
     ap.add_argument("--n-splits", type=int, default=None, help="override the sparse split count")
     ap.add_argument("--dense-splits", type=int, default=None,
                     help="override the dense split count")
@@ -70,9 +86,9 @@ def parse():
     ap.add_argument("--no-fp8-line", action="store_true",
                     help="skip the 8-bit metadata measurement of a default run")
     ap.add_argument("--no-topdelta-line", action="store_true",
-                    help="skip the top-delta selection measurement of a default run")
+                    help="skip the top-delta selection measurements of a default run")
     ap.add_argument("--delta", type=float, default=5.0,
-                    help="delta of the top-delta selection line (natural-log units)")
+                    help="delta of the top-delta selection lines (natural-log units)")
     ap.add_argument("--only-kernel", default=None,
                     help="profiling aid: after setup, launch only this stage --steps times "
                          "(score | step | copy: a 1 GiB device-to-device copy)")
@@ -246,7 +262,7 @@ def parity_gate(s, w, units, wl):
                                    hu["page_size"])
             mt = ref.pseudo_max(hu["q"][0].astype(np.float64), kf, hu["scale"])
             amb = ref.ambiguous_pages_topdelta(r["scores"], n, w.budget_pages, w.n_sink,
-                                               w.n_local, hu["scale"], mt, delta, rel=1e-5,
+                                               w.n_local, hu["scale"], mt, delta,
                                                mag=r["mag"])
         got = set(int(x) for x in sel[b, g, :k])
         want = set(int(x) for x in r["sel"])
@@ -267,49 +283,159 @@ def parity_gate(s, w, units, wl):
             "ambiguous_pages": n_amb, "units_differing_inside_band": n_diff}
 
 
-def cpu_baseline(s, w, units, wl, seconds):
-    """The fp64 oracle's decode step (score, select, attend; metadata given,
-    as on the device) timed on the host, single-threaded: whole steps over
-    the given units, repeated until about `seconds` of CPU work (at most three
-    times that), scaled to the whole step when the units are a sample."""
+# The oracle's step on the host. Every (request, KV head) unit of the timed
+# sample is laid out once in one shared-memory block (queries, the
+# precomputed metadata as on the device, the unit's K and V pages); worker
+# processes started fresh (spawn) attach to it and run the oracle's stages
+# 2-4 (scores, selection, attention) unit by unit.
+
+_ORACLE = {}
+
+
+def _oracle_attach(spec):
+    """Worker initialiser: attach to the shared block (the parent, which
+    shares its resource tracker with the workers, unlinks it)."""
+    from multiprocessing import shared_memory
+
+    _ORACLE.update(shm=shared_memory.SharedMemory(name=spec["name"]), spec=spec)
+
+
+def _oracle_view(i):
     import numpy as np
-    from threadpoolctl import threadpool_limits
+
+    spec, buf = _ORACLE["spec"], _ORACLE["shm"].buf
+    u = spec["units"][i]
+
+    def arr(key):
+        off, dtype, shape = u[key]
+        return np.ndarray(shape, dtype=dtype, buffer=buf, offset=off)
+    return u, arr
+
+
+def _oracle_unit(i):
+    """Stages 2-4 of the oracle for unit i: scores from the precomputed
+    metadata, selection, softmax attention of every query head of the group
+    over the kept pages (with the sink when there is one)."""
+    import numpy as np
+
+    import oracle as ref
+
+    spec = _ORACLE["spec"]
+    u, arr = _oracle_view(i)
+    qg, kmax, kmin = arr("q"), arr("kmax"), arr("kmin")
+    k_pool, v_pool = arr("k"), arr("v")
+    n = kmax.shape[0]
+    table = np.arange(n, dtype=np.int32)[None, :]
+    lens = np.array([u["len"]], dtype=np.int64)
+    _, sc = ref.unit_scores(qg, kmax, kmin)
+    sel, _, _ = ref.select_pages(sc, n, spec["budget"], spec["n_sink"], spec["n_local"])
+    keys = ref.gather_tokens(k_pool, spec["kv_dtype"], table, lens, 0, 0, sel, spec["page"])
+    vals = ref.gather_tokens(v_pool, spec["kv_dtype"], table, lens, 0, 0, sel, spec["page"])
+    sink = None if u["sink"] is None else u["sink"]
+    for h in range(qg.shape[0]):
+        ref.attend(qg[h], keys, vals, spec["scale"], None if sink is None else sink[h])
+    return 0
+
+
+def _oracle_pack(s, w, units, wl):
+    """Lay out the units' oracle inputs in one new shared-memory block.
+    Returns (SharedMemory, spec)."""
+    import numpy as np
+    from multiprocessing import shared_memory
 
     import oracle as ref
 
     inp = s["inp"]
-    prepared = []
+    records, arrays, off = [], [], 0
     for b, g in units:
         hu = unit_host(inp, b, g, wl)
         kmax, kmin = ref.unit_page_meta(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
                                         hu["seq_lens"], 0, 0, hu["page_size"])
-        prepared.append((hu, kmax, kmin))
-    passes, total = 0, 0.0
-    with threadpool_limits(limits=1):
-        while passes == 0 or (total < seconds and total < 3 * seconds - total / passes):
-            t0 = time.perf_counter()
-            for hu, kmax, kmin in prepared:
-                qg = hu["q"][0].astype(np.float64)
-                _, sc = ref.unit_scores(qg, kmax, kmin)
-                sel, _, _ = ref.select_pages(sc, kmax.shape[0], w.budget_pages, w.n_sink,
-                                             w.n_local)
-                keys = ref.gather_tokens(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
-                                         hu["seq_lens"], 0, 0, sel, hu["page_size"])
-                vals = ref.gather_tokens(hu["v_pool"], hu["kv_dtype"], hu["page_table"],
-                                         hu["seq_lens"], 0, 0, sel, hu["page_size"])
-                for i in range(w.group):
-                    sk = None if hu["sink"] is None else hu["sink"][i]
-                    ref.attend(qg[i], keys, vals, hu["scale"], sk)
-            total += time.perf_counter() - t0
-            passes += 1
+        rec = {"len": int(hu["seq_lens"][0]),
+               "sink": None if hu["sink"] is None else [float(x) for x in hu["sink"]]}
+        for key, a in (("q", hu["q"][0].astype(np.float64)), ("kmax", kmax), ("kmin", kmin),
+                       ("k", hu["k_pool"]), ("v", hu["v_pool"])):
+            a = np.ascontiguousarray(a)
+            rec[key] = (off, a.dtype.str, a.shape)
+            arrays.append((off, a))
+            off += (a.nbytes + 255) // 256 * 256
+        records.append(rec)
+    shm = shared_memory.SharedMemory(create=True, size=max(off, 1))
+    for o, a in arrays:
+        np.ndarray(a.shape, dtype=a.dtype, buffer=shm.buf, offset=o)[...] = a
+    spec = {"name": shm.name, "units": records, "budget": w.budget_pages, "n_sink": w.n_sink,
+            "n_local": w.n_local, "kv_dtype": w.kv_dtype, "page": w.page_size,
+            "scale": inp["scale"]}
+    return shm, spec
+
+
+def oracle_workers(requested):
+    """Worker processes for the oracle: the cores this process may run on,
+    at most 16 (the host share of one GPU), or the number requested."""
+    avail = len(os.sched_getaffinity(0))
+    return max(1, min(requested, avail) if requested > 0 else min(avail, 16))
+
+
+def cpu_baseline(s, w, units, wl, seconds, workers, single_core=True):
+    """The fp64 oracle's decode step (scores, selection, attention; metadata
+    given, as on the device) timed on the host: whole passes over the given
+    units, on `workers` processes (one BLAS thread each), repeated until about
+    `seconds` of wall time, scaled to the whole step when the units are a
+    sample; with single_core, the same passes in this process, one thread."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
+
+    shm, spec = _oracle_pack(s, w, units, wl)
     total_units = w.batch * w.num_kv_heads
-    us = total / passes * total_units / len(units) * 1e6
-    what = (f"all {total_units} (request, KV head) units of one step" if len(units) == total_units
-            else f"{len(units)} of {total_units} (request, KV head) units of one step, "
-                 f"scaled x{total_units}/{len(units)}")
-    return {"value": us, "unit": "us/decode-step", "cores": 1, "kind": "oracle",
-            "sample": f"{what}, {passes} passes ({total:.1f} s), single-threaded numpy fp64; "
-                      "metadata precomputed as on the device"}
+    scale = total_units / len(units)
+    out = {"unit": "us/decode-step", "kind": "oracle"}
+    try:
+        ctx = mp.get_context("spawn")
+        env_threads = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                      "MKL_NUM_THREADS")}
+        for k in env_threads:  # one BLAS thread per worker (inherited by the spawned children)
+            os.environ[k] = "1"
+        try:
+            with ctx.Pool(workers, initializer=_oracle_attach, initargs=(spec,)) as pool:
+                pool.map(_oracle_unit, range(len(units)), chunksize=1)  # warm-up pass
+                passes, total = 0, 0.0
+                while passes == 0 or total < seconds:
+                    t0 = time.perf_counter()
+                    pool.map(_oracle_unit, range(len(units)), chunksize=1)
+                    total += time.perf_counter() - t0
+                    passes += 1
+        finally:
+            for k, v in env_threads.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        out["value"] = total / passes * scale * 1e6
+        out["cores"] = workers
+        what = (f"all {total_units} (request, KV head) units of one step" if scale == 1
+                else f"{len(units)} of {total_units} (request, KV head) units of one step, "
+                     f"scaled x{total_units}/{len(units)}")
+        out["sample"] = (f"{what}; {passes} passes ({total:.1f} s wall) on {workers} worker "
+                         f"processes, numpy fp64, one BLAS thread each; metadata precomputed "
+                         f"as on the device")
+        if single_core:
+            _ORACLE.update(shm=shm, spec=spec)
+            with threadpool_limits(limits=1):
+                passes1, total1 = 0, 0.0
+                while passes1 == 0 or total1 < seconds / 2:
+                    t0 = time.perf_counter()
+                    for i in range(len(units)):
+                        _oracle_unit(i)
+                    total1 += time.perf_counter() - t0
+                    passes1 += 1
+            _ORACLE.clear()
+            out["single_core_value"] = total1 / passes1 * scale * 1e6
+            out["single_core_sample"] = f"the same units, {passes1} passes ({total1:.1f} s) in one thread"
+    finally:
+        shm.close()
+        shm.unlink()
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -344,6 +470,31 @@ def measured_traffic(workload: str):
 
 
 # ---------------------------------------------------------------------------
+
+
+def timed_steps(multi, singles, r, steps, torch):
+    """Time exactly `steps` decode steps: steps // r replays of the graph of
+    r steps, then steps % r one-step graphs, each replay between its own HIP
+    events on torch's current stream (the stream the graphs are launched on).
+    Returns (ms from the first event to the last, sorted per-step us of the
+    r-step replays, or of the one-step replays when there are none)."""
+    n_multi = steps // r
+    ev = []
+    for i in range(n_multi + steps % r):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        (multi if i < n_multi else singles[i - n_multi]).replay()
+        b.record()
+        ev.append((a, b, r if i < n_multi else 1))
+    torch.cuda.synchronize()
+    total = ev[0][0].elapsed_time(ev[-1][1])
+    sel = [e for e in ev if e[2] == r] if n_multi else ev
+    return total, sorted(a.elapsed_time(b) * 1e3 / k for a, b, k in sel)
+
+
+def pct(sorted_vals, p):
+    return sorted_vals[min(len(sorted_vals) - 1, int(round(p * (len(sorted_vals) - 1))))]
 
 
 def main():
@@ -413,37 +564,20 @@ def main():
         graphs[i % len(graphs)].replay()
     multi.replay()
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    gpu_ms, per_step = timed_steps(multi, graphs, len(sets), args.steps, torch)
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    ms_per_step = gpu_ms / args.steps
+    step_us = pct(per_step, 0.5)  # the median replay
+    print(f"# timed {args.steps} steps: median {step_us:.2f} us/step, mean "
+          f"{ms_per_step * 1e3:.2f}", file=sys.stderr, flush=True)
+
+    # -- warm steps: as many steps per graph as the timed graph on ONE input
+    # set, whose working set then stays in the memory-side cache ("warm",
+    # reported as such)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps // len(sets)):
-        multi.replay()
-    for i in range(args.steps % len(sets)):
-        graphs[i].replay()
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    gpu_ms = e0.elapsed_time(e1)
-    ms_per_step = gpu_ms / args.steps
-    print(f"# timed {args.steps} steps: {ms_per_step * 1e3:.2f} us/step", file=sys.stderr,
-          flush=True)
 
-    # -- distribution over replays, and warm steps ------------------------------
-    # per-replay times of the multi-step graph (median, p10, p90 per step), and
-    # the same number of steps per graph on ONE input set, whose working set
-    # then stays in the memory-side cache ("warm", reported as such)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(max(args.steps // len(sets), 1))]
-    for a, b in ev:
-        a.record()
-        multi.replay()
-        b.record()
-    torch.cuda.synchronize()
-    per_step = sorted(a.elapsed_time(b) * 1e3 / len(sets) for a, b in ev)
-
-    def pct(p):
-        return per_step[min(len(per_step) - 1, int(round(p * (len(per_step) - 1))))]
     def same_set(_):  # as many steps per graph as the timed graph, one input set
         for _ in sets:
             run_sparse_step(s0)
@@ -626,7 +760,6 @@ def main():
     kv_b = acc.selected_kv_bytes(lens, lists, w.head_dim, elem, w.page_size)
     touched = meta_b + kv_b
     dense_b = acc.dense_kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
-    step_us = ms_per_step * 1e3
     eff_gbps = touched / (step_us * 1e-6) / 1e9
     # the dominant kernel: the step's score launch with the last-page
     # refresh: metadata of every page read, one fp32 score per page written,
@@ -683,8 +816,11 @@ def main():
         "copy_gbps_read_plus_write": round(copy_gbps, 1),
         "read_stream_gbps": round(read_gbps, 1),
         "timed_wall_ms": round(wall_ms, 3),
+        "mean_us_per_step": round(ms_per_step * 1e3, 3),
         "eager_us_per_step": round(eager_us, 3),
-        "us_per_step_p10_p50_p90": [round(pct(0.1), 3), round(pct(0.5), 3), round(pct(0.9), 3)],
+        "us_per_step_p10_p50_p90": [round(pct(per_step, 0.1), 3), round(pct(per_step, 0.5), 3),
+                                    round(pct(per_step, 0.9), 3)],
+        "timed_replays": len(per_step),
         "warm_same_set_us_per_step": round(warm_us, 3),
         "one_step_per_graph_us_per_step": round(one_graph_us, 3),
         "parity": parity,
@@ -707,13 +843,220 @@ def main():
     if args.meta_format == "kv" and not args.no_topdelta_line:
         print("# top-delta selection", file=sys.stderr, flush=True)
         result["topdelta_selection"] = topdelta_line(args, w, sets, step_us, torch, wl, ps)
+    workers = oracle_workers(args.cpu_workers)
     if not args.no_cpu_baseline:
         print("# cpu baseline", file=sys.stderr, flush=True)
         n_units = w.batch * w.num_kv_heads
         result["cpu_baseline"] = cpu_baseline(
             s0, w, sample_units(w, args.cpu_units if args.cpu_units > 0 else n_units), wl,
-            args.cpu_seconds)
+            args.cpu_seconds, workers)
+    headline_entry = {
+        "us_per_step_median": result["value"],
+        "us_per_step_p10_p50_p90": result["us_per_step_p10_p50_p90"],
+        "effective_hbm_gbps": result["effective_hbm_gbps"],
+        "hbm_frac_of_peak": result["hbm_frac_of_peak"], "touched_bytes": touched,
+        "dense_us_per_step": result["dense_us_per_step"],
+        "speedup_vs_dense": result["speedup_vs_dense"], "parity": parity,
+        "n_splits": w.n_splits, "input_sets": len(sets), "path": path,
+        "selection_in_decode_us": result["selection_in_decode_us"],
+        "oracle_us_per_step": (result["cpu_baseline"]["value"]
+                               if "cpu_baseline" in result else None),
+        "oracle_cores": workers if "cpu_baseline" in result else None}
+    # free the headline's input sets before the other workloads
+    del sets, graphs, multi, dgraphs
+    if "s0" in locals():
+        del s0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    names = [n for n in CONFIGS if n != w.name] if args.configs == "all" else (
+        [] if args.configs == "none" else [n for n in args.configs.split(",") if n])
+    configs = {w.name: headline_entry}
+    for name in names:
+        print(f"# config {name}", file=sys.stderr, flush=True)
+        configs[name] = config_line(args, wl.WORKLOADS[name], workers, torch, wl, ps, acc)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    result["configs"] = {n: configs[n] for n in CONFIGS if n in configs}
+    for n in configs:
+        if n not in result["configs"]:
+            result["configs"][n] = configs[n]
+    if args.meta_format == "kv" and not args.no_topdelta_line:
+        print("# top-delta where the threshold binds", file=sys.stderr, flush=True)
+        result["topdelta_binds"] = topdelta_binds_line(args, torch, wl, ps, acc)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     print(json.dumps(result), flush=True)
+
+
+def dense_parity(s, w, units, wl):
+    """The dense path (budget covering every page) against exact softmax
+    attention of the oracle; returns a summary dict, raises on failure."""
+    import numpy as np
+
+    import oracle as ref
+
+    gate = 2e-3 if w.kv_dtype == "bf16" else 1e-5
+    out = s["step"].out.cpu().double().numpy()
+    worst = 0.0
+    for b, g in units:
+        hu = unit_host(s["inp"], b, g, wl)
+        for i in range(w.group):
+            o, _ = ref.full_decode(hu, 0, i)
+            e = float(np.linalg.norm(out[b, g * w.group + i] - o) / np.linalg.norm(o))
+            worst = max(worst, e)
+    if not worst <= gate:
+        raise AssertionError(f"parity: dense rel-L2 {worst} above {gate}")
+    return {"units_checked": len(units), "max_rel_l2": worst, "gate": gate,
+            "oracle": "exact softmax attention over every valid token"}
+
+
+def config_line(args, w, workers, torch, wl, ps, acc):
+    """One workload under "configs": its parity gate (every unit of the small
+    workloads, sampled units of the others), then its step timed as the
+    headline's (one graph of one step per input set, each replay between its
+    own events, median), the touched bytes and their rate, the dense decode
+    and the speedup over it, and the oracle on the host's cores (sampled
+    units, scaled to the step)."""
+    import numpy as np
+
+    r = default_sets(w, "kv", acc)
+    sets = [make_set(w, w.seed + 17 * i, torch, wl, ps) for i in range(r)]
+    torch.cuda.synchronize()
+    s0 = sets[0]
+    path = s0["step"].path_for(s0["inp"]["seq_lens_host"])
+    run = run_sparse_step if path == "sparse" else run_dense_step
+    n_units = w.batch * w.num_kv_heads
+    units = sample_units(w, n_units if n_units <= 16 else args.parity_units)
+    run(s0)
+    torch.cuda.synchronize()
+    parity = (parity_gate(s0, w, units, wl) if path == "sparse"
+              else dense_parity(s0, w, units, wl))
+    graphs = [capture(run, s, torch) for s in sets]
+
+    def all_sets(_):
+        for s in sets:
+            run(s)
+    multi = capture(all_sets, None, torch)
+    for i in range(args.warmup):
+        graphs[i % r].replay()
+    multi.replay()
+    torch.cuda.synchronize()
+    total_ms, per = timed_steps(multi, graphs, r, args.config_steps, torch)
+    step_us = pct(per, 0.5)
+
+    lens = [int(x) for x in s0["inp"]["seq_lens_host"]]
+    elem = 2 if w.kv_dtype == "bf16" else 4
+    if path == "sparse":
+        meta_b = acc.meta_bytes(lens, w.num_kv_heads, w.head_dim, elem, w.page_size)
+        sel_h = s0["step"].sel.cpu().numpy()
+        lists = {(b, g): list(sel_h[b, g]) for b in range(w.batch)
+                 for g in range(w.num_kv_heads)}
+        kv_b = acc.selected_kv_bytes(lens, lists, w.head_dim, elem, w.page_size)
+    else:
+        meta_b, kv_b = 0, acc.dense_kv_bytes(lens, w.num_kv_heads, w.head_dim, elem)
+    touched = meta_b + kv_b
+    gbps = touched / (step_us * 1e-6) / 1e9
+    out = {"us_per_step_median": round(step_us, 3),
+           "us_per_step_p10_p50_p90": [round(pct(per, 0.1), 3), round(pct(per, 0.5), 3),
+                                       round(pct(per, 0.9), 3)],
+           "mean_us_per_step": round(total_ms * 1e3 / args.config_steps, 3),
+           "timed_steps": args.config_steps, "timed_replays": len(per),
+           "touched_bytes": touched,
+           "touched_bytes_split": {"metadata": meta_b, "kv": kv_b},
+           "effective_hbm_gbps": round(gbps, 1),
+           "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+           "path": path, "n_splits": w.n_splits if path == "sparse" else w.dense_splits,
+           "input_sets": r, "parity": parity,
+           "config": {"batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                      "head_dim": w.head_dim,
+                      "context": w.context if w.context else list(w.ctx_range),
+                      "budget_pages": w.budget_pages, "n_sink_pages": w.n_sink,
+                      "n_local_pages": w.n_local, "needles": w.needles,
+                      "kv_storage": w.kv_dtype, "learned_sink": w.sink_logits,
+                      "permuted_pool": w.permuted_pool}}
+    if w.kv_dtype == "bf16" or path == "sparse":
+        out["launches"] = (step_launches(s0["step"]) if path == "sparse"
+                           else ["ps_full_decode", "ps_combine"])
+    if path == "sparse":  # the in-house dense decode on the same inputs
+        dgraphs = [capture(run_dense_step, s, torch) for s in sets]
+        for i in range(3):
+            dgraphs[i % r].replay()
+        torch.cuda.synchronize()
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record()
+        for i in range(args.dense_steps):
+            dgraphs[i % r].replay()
+        d1.record()
+        torch.cuda.synchronize()
+        dense_us = d0.elapsed_time(d1) / args.dense_steps * 1e3
+        out["dense_us_per_step"] = round(dense_us, 3)
+        out["speedup_vs_dense"] = round(dense_us / step_us, 3)
+        del dgraphs
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(s0, w, sample_units(w, min(n_units, 16)), wl, 3.0, workers,
+                          single_core=False)
+        out["oracle_us_per_step"] = round(cb["value"], 1)
+        out["oracle_cores"] = cb["cores"]
+        out["oracle_sample"] = cb["sample"]
+    del sets, graphs, multi, s0
+    return out
+
+
+def topdelta_binds_line(args, torch, wl, ps, acc):
+    """Top-delta selection on a workload where the threshold removes pages
+    (one query head per KV head; a forced sink page whose keys follow the
+    needle recipe, so the pseudo-max over the forced tokens is high): parity
+    against the oracle's top-delta rule, the step timed as the headline's,
+    the pages kept per unit against the budget, the bytes actually read, and
+    the top-k step on the same inputs."""
+    import numpy as np
+
+    w = wl.TOPDELTA_BINDS
+    r = default_sets(w, "kv", acc)
+    base = [make_set(w, w.seed + 17 * i, torch, wl, ps) for i in range(r)]
+    sets = [dict(s, step=ps.DecodeStep(s["g"], w.budget_pages, w.n_sink, w.n_local, w.n_splits,
+                                       w.dense_splits, s["inp"]["scale"], delta=args.delta))
+            for s in base]
+    run_sparse_step(sets[0])
+    torch.cuda.synchronize()
+    parity = parity_gate(sets[0], w, sample_units(w, args.parity_units), wl)
+    kept = sets[0]["step"].sel_count.cpu().numpy()
+    res = {}
+    for kind, ss in (("topdelta", sets), ("topk", base)):
+        graphs = [capture(run_sparse_step, s, torch) for s in ss]
+
+        def all_sets(_, ss=ss):
+            for s in ss:
+                run_sparse_step(s)
+        multi = capture(all_sets, None, torch)
+        for i in range(args.warmup):
+            graphs[i % r].replay()
+        torch.cuda.synchronize()
+        _, per = timed_steps(multi, graphs, r, args.config_steps, torch)
+        res[kind] = pct(per, 0.5)
+        del graphs, multi
+    for s in sets:  # leave every set as one whole top-delta step leaves it
+        run_sparse_step(s)
+    torch.cuda.synchronize()
+    lens = [int(x) for x in sets[0]["inp"]["seq_lens_host"]]
+    meta_b = acc.meta_bytes(lens, w.num_kv_heads, w.head_dim, 2, w.page_size)
+    sel_h = sets[0]["step"].sel.cpu().numpy()
+    lists = {(b, g): list(sel_h[b, g][:int(kept[b, g])]) for b in range(w.batch)
+             for g in range(w.num_kv_heads)}
+    kv_b = acc.selected_kv_bytes(lens, lists, w.head_dim, 2, w.page_size)
+    out = {"workload": w.name, "delta": args.delta,
+           "us_per_step_median": round(res["topdelta"], 3),
+           "topk_us_per_step_median": round(res["topk"], 3),
+           "kept_pages_per_unit": {"mean": round(float(np.mean(kept)), 2), "min": int(kept.min()),
+                                   "max": int(kept.max()), "budget": w.budget_pages},
+           "touched_bytes": meta_b + kv_b,
+           "touched_bytes_split": {"metadata": meta_b, "selected_kv": kv_b},
+           "effective_hbm_gbps": round((meta_b + kv_b) / (res["topdelta"] * 1e-6) / 1e9, 1),
+           "launches": step_launches(sets[0]["step"]),
+           "parity": dict(parity, oracle="top-delta rule")}
+    del sets, base
+    return out
 
 
 def step_launches(step):

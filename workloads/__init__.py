@@ -24,6 +24,11 @@ Recipe (the same for every workload, see each Workload for its sizes):
 * Slots past the end of a partial last page hold the sentinel 1.0e4 in K and
   V, so a consumer that does not mask them produces visibly wrong results.
 * Sink logits (``sink_logits``) ~ N(0, 1), one per query head, fp32.
+* ``sink_page_needle``: the first page of every (request, KV head) gets the
+  needle recipe too, so that the first (sink) page holds the keys the
+  queries align with, as an attention sink does; with a forced sink page this
+  gives the top-delta threshold (the pseudo-max over the forced pages) a high
+  value.
 """
 
 from __future__ import annotations
@@ -57,6 +62,7 @@ class Workload:
     sink_logits: bool = False
     permuted_pool: bool = False
     max_pages: Optional[int] = None        # page-table row stride (default: max pages)
+    sink_page_needle: bool = False         # page 0 of every (b, g) follows the needle recipe
     seed: int = 0
     n_splits: int = 8                      # split-KV count of the sparse decode
     dense_splits: int = 32                 # split-KV count of the dense decode
@@ -86,7 +92,18 @@ RAGGED = Workload("b64_ragged_4k_128k_shared_pool", batch=64, num_q_heads=28, nu
                   head_dim=128, ctx_range=(4096, 131072), budget_pages=128, needles=8,
                   permuted_pool=True, max_pages=8192, seed=1005, n_splits=1, dense_splits=64)
 
-WORKLOADS = {w.name: w for w in (TINY, TINY_DENSE, B8_16K, B32_64K, SINK, RAGGED)}
+# The headline shape with one query head per KV head, a forced sink page whose
+# keys follow the needle recipe and the last 4 pages forced: the top-delta
+# threshold (pseudo-max over the forced pages' tokens, minus delta) then
+# removes the random pages and keeps the needles (used for the top-delta
+# measurement where the threshold binds).
+TOPDELTA_BINDS = Workload("b32_64k_g1_sink_needle_topdelta", batch=32, num_q_heads=2,
+                          num_kv_heads=2, head_dim=128, context=65536, budget_pages=128,
+                          n_sink=1, n_local=4, needles=8, sink_page_needle=True, seed=1006,
+                          n_splits=4, dense_splits=64)
+
+WORKLOADS = {w.name: w for w in (TINY, TINY_DENSE, B8_16K, B32_64K, SINK, RAGGED,
+                                 TOPDELTA_BINDS)}
 
 
 def _pages(n_tokens: int, page: int) -> int:
@@ -164,6 +181,8 @@ def make_inputs(w: Workload, device="cpu", seed: Optional[int] = None):
                 chosen = sorted(int(x) for x in rng.choice(pool, size=k, replace=False))
                 needle_pages[(b, g)] = chosen
                 sites += [(b, g, p) for p in chosen]
+                if w.sink_page_needle and n >= 1 and int(lens[b]) >= ps:
+                    sites.append((b, g, 0))
         if sites:
             qbar = q.view(b_, hkv, grp, d).mean(dim=2)                      # [B, Hkv, D]
             qhat = math.sqrt(d) * qbar / qbar.norm(dim=-1, keepdim=True)
