@@ -53,7 +53,17 @@ hipError_t launch_select_decode(const Shape& s, const float* q, const void* k_po
 // Fixed size of the library's own workspace array (ps_noalloc.hip), and the
 // bytes a scratch-backed selecting decode of this shape needs in it.
 constexpr int64_t kNoAllocScratchBytes = int64_t(8) << 20;
-int64_t noalloc_scratch_bytes(const Shape& s, int n_splits);
+constexpr int64_t scratch_align(int64_t x) { return (x + 255) & ~int64_t(255); }
+// Scratch layout: arrivals [B, Hkv] int32, then part_ml [B, Hq, S, 2] and
+// part_acc [B, Hq, S, D] fp32, each at a 256-byte boundary. -1 when a size
+// does not fit in 64 bits (the caller validated the geometry first).
+inline int64_t noalloc_scratch_bytes(const Shape& s, int n_splits) {
+  const int64_t units = (int64_t)s.batch * s.hkv;
+  const int64_t rows = (int64_t)s.batch * s.hq * n_splits;
+  if (units < 0 || rows < 0 || rows > (INT64_MAX / 4) / (s.head_dim + 2)) return -1;
+  return scratch_align(units * 4) + scratch_align(rows * 2 * 4) +
+         scratch_align(rows * s.head_dim * 4);
+}
 
 // launch_select_decode with the partials and arrival counters in that array
 // (the merged output is always written).

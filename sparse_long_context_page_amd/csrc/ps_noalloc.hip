@@ -53,19 +53,7 @@ __global__ void zero_counters(int32_t* __restrict__ p, int n) {
   if (i < n) p[i] = 0;
 }
 
-constexpr int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
-
 }  // namespace
-
-// Scratch layout: arrivals [B, Hkv] int32, then part_ml [B, Hq, S, 2] and
-// part_acc [B, Hq, S, D] fp32, each at a 256-byte boundary. -1 when a size
-// does not fit in 64 bits (the caller validated the geometry first).
-int64_t noalloc_scratch_bytes(const Shape& s, int n_splits) {
-  const int64_t units = (int64_t)s.batch * s.hkv;
-  const int64_t rows = (int64_t)s.batch * s.hq * n_splits;
-  if (units < 0 || rows < 0 || rows > (INT64_MAX / 4) / (s.head_dim + 2)) return -1;
-  return align256(units * 4) + align256(rows * 2 * 4) + align256(rows * s.head_dim * 4);
-}
 
 hipError_t launch_select_decode_noalloc(const Shape& s, const float* q, const void* k_pool,
                                         const void* v_pool, const int32_t* page_table,
@@ -83,8 +71,9 @@ hipError_t launch_select_decode_noalloc(const Shape& s, const float* q, const vo
   const int64_t units = (int64_t)s.batch * s.hkv;
   const int64_t rows = (int64_t)s.batch * s.hq * n_splits;
   int32_t* arrivals = reinterpret_cast<int32_t*>(p);
-  float* part_ml = reinterpret_cast<float*>(p + align256(units * 4));
-  float* part_acc = reinterpret_cast<float*>(p + align256(units * 4) + align256(rows * 2 * 4));
+  float* part_ml = reinterpret_cast<float*>(p + scratch_align(units * 4));
+  float* part_acc =
+      reinterpret_cast<float*>(p + scratch_align(units * 4) + scratch_align(rows * 2 * 4));
   if (n_splits > 1) {
     const int n = (int)units;  // units * 4 <= kNoAllocScratchBytes
     hipLaunchKernelGGL(zero_counters, dim3((n + 255) / 256), dim3(256), 0, st, arrivals, n);
