@@ -83,6 +83,13 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--meta-format", default="kv", choices=("kv", "fp8"),
                     help="page metadata: in the key dtype (kv) or 8-bit E4M3 bounds (fp8)")
+    ap.add_argument("--meta-layout", default=None, choices=("physical", "logical"),
+                    help="page metadata per physical page or per request in logical page "
+                         "order (the score then reads no page table); default: each "
+                         "workload's measured choice")
+    ap.add_argument("--fp8-meta-layout", default="physical", choices=("physical", "logical"),
+                    help="metadata layout of the 8-bit metadata line (physical measured "
+                         "faster with 8-bit codes)")
     ap.add_argument("--no-fp8-line", action="store_true",
                     help="skip the 8-bit metadata measurement of a default run")
     ap.add_argument("--no-topdelta-line", action="store_true",
@@ -121,9 +128,15 @@ def default_sets(w, meta_format, acc):
     return int(min(32, max(4, math.ceil(3 * MALL_BYTES / max(touched, 1)))))
 
 
-def make_set(w, seed, torch, wl, ps, meta_format="kv", inp=None):
+def layout_of(args, w):
+    """The metadata layout a workload is run with: the command line's, else
+    the workload's own (measured) choice."""
+    return args.meta_layout or w.meta_layout
+
+
+def make_set(w, seed, torch, wl, ps, meta_format="kv", inp=None, meta_layout="physical"):
     inp = wl.make_inputs(w, device="cuda", seed=seed) if inp is None else inp
-    g = ps.Geometry.of(inp["q"], inp["k_pool"], inp["page_table"], meta_format)
+    g = ps.Geometry.of(inp["q"], inp["k_pool"], inp["page_table"], meta_format, meta_layout)
     meta = ps.build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
     step = ps.DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
                          inp["scale"])
@@ -527,7 +540,8 @@ def main():
     if args.sets is None:
         args.sets = default_sets(w, args.meta_format, acc)
     print(f"# setup {w.name}: {args.sets} input sets", file=sys.stderr, flush=True)
-    sets = [make_set(w, w.seed + 17 * i, torch, wl, ps, args.meta_format)
+    sets = [make_set(w, w.seed + 17 * i, torch, wl, ps, args.meta_format,
+                     meta_layout=layout_of(args, w))
             for i in range(args.sets)]
     torch.cuda.synchronize()
 
@@ -774,7 +788,8 @@ def main():
     dec_key = "select_decode" if fused else "sparse_decode"
     decode_gbps = kv_b / (kern_us[dec_key] * 1e-6) / 1e9
 
-    traffic = measured_traffic(w.name + ("_fp8meta" if args.meta_format == "fp8" else ""))
+    traffic = measured_traffic(w.name + ("_fp8meta" if args.meta_format == "fp8" else "") +
+                               ("_logicalmeta" if layout_of(args, w) == "logical" else ""))
     result = {
         "metric": METRIC,
         "value": round(step_us, 3),
@@ -794,6 +809,7 @@ def main():
                    "page_size": w.page_size, "budget_pages": w.budget_pages,
                    "n_sink_pages": w.n_sink, "n_local_pages": w.n_local, "needles": w.needles,
                    "kv_storage": w.kv_dtype, "metadata": args.meta_format,
+                   "metadata_layout": layout_of(args, w),
                    "n_splits": w.n_splits, "input_sets": len(sets),
                    "path": path,
                    "graph_captured": f"{len(sets)} steps (one per input set) per graph"},
@@ -920,7 +936,8 @@ def config_line(args, w, workers, torch, wl, ps, acc):
     import numpy as np
 
     r = default_sets(w, "kv", acc)
-    sets = [make_set(w, w.seed + 17 * i, torch, wl, ps) for i in range(r)]
+    sets = [make_set(w, w.seed + 17 * i, torch, wl, ps, meta_layout=layout_of(args, w))
+            for i in range(r)]
     torch.cuda.synchronize()
     s0 = sets[0]
     path = s0["step"].path_for(s0["inp"]["seq_lens_host"])
@@ -973,7 +990,8 @@ def config_line(args, w, workers, torch, wl, ps, acc):
                       "budget_pages": w.budget_pages, "n_sink_pages": w.n_sink,
                       "n_local_pages": w.n_local, "needles": w.needles,
                       "kv_storage": w.kv_dtype, "learned_sink": w.sink_logits,
-                      "permuted_pool": w.permuted_pool}}
+                      "permuted_pool": w.permuted_pool,
+                      "metadata_layout": layout_of(args, w)}}
     if w.kv_dtype == "bf16" or path == "sparse":
         out["launches"] = (step_launches(s0["step"]) if path == "sparse"
                            else ["ps_full_decode", "ps_combine"])
@@ -1014,7 +1032,8 @@ def topdelta_binds_line(args, torch, wl, ps, acc):
 
     w = wl.TOPDELTA_BINDS
     r = default_sets(w, "kv", acc)
-    base = [make_set(w, w.seed + 17 * i, torch, wl, ps) for i in range(r)]
+    base = [make_set(w, w.seed + 17 * i, torch, wl, ps, meta_layout=layout_of(args, w))
+            for i in range(r)]
     sets = [dict(s, step=ps.DecodeStep(s["g"], w.budget_pages, w.n_sink, w.n_local, w.n_splits,
                                        w.dense_splits, s["inp"]["scale"], delta=args.delta))
             for s in base]
@@ -1140,7 +1159,9 @@ def fp8_line(args, w, sets, step_us_kv, torch, wl, ps, acc):
     """The same inputs with 8-bit metadata bounds: parity against the oracle
     scoring the 8-bit bounds, then the step timed as the main one (one graph
     of one step per input set) and the refresh+score launch on its own."""
-    sets8 = [make_set(w, None, torch, wl, ps, "fp8", inp=s["inp"]) for s in sets]
+    sets8 = [make_set(w, None, torch, wl, ps, "fp8", inp=s["inp"],
+                      meta_layout=args.fp8_meta_layout)
+             for s in sets]
     run_sparse_step(sets8[0])
     torch.cuda.synchronize()
     parity = parity_gate(sets8[0], w, sample_units(w, args.parity_units), wl)
@@ -1202,6 +1223,7 @@ def fp8_line(args, w, sets, step_us_kv, torch, wl, ps, acc):
             "refresh_score_gbps": round(gbps, 1),
             "refresh_score_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
             "refresh_score_algorithmic_bytes": dom_b,
+            "metadata_layout": args.fp8_meta_layout,
             "parity": dict(parity, oracle="scores on the 8-bit bounds")}
 
 

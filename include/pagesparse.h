@@ -80,6 +80,23 @@ typedef enum {
   PS_META_FP8_E4M3 = 1
 } ps_meta_format;
 
+/* Where a page's metadata lives.
+ *   PS_META_PHYSICAL  with the physical page: meta [num_phys_pages, Hkv, 2, D],
+ *                     the entry of (b, p) at page_table[b, p] (pages shared
+ *                     by several requests share their metadata).
+ *   PS_META_LOGICAL   per request, in logical page order: meta
+ *                     [B, Hkv, max_pages, 2, D], the entry of (b, g, p) at
+ *                     [b, g, p]. The page score then reads the metadata
+ *                     without going through the page table (one dependent
+ *                     memory round trip fewer before its first page);
+ *                     entries at p >= n_b are neither written nor used. A
+ *                     page shared by several requests has one entry per
+ *                     request. */
+typedef enum {
+  PS_META_PHYSICAL = 0,
+  PS_META_LOGICAL = 1
+} ps_meta_layout;
+
 /* Geometry shared by every call of one decode step.
  *   batch           B  >= 0 (0: validate, enqueue nothing, return PS_OK)
  *   num_q_heads     Hq >= 1, a multiple of num_kv_heads, with
@@ -93,7 +110,9 @@ typedef enum {
  *   meta_format     element type of the metadata (ps_meta_format); entry
  *                   points that do not read metadata ignore it. A value
  *                   outside ps_meta_format is PS_ERR_SHAPE in every entry
- *                   point                                                */
+ *                   point
+ *   meta_layout     where the metadata of a page lives (ps_meta_layout);
+ *                   a value outside it is PS_ERR_SHAPE in every entry point */
 typedef struct {
   int32_t batch;
   int32_t num_q_heads;
@@ -104,11 +123,14 @@ typedef struct {
   int64_t num_phys_pages;
   int32_t kv_dtype;    /* ps_dtype */
   int32_t meta_format; /* ps_meta_format */
+  int32_t meta_layout; /* ps_meta_layout */
 } ps_geom;
 
 /* Array layouts (all contiguous, row-major):
  *   k_pool, v_pool [num_phys_pages, Hkv, page_size, D]    kv_dtype
- *   meta           [num_phys_pages, Hkv, 2, D]            kv_dtype (PS_META_KV) or uint8 codes
+ *   meta           [num_phys_pages, Hkv, 2, D] (PS_META_PHYSICAL) or
+ *                  [B, Hkv, max_pages, 2, D] (PS_META_LOGICAL)
+ *                                                          kv_dtype (PS_META_KV) or uint8 codes
  *                                                          (PS_META_FP8_E4M3); [..,0,:] = kmax,
  *                                                          [..,1,:] = kmin
  *   page_table     [B, max_pages]  int32, logical page -> physical page; entries
@@ -129,9 +151,10 @@ typedef struct {
  * skipping": each page keeps the elementwise min and max of its keys.)
  * For every request b, KV head g and logical page p in
  * [begin_b, min(begin_b + n_pages, n_b)) with begin_b = page_begin[b] (or 0
- * when page_begin is NULL):
- *   meta[page_table[b,p], g, 0, d] = max over the page's valid tokens t of K[t, d]
- *   meta[page_table[b,p], g, 1, d] = min over the same tokens.
+ * when page_begin is NULL), with M = meta[page_table[b,p], g] (physical
+ * layout) or meta[b, g, p] (logical layout):
+ *   M[0, d] = max over the page's valid tokens t of K[t, d]
+ *   M[1, d] = min over the same tokens.
  * The result is exact (a selection among stored values); with
  * PS_META_FP8_E4M3 it is kmax rounded up and kmin rounded down to E4M3. Passing
  * page_begin[b] = n_b - 1 and n_pages = 1 refreshes only the tail page, the
@@ -139,7 +162,8 @@ typedef struct {
  * n_pages >= 1 (use max_pages for a full build).
  * Device preconditions: 1 <= seq_lens[b] <= max_pages*page_size;
  * 0 <= page_table[b,p] < num_phys_pages for p < n_b; 0 <= page_begin[b];
- * no physical page is mapped by two (b, p) within the rebuilt ranges. */
+ * no physical page is mapped by two (b, p) within the rebuilt ranges
+ * (physical layout). */
 int ps_build_page_meta(const ps_geom* geom, const void* k_pool, const int32_t* page_table,
                        const int32_t* seq_lens, const int32_t* page_begin, int32_t n_pages,
                        void* meta, void* stream);
@@ -149,7 +173,8 @@ int ps_build_page_meta(const ps_geom* geom, const void* k_pool, const int32_t* p
  * every key of the page.) For every b, KV head g and logical page p < n_b:
  *   scores[b,g,p] = max over the group's query heads h of
  *                   sum_d max(q[b,h,d]*kmin_d, q[b,h,d]*kmax_d)
- * with (kmax, kmin) = meta[page_table[b,p], g]. Unscaled; the max over the
+ * with (kmax, kmin) the page's metadata (meta[page_table[b,p], g], or
+ * meta[b, g, p] in the logical layout). Unscaled; the max over the
  * group makes one page list per KV head admissible for all its heads.
  * Computed in fp32 as sum_d (max(q,0)*kmax_d + min(q,0)*kmin_d) with exact
  * products and a fixed summation order (bf16 metadata: on the matrix cores,
@@ -170,8 +195,8 @@ int ps_score_pages(const ps_geom* geom, const float* q, const void* meta,
  * appends to each request's last page only.) meta is read for every page and
  * written for page n_b - 1 of every request.
  * Host checks: those of ps_score_pages.
- * Device preconditions: as ps_build_page_meta and ps_score_pages; no two
- * requests share their last physical page. */
+ * Device preconditions: as ps_build_page_meta and ps_score_pages; in the
+ * physical layout, no two requests share their last physical page. */
 int ps_refresh_score_pages(const ps_geom* geom, const float* q, const void* k_pool, void* meta,
                            const int32_t* page_table, const int32_t* seq_lens, float* scores,
                            void* stream);

@@ -42,6 +42,8 @@ ENTRY_POINTS = (
 
 PS_META_KV = 0
 PS_META_FP8_E4M3 = 1
+PS_META_PHYSICAL = 0
+PS_META_LOGICAL = 1
 
 
 class PsGeom(ctypes.Structure):
@@ -55,6 +57,7 @@ class PsGeom(ctypes.Structure):
         ("num_phys_pages", ctypes.c_int64),
         ("kv_dtype", ctypes.c_int32),
         ("meta_format", ctypes.c_int32),
+        ("meta_layout", ctypes.c_int32),
     ]
 
 

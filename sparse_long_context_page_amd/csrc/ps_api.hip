@@ -32,6 +32,8 @@ bool prod_ok(std::initializer_list<int64_t> xs, int64_t* out) {
 int check_geom(const ps_geom* g, ps::Shape* s) {
   if (!g) return PS_ERR_NULL;
   if (g->meta_format != PS_META_KV && g->meta_format != PS_META_FP8_E4M3) return PS_ERR_SHAPE;
+  if (g->meta_layout != PS_META_PHYSICAL && g->meta_layout != PS_META_LOGICAL)
+    return PS_ERR_SHAPE;
   if (g->batch < 0 || g->num_q_heads < 1 || g->num_kv_heads < 1 || g->head_dim < 1 ||
       g->page_size < 1 || g->max_pages < 1 || g->num_phys_pages < 1)
     return PS_ERR_SHAPE;
@@ -48,6 +50,10 @@ int check_geom(const ps_geom* g, ps::Shape* s) {
   // pool bytes, metadata bytes, per-request page-table, score and query sizes
   if (!prod_ok({g->num_phys_pages, g->num_kv_heads, g->page_size, g->head_dim, elem}, &t))
     return PS_ERR_OVERFLOW;
+  // logical-layout metadata [B, Hkv, max_pages, 2, D]
+  if (g->meta_layout == PS_META_LOGICAL &&
+      !prod_ok({g->batch, g->num_kv_heads, g->max_pages, 2, g->head_dim, elem}, &t))
+    return PS_ERR_OVERFLOW;
   if (!prod_ok({g->batch, g->max_pages}, &t)) return PS_ERR_OVERFLOW;
   if (!prod_ok({g->batch, g->num_kv_heads, g->max_pages, 4}, &t)) return PS_ERR_OVERFLOW;
   if (!prod_ok({g->max_pages, g->num_kv_heads}, &t) || t > INT32_MAX) return PS_ERR_OVERFLOW;
@@ -62,6 +68,7 @@ int check_geom(const ps_geom* g, ps::Shape* s) {
   s->num_phys_pages = g->num_phys_pages;
   s->kv_bf16 = g->kv_dtype == PS_BF16;
   s->meta8 = g->meta_format == PS_META_FP8_E4M3;
+  s->meta_logical = g->meta_layout == PS_META_LOGICAL;
   return PS_OK;
 }
 
@@ -317,4 +324,4 @@ PS_API const char* ps_strerror(int status) {
   }
 }
 
-PS_API int ps_abi_version(void) { return (1 << 16) | 7; }  // 1.7: decode without allocation
+PS_API int ps_abi_version(void) { return (2 << 16) | 0; }  // 2.0: ps_geom.meta_layout

@@ -12,6 +12,7 @@ struct Shape {
   int64_t num_phys_pages;
   int kv_bf16;  // 1: bf16 pools, 0: fp32 pools
   int meta8;    // 1: 8-bit metadata bounds, 0: metadata in the pool dtype
+  int meta_logical;  // 1: metadata [B, Hkv, max_pages, 2, D], 0: [P_phys, Hkv, 2, D]
 };
 
 hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int32_t* page_table,

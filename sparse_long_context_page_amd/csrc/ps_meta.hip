@@ -4,7 +4,8 @@
 // One wavefront per (request, logical page, KV head) folds the page
 // (PageFold), and two lane groups write the kmax and kmin rows: in the key
 // dtype, or as 8-bit codes with kmax rounded up and kmin rounded down
-// (fp8_e4m3_directed).
+// (fp8_e4m3_directed). The rows go to the physical page's slot
+// [phys, g] or to the request's logical slot [b, g, p].
 #include "ps_launch.h"
 #include "ps_meta.h"
 
@@ -16,7 +17,7 @@ template <typename T, int D, bool META8>
 __global__ __launch_bounds__(kMetaWaves * kWave) void build_page_meta_kernel(
     const T* __restrict__ k_pool, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ page_begin, int n_pages,
-    int batch, int hkv, int max_pages, int items_per_req, void* __restrict__ meta) {
+    int batch, int hkv, int max_pages, int items_per_req, int logical, void* __restrict__ meta) {
   using L = RowLayout<T, D>;
   constexpr int V = L::kVec;
   const int wave = threadIdx.x / kWave;
@@ -43,7 +44,9 @@ __global__ __launch_bounds__(kMetaWaves * kWave) void build_page_meta_kernel(
   float mx[V], mn[V];
   pf.fold(cnt, lane, mx, mn);
   if (r0 < 2) {
-    const int64_t off = ((int64_t)phys * hkv + g) * 2 * D + r0 * D + c * V;
+    const int64_t slot = logical ? ((int64_t)b * hkv + g) * max_pages + p
+                                 : (int64_t)phys * hkv + g;
+    const int64_t off = slot * 2 * D + r0 * D + c * V;
     if constexpr (META8 && V == 8) {
       *reinterpret_cast<uint2*>(static_cast<uint8_t*>(meta) + off) =
           r0 == 0 ? fp8_pack8(mx, true) : fp8_pack8(mn, false);
@@ -69,14 +72,16 @@ hipError_t launch_build_page_meta(const Shape& s, const void* k_pool, const int3
     PS_WITH_KV(s.kv_bf16, s.head_dim, {
       hipLaunchKernelGGL((build_page_meta_kernel<TElem, kD, true>), grid, block, 0, st,
                          static_cast<const TElem*>(k_pool), page_table, seq_lens, page_begin,
-                         pages, s.batch, s.hkv, s.max_pages, items_per_req, meta);
+                         pages, s.batch, s.hkv, s.max_pages, items_per_req, s.meta_logical,
+                         meta);
     });
     return hipGetLastError();
   }
   PS_WITH_KV(s.kv_bf16, s.head_dim, {
     hipLaunchKernelGGL((build_page_meta_kernel<TElem, kD, false>), grid, block, 0, st,
                        static_cast<const TElem*>(k_pool), page_table, seq_lens, page_begin,
-                       pages, s.batch, s.hkv, s.max_pages, items_per_req, meta);
+                       pages, s.batch, s.hkv, s.max_pages, items_per_req, s.meta_logical,
+                         meta);
   });
   return hipGetLastError();
 }

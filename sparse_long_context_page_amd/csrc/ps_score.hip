@@ -19,6 +19,11 @@
 // folds them with the lane layout of the scoring (lane = (row, column
 // vector)), writes the page's metadata and scores the page from the folded
 // registers.
+//
+// LOGICAL: the metadata sit in the request's logical page order
+// ([B, Hkv, max_pages, 2, D]), so a page's metadata are read at an address
+// known from the page index alone; only a refresh reads the page table (for
+// the last page's keys).
 #include <algorithm>
 #include <type_traits>
 
@@ -42,7 +47,7 @@ struct ScoreCfg {
 // META8: the metadata are 8-bit codes (4 per lane and bound), widened
 // exactly to fp32. meta is not restrict-qualified: a refresh writes the last
 // pages' metadata through meta_out, which is the same buffer.
-template <typename T, int D, int G, bool REFRESH, bool META8>
+template <typename T, int D, int G, bool REFRESH, bool META8, bool LOGICAL>
 __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
     const float* __restrict__ q, const void* meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
@@ -87,7 +92,7 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
     const int p = p0 + it * C::kPagesPerLoad + slot;
-    phys_it[it] = page_table[(int64_t)b * max_pages + min(p, np - 1)];
+    phys_it[it] = LOGICAL ? 0 : page_table[(int64_t)b * max_pages + min(p, np - 1)];
   }
   PageFold<T, D> tail_keys;
   int64_t tail_base = g;
@@ -102,8 +107,10 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   MV vmax[kScoreIters], vmin[kScoreIters];
 #pragma unroll
   for (int it = 0; it < kScoreIters; ++it) {
-    const uint8_t* src = static_cast<const uint8_t*>(meta) +
-                         (((int64_t)phys_it[it] * hkv + g) * 2 * D + c * V) * EB;
+    const int64_t mslot =
+        LOGICAL ? (int64_t)unit * max_pages + min(p0 + it * C::kPagesPerLoad + slot, np - 1)
+                : (int64_t)phys_it[it] * hkv + g;
+    const uint8_t* src = static_cast<const uint8_t*>(meta) + (mslot * 2 * D + c * V) * EB;
     vmax[it] = *reinterpret_cast<const MV*>(src);
     vmin[it] = *reinterpret_cast<const MV*>(src + D * EB);
   }
@@ -132,7 +139,8 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
   float tx[V], tn[V];
   if constexpr (REFRESH) {
     tail_keys.fold(len - tail * kPage, lane, tx, tn);
-    uint8_t* dst = static_cast<uint8_t*>(meta_out) + (tail_base * 2 * D + slot * D + c * V) * EB;
+    const int64_t tslot = LOGICAL ? (int64_t)unit * max_pages + tail : tail_base;
+    uint8_t* dst = static_cast<uint8_t*>(meta_out) + (tslot * 2 * D + slot * D + c * V) * EB;
     if constexpr (META8) {
       const uint32_t cx = fp8_pack4(tx, true), cn = fp8_pack4(tn, false);
       if (has_tail && slot < 2) *reinterpret_cast<uint32_t*>(dst) = slot == 0 ? cx : cn;
@@ -191,6 +199,10 @@ __global__ __launch_bounds__(kScoreWaves * kWave) void score_pages_kernel(
 // its own slice of the queries in registers (no LDS, no barrier), reads its
 // table entries once up front, and keeps the metadata of the next two tiles
 // in flight while the current tile is scored.
+// LOGICAL: the tiles' metadata are read at the request's logical slots, with
+// no page table in front of them; a refresh then folds the last page after
+// the wavefront's other tiles (its keys' physical page is the only table
+// entry read), so the first tile waits for one memory round trip, not two.
 // META8: the metadata are 8-bit codes, widened exactly to bf16 in registers
 // before the same contraction. Each lane then takes one contiguous quarter
 // of the page's coordinates (block kb of lane group kgrp holds coordinates
@@ -228,7 +240,7 @@ constexpr int kMeta8InFlight = 3;
 // it to meta_out and scores the page with it. NF: tiles of metadata in flight
 // per wavefront.
 // meta is not restrict-qualified: meta_out (a refresh) is the same buffer.
-template <int D, int G, bool REFRESH, bool META8, int NF>
+template <int D, int G, bool REFRESH, bool META8, bool LOGICAL, int NF>
 __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel(
     const float* __restrict__ q, const void* meta,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens, int hkv,
@@ -280,7 +292,7 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   int phys[kMaxTiles];
 #pragma unroll
   for (int t = 0; t < kMaxTiles; ++t)
-    phys[t] = row[min(tile_page(t) + col, (int64_t)max_pages - 1)];
+    phys[t] = LOGICAL ? 0 : row[min(tile_page(t) + col, (int64_t)max_pages - 1)];
   __builtin_amdgcn_sched_barrier(0);
   const float* qh = q + ((int64_t)b * hkv * G + g * G + min(col, G - 1)) * D;
   float4 qv[KB][2];
@@ -297,13 +309,17 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
   const int n_tiles = wu < n_all ? min(tiles_per_wave, ceil_div(n_all - wu, w_u)) : 0;
   // A page past the request reads the metadata of physical page 0 (shared by
   // all such lanes, so it stays in cache) and its score is not written; an
-  // entry of a live page is clamped into the pool.
+  // entry of a live page is clamped into the pool. Logical layout: such a
+  // page reads its own slot (in the buffer, contents unused: a B column only
+  // reaches its own page's output).
 #pragma unroll
   for (int t = 0; t < kMaxTiles; ++t)
     phys[t] = tile_page(t) + col < np ? min(max(phys[t], 0), last_phys) : 0;
   auto load = [&](int t, uint4 (&bx)[ML], uint4 (&bn)[ML]) {
-    const uint8_t* src = static_cast<const uint8_t*>(meta) +
-                         (((int64_t)phys[t] * hkv + g) * 2 * D + coord(kgrp, 0)) * EB;
+    const int64_t mslot =
+        LOGICAL ? (int64_t)unit * max_pages + min(tile_page(t) + col, (int64_t)max_pages - 1)
+                : (int64_t)phys[t] * hkv + g;
+    const uint8_t* src = static_cast<const uint8_t*>(meta) + (mslot * 2 * D + coord(kgrp, 0)) * EB;
 #pragma unroll
     for (int i = 0; i < ML; ++i) {
       // bf16: block i's 8 coordinates; 8-bit: blocks 2i and 2i+1
@@ -312,19 +328,23 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
       bn[i] = ld16(src + D * EB + off);
     }
   };
-  // The last page's keys: read by every wavefront of a refresh launch, the
-  // one holding the page reading its own, the others page 0 of this KV head
-  // (the same rows for all, so they stay in cache). Requested before the
-  // metadata tiles, so waiting for them waits for no tile, and with no branch
-  // around the loads or the fold (a branch made the first tile wait for every
-  // load in flight: the compiler could not tell whether the key registers,
-  // reused after the fold, still had loads pending).
+  // Physical layout: the last page's keys are read by every wavefront of a
+  // refresh launch, the one holding the page reading its own, the others
+  // page 0 of this KV head (the same rows for all, so they stay in cache).
+  // Requested before the metadata tiles, so waiting for them waits for no
+  // tile, and with no branch around the loads or the fold (a branch made the
+  // first tile wait for every load in flight: the compiler could not tell
+  // whether the key registers, reused after the fold, still had loads
+  // pending).
   const int tail = np - 1;
   const bool has_tail = REFRESH && n_tiles > 0 && (tail / 16) % w_u == wu;
   const int col_tail = tail % 16;
   PageFold<bf16_t, D> tail_keys;
   int phys_tail = 0;
-  if constexpr (REFRESH) {
+  if constexpr (REFRESH && LOGICAL) {
+    // the last page's physical page, for its keys (read before the last tile)
+    phys_tail = has_tail ? min(max(row[max(tail, 0)], 0), last_phys) : 0;
+  } else if constexpr (REFRESH) {
     int pt = phys[0];
 #pragma unroll
     for (int t = 1; t < kMaxTiles; ++t) pt = t == (tail / 16) / w_u ? phys[t] : pt;
@@ -365,17 +385,16 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
     }
   }
 
-  // The last page's metadata: folded from its keys (by every wavefront of a
-  // refresh launch), written out and kept in LDS for the last tile by the
-  // wavefront holding the page.
-  if constexpr (REFRESH) {
+  // The last page's metadata: folded from its keys, written out and kept in
+  // LDS for the last tile by the wavefront holding the page.
+  const int64_t tail_slot =
+      LOGICAL ? (int64_t)unit * max_pages + tail : (int64_t)phys_tail * hkv + g;
+  auto publish_tail = [&](const float (&mx)[8], const float (&mn)[8]) {
     using LP = RowLayout<bf16_t, D>;
-    float mx[8], mn[8];
-    tail_keys.fold(len - tail * kPage, lane, mx, mn);
     const int r0 = lane / LP::kLanesPerRow;
     const int c = lane % LP::kLanesPerRow;
     if (has_tail && r0 < 2) {
-      const int64_t off = ((int64_t)phys_tail * hkv + g) * 2 * D + r0 * D + c * 8;
+      const int64_t off = tail_slot * 2 * D + r0 * D + c * 8;
       if constexpr (META8) {
         const uint2 codes = r0 == 0 ? fp8_pack8(mx, true) : fp8_pack8(mn, false);
         *reinterpret_cast<uint2*>(static_cast<uint8_t*>(meta_out) + off) = codes;
@@ -389,12 +408,30 @@ __global__ __launch_bounds__(kMfmaWaves * kWave, 2) void score_pages_mfma_kernel
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  // Physical layout: every wavefront of a refresh launch folds (its tiles'
+  // table round trip has to pass anyway; the fold needs no branch).
+  if constexpr (REFRESH && !LOGICAL) {
+    float mx[8], mn[8];
+    tail_keys.fold(len - tail * kPage, lane, mx, mn);
+    publish_tail(mx, mn);
   }
 
   // 3. per tile: one accumulator per (sign, 32-coordinate block), lo then mid
   // then hi, summed in a fixed tree; max over the group's heads
   float* out = scores + (int64_t)unit * max_pages;
   auto score_tile = [&](int t, const uint4 (&bx_in)[ML], const uint4 (&bn_in)[ML], bool last) {
+    if constexpr (REFRESH && LOGICAL) {
+      // Logical layout: only the wavefront holding the last page reads its
+      // keys and folds them, just before its last tile (folding earlier, with
+      // the keys held in registers or staged in LDS, measured no faster).
+      if (last && has_tail) {
+        tail_keys.load(k_pool + ((int64_t)phys_tail * hkv + g) * kPage * D, lane);
+        float mx[8], mn[8];
+        tail_keys.fold(len - tail * kPage, lane, mx, mn);
+        publish_tail(mx, mn);
+      }
+    }
     uint4 bx[KB], bn[KB];
 #pragma unroll
     for (int i = 0; i < ML; ++i) {
@@ -506,15 +543,20 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
     const dim3 grid((unsigned)blocks);
     const int last_phys = (int)std::min<int64_t>(s.num_phys_pages - 1, 0x7fffffff);
     const bf16_t* kp = static_cast<const bf16_t*>(k_pool);
-#define PS_SCORE_MFMA(DD, RR, M8)                                                          \
-  hipLaunchKernelGGL((score_pages_mfma_kernel<DD, kG, RR, M8, M8 ? kMeta8InFlight : 2>),      \
+#define PS_SCORE_MFMA(DD, RR, M8, LG)                                                      \
+  hipLaunchKernelGGL((score_pages_mfma_kernel<DD, kG, RR, M8, LG, M8 ? kMeta8InFlight : 2>),  \
                      grid, block, 0, st, q, meta,                                            \
                      page_table, seq_lens, s.hkv, s.max_pages, last_phys, chunks, tpw,       \
                      scores, kp, meta_out)
-#define PS_SCORE_MFMA_M(DD, RR)             \
-  do {                                      \
-    if (s.meta8) PS_SCORE_MFMA(DD, RR, true);  \
-    else PS_SCORE_MFMA(DD, RR, false);         \
+#define PS_SCORE_MFMA_L(DD, RR, M8)                       \
+  do {                                                    \
+    if (s.meta_logical) PS_SCORE_MFMA(DD, RR, M8, true);  \
+    else PS_SCORE_MFMA(DD, RR, M8, false);                \
+  } while (0)
+#define PS_SCORE_MFMA_M(DD, RR)                  \
+  do {                                           \
+    if (s.meta8) PS_SCORE_MFMA_L(DD, RR, true);  \
+    else PS_SCORE_MFMA_L(DD, RR, false);         \
   } while (0)
     PS_WITH_GROUP(s.group, {
       if (s.head_dim == 64) {
@@ -526,15 +568,21 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
       }
     });
 #undef PS_SCORE_MFMA_M
+#undef PS_SCORE_MFMA_L
 #undef PS_SCORE_MFMA
     return hipGetLastError();
   }
   // fp32 K: the vector-ALU kernel (fp32 or 8-bit metadata)
   const float* kp = static_cast<const float*>(k_pool);
-#define PS_SCORE_F32_LAUNCH(DD, RR, M8)                                                     \
-  hipLaunchKernelGGL((score_pages_kernel<float, DD, kG, RR, M8>), grid, block, 0, st, q,    \
+#define PS_SCORE_F32_LAUNCH_L(DD, RR, M8, LG)                                               \
+  hipLaunchKernelGGL((score_pages_kernel<float, DD, kG, RR, M8, LG>), grid, block, 0, st, q, \
                      meta, page_table, seq_lens, s.hkv, s.max_pages, chunks, scores, kp,   \
                      meta_out)
+#define PS_SCORE_F32_LAUNCH(DD, RR, M8)                                    \
+  do {                                                                     \
+    if (s.meta_logical) PS_SCORE_F32_LAUNCH_L(DD, RR, M8, true);           \
+    else PS_SCORE_F32_LAUNCH_L(DD, RR, M8, false);                         \
+  } while (0)
 #define PS_SCORE_F32(DD)                                                                    \
   do {                                                                                      \
     const int per_block = ScoreCfg<float, DD>::kPagesPerBlock;                              \
@@ -558,6 +606,7 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
     PS_SCORE_F32(128);
 #undef PS_SCORE_F32
 #undef PS_SCORE_F32_LAUNCH
+#undef PS_SCORE_F32_LAUNCH_L
   return hipGetLastError();
 }
 

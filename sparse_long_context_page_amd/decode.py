@@ -135,8 +135,8 @@ class DecodeStep:
 
 
 def build_meta(geom: Geometry, k_pool, page_table, seq_lens, stream=None) -> torch.Tensor:
-    """Allocate and fill the metadata pool for every mapped page."""
-    meta = torch.empty((geom.num_phys_pages, geom.num_kv_heads, 2, geom.head_dim),
-                       device=k_pool.device, dtype=geom.meta_dtype)
+    """Allocate and fill the metadata of every page of every request (per
+    physical page or per logical slot, as geom.meta_layout says)."""
+    meta = torch.empty(ops.meta_shape(geom), device=k_pool.device, dtype=geom.meta_dtype)
     ops.ps_build_page_meta(geom, k_pool, page_table, seq_lens, None, geom.max_pages, meta, stream)
     return meta

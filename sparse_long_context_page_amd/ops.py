@@ -19,6 +19,7 @@ from . import _lib
 
 KV_DTYPES = {torch.bfloat16: _lib.PS_BF16, torch.float32: _lib.PS_F32}
 META_FORMATS = {"kv": _lib.PS_META_KV, "fp8": _lib.PS_META_FP8_E4M3}
+META_LAYOUTS = {"physical": _lib.PS_META_PHYSICAL, "logical": _lib.PS_META_LOGICAL}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -32,6 +33,9 @@ class Geometry:
     kv_dtype: torch.dtype = torch.bfloat16
     page_size: int = 16
     meta_format: str = "kv"  # "kv": metadata in kv_dtype; "fp8": 8-bit E4M3 bounds
+    # "physical": metadata per physical page [P_phys, Hkv, 2, D];
+    # "logical": per request in logical page order [B, Hkv, max_pages, 2, D]
+    meta_layout: str = "physical"
 
     @property
     def meta_dtype(self) -> torch.dtype:
@@ -47,18 +51,22 @@ class Geometry:
             raise TypeError(f"unsupported kv dtype {self.kv_dtype}")
         if self.meta_format not in META_FORMATS:
             raise ValueError(f"unknown metadata format {self.meta_format!r}")
+        if self.meta_layout not in META_LAYOUTS:
+            raise ValueError(f"unknown metadata layout {self.meta_layout!r}")
         return _lib.PsGeom(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim,
                            self.page_size, self.max_pages, self.num_phys_pages,
-                           KV_DTYPES[self.kv_dtype], META_FORMATS[self.meta_format])
+                           KV_DTYPES[self.kv_dtype], META_FORMATS[self.meta_format],
+                           META_LAYOUTS[self.meta_layout])
 
     @staticmethod
     def of(q: torch.Tensor, k_pool: torch.Tensor, page_table: torch.Tensor,
-           meta_format: str = "kv") -> "Geometry":
+           meta_format: str = "kv", meta_layout: str = "physical") -> "Geometry":
         b, hq, d = q.shape
         p_phys, hkv, ps, d2 = k_pool.shape
         if d2 != d or page_table.shape[0] != b:
             raise ValueError("q, k_pool and page_table disagree on batch or head_dim")
-        return Geometry(b, hq, hkv, d, page_table.shape[1], p_phys, k_pool.dtype, ps, meta_format)
+        return Geometry(b, hq, hkv, d, page_table.shape[1], p_phys, k_pool.dtype, ps, meta_format,
+                        meta_layout)
 
 
 def _stream(stream) -> int:
@@ -89,7 +97,9 @@ def _pool_shape(g: Geometry):
     return (g.num_phys_pages, g.num_kv_heads, g.page_size, g.head_dim)
 
 
-def _meta_shape(g: Geometry):
+def meta_shape(g: Geometry):
+    if g.meta_layout == "logical":
+        return (g.batch, g.num_kv_heads, g.max_pages, 2, g.head_dim)
     return (g.num_phys_pages, g.num_kv_heads, 2, g.head_dim)
 
 
@@ -101,7 +111,7 @@ def ps_build_page_meta(g: Geometry, k_pool, page_table, seq_lens, page_begin, n_
         _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
         _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
         _ptr(page_begin, "page_begin", torch.int32, (g.batch,), optional=True), int(n_pages),
-        _ptr(meta, "meta", g.meta_dtype, _meta_shape(g)), _stream(stream))
+        _ptr(meta, "meta", g.meta_dtype, meta_shape(g)), _stream(stream))
     _lib.check("ps_build_page_meta", rc)
 
 
@@ -109,7 +119,7 @@ def ps_score_pages(g: Geometry, q, meta, page_table, seq_lens, scores, stream=No
     lib = _lib.load()
     rc = lib.ps_score_pages(
         g.c(), _ptr(q, "q", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
-        _ptr(meta, "meta", g.meta_dtype, _meta_shape(g)),
+        _ptr(meta, "meta", g.meta_dtype, meta_shape(g)),
         _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
         _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
         _ptr(scores, "scores", torch.float32, (g.batch, g.num_kv_heads, g.max_pages)),
@@ -125,7 +135,7 @@ def ps_refresh_score_pages(g: Geometry, q, k_pool, meta, page_table, seq_lens, s
     rc = lib.ps_refresh_score_pages(
         g.c(), _ptr(q, "q", torch.float32, (g.batch, g.num_q_heads, g.head_dim)),
         _ptr(k_pool, "k_pool", g.kv_dtype, _pool_shape(g)),
-        _ptr(meta, "meta", g.meta_dtype, _meta_shape(g)),
+        _ptr(meta, "meta", g.meta_dtype, meta_shape(g)),
         _ptr(page_table, "page_table", torch.int32, (g.batch, g.max_pages)),
         _ptr(seq_lens, "seq_lens", torch.int32, (g.batch,)),
         _ptr(scores, "scores", torch.float32, (g.batch, g.num_kv_heads, g.max_pages)),

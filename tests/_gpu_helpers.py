@@ -23,8 +23,24 @@ def gate(w) -> float:
     return BF16_GATE if w.kv_dtype == "bf16" else F32_GATE
 
 
-def geometry(inp, meta_format="kv") -> Geometry:
-    return Geometry.of(inp["q"], inp["k_pool"], inp["page_table"], meta_format)
+def geometry(inp, meta_format="kv", meta_layout="physical") -> Geometry:
+    return Geometry.of(inp["q"], inp["k_pool"], inp["page_table"], meta_format, meta_layout)
+
+
+def unit_meta(inp, meta, b, g):
+    """The metadata of the n_b pages of (request b, KV head g), [n_b, 2, D],
+    from either layout: [P_phys, Hkv, 2, D] (gathered through the page
+    table) or [B, Hkv, max_pages, 2, D] (the request's own slots)."""
+    n = int(inp["n_pages_host"][b])
+    if meta.dim() == 5:
+        return meta[b, g, :n]
+    return meta[inp["page_table"][b, :n].long().to(meta.device), g]
+
+
+def bits(t):
+    """Integer view of a tensor, so that equality is bit equality (NaN
+    patterns in never-written slots included)."""
+    return t.view({1: torch.uint8, 2: torch.int16, 4: torch.int32}[t.element_size()])
 
 
 def unit_host(inp, b, g, meta_format="kv"):
@@ -53,10 +69,10 @@ def unit_host(inp, b, g, meta_format="kv"):
 
 
 def run_step(inp, budget=None, n_splits=None, n_sink=None, n_local=None, sink="input",
-             meta_format="kv"):
+             meta_format="kv", meta_layout="physical"):
     """Metadata build + sparse step on the device; returns host copies."""
     w = inp["workload"]
-    g = geometry(inp, meta_format)
+    g = geometry(inp, meta_format, meta_layout)
     budget = w.budget_pages if budget is None else budget
     step = DecodeStep(g, budget, w.n_sink if n_sink is None else n_sink,
                       w.n_local if n_local is None else n_local,
@@ -83,9 +99,7 @@ def run_step(inp, budget=None, n_splits=None, n_sink=None, n_local=None, sink="i
 
 def check_meta_unit(inp, meta, hu, b, g):
     """Device metadata of one unit equals the oracle's, value for value."""
-    n = int(inp["n_pages_host"][b])
-    phys = inp["page_table"][b, :n].long()
-    dev = wl.kv_bits_numpy(meta[phys, g])  # [n, 2, D]
+    dev = wl.kv_bits_numpy(unit_meta(inp, meta, b, g))  # [n, 2, D]
     kmax, kmin = ref.unit_page_meta(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
                                     hu["seq_lens"], 0, 0, hu["page_size"])
     got_max = ref.widen(np.ascontiguousarray(dev[:, 0]), hu["kv_dtype"])

@@ -144,7 +144,7 @@ int main() {
       ++failures;
     }
   }
-  if ((ps_abi_version() >> 16) != 1) ++failures;
+  if ((ps_abi_version() >> 16) != 2) ++failures;
   if (failures) return 1;
   printf("abi driver: all checks passed\n");
   return 0;

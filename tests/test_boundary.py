@@ -40,7 +40,7 @@ def test_library_exports_exactly_the_header():
 
 
 def test_abi_version_and_strerror():
-    assert ops.ps_abi_version() >> 16 == 1
+    assert ops.ps_abi_version() >> 16 == 2
     for code in range(0, -8, -1):
         assert ops.ps_strerror(code).startswith("PS_")
     assert "unknown" in ops.ps_strerror(17)
@@ -49,7 +49,7 @@ def test_abi_version_and_strerror():
 def geom(**kw):
     base = dict(batch=2, num_q_heads=12, num_kv_heads=2, head_dim=128, page_size=16,
                 max_pages=64, num_phys_pages=128, kv_dtype=_lib.PS_BF16,
-                meta_format=_lib.PS_META_KV)
+                meta_format=_lib.PS_META_KV, meta_layout=_lib.PS_META_PHYSICAL)
     base.update(kw)
     return _lib.PsGeom(**base)
 
@@ -64,6 +64,12 @@ def score(g):
 @pytest.mark.parametrize("kw,code", [
     (dict(meta_format=2), _lib.PS_ERR_SHAPE),
     (dict(meta_format=-1), _lib.PS_ERR_SHAPE),
+    (dict(meta_layout=2), _lib.PS_ERR_SHAPE),
+    (dict(meta_layout=-1), _lib.PS_ERR_SHAPE),
+    # logical metadata B * Hkv * max_pages * 2 * D * 4 bytes beyond int64 (the
+    # physical layout of the same geometry is in range)
+    (dict(batch=(1 << 31) - 1, num_q_heads=8, num_kv_heads=8, max_pages=(1 << 26) - 1,
+          kv_dtype=_lib.PS_F32, meta_layout=_lib.PS_META_LOGICAL), _lib.PS_ERR_OVERFLOW),
     (dict(batch=-1), _lib.PS_ERR_SHAPE),
     (dict(num_q_heads=0), _lib.PS_ERR_SHAPE),
     (dict(num_q_heads=13), _lib.PS_ERR_SHAPE),
@@ -86,11 +92,12 @@ def test_geometry_validation(kw, code):
     assert score(geom(**kw)) == code
 
 
+@pytest.mark.parametrize("layout", [_lib.PS_META_PHYSICAL, _lib.PS_META_LOGICAL])
 @pytest.mark.parametrize("kv", [_lib.PS_BF16, _lib.PS_F32])
-def test_fp8_metadata_geometry_accepted(kv):
-    """8-bit metadata with bf16 or fp32 pools passes the geometry checks (a
-    call with batch 0 validates and enqueues nothing)."""
-    g = geom(meta_format=_lib.PS_META_FP8_E4M3, batch=0, kv_dtype=kv)
+def test_fp8_metadata_geometry_accepted(kv, layout):
+    """8-bit metadata with bf16 or fp32 pools, in either layout, passes the
+    geometry checks (a call with batch 0 validates and enqueues nothing)."""
+    g = geom(meta_format=_lib.PS_META_FP8_E4M3, batch=0, kv_dtype=kv, meta_layout=layout)
     lib = _lib.load()
     assert lib.ps_score_pages(g, X, X, X, X, X, None) == _lib.PS_OK
     assert lib.ps_build_page_meta(g, X, X, X, None, 4, X, None) == _lib.PS_OK

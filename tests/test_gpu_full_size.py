@@ -1,5 +1,6 @@
 """HIP path vs the fp64 oracle at the full sizes of the four bf16 workloads,
-in the launch configuration the benchmark times (the workload's split counts):
+in the launch configuration the benchmark times (the workload's split counts
+and metadata layout; 8-bit metadata in the physical layout):
 
   b8_16k_needles_sink_page        8 x 16k tokens, GQA 6, sink page kept
   b32_64k_needles_local4          32 x 64k tokens, GQA 6, last 4 pages kept
@@ -16,7 +17,9 @@ gate on sampled units and on every unit whose list differs from the oracle's
 inside the band (there on the device's list). Properties that hold at any size
 (count, order, padding, forced pages) are checked on every unit. The dense
 decode is checked against exact softmax attention on sampled units of every
-workload.
+workload. The step as the benchmark runs it (the last pages' metadata
+refreshed inside the score launch, from stale values) and the step with the
+metadata in the other layout both equal the checked step bit for bit.
 """
 
 import concurrent.futures as cf
@@ -28,13 +31,15 @@ import torch
 
 import oracle as ref
 import workloads as wl
-from _gpu_helpers import (SCORE_REL, check_meta_unit, check_selection, check_unit_outputs,
-                          gate, geometry, rel_l2, run_step, score_rel_err, unit_host)
+from _gpu_helpers import (SCORE_REL, bits, check_meta_unit, check_selection,
+                          check_unit_outputs, gate, geometry, rel_l2, run_step, score_rel_err,
+                          unit_host, unit_meta)
 from sparse_long_context_page_amd import DecodeStep
 
 pytestmark = pytest.mark.gpu
 
 FULL = [wl.B8_16K, wl.B32_64K, wl.SINK, wl.RAGGED]
+FP8_LAYOUT = "physical"  # the layout of the benchmark's 8-bit metadata line
 
 
 def _sample_units(w, k=3):
@@ -50,7 +55,7 @@ def full(request):
     w = request.param
     print(f"\n[full-size] generating {w.name}", flush=True)
     inp = wl.make_inputs(w, device="cuda")
-    res = run_step(inp)
+    res = run_step(inp, meta_layout=w.meta_layout)
     yield w, inp, res
     del inp, res
     torch.cuda.empty_cache()
@@ -83,7 +88,7 @@ def _unit_keys(inp, meta, b, g):
         "k_pool": wl.kv_bits_numpy(inp["k_pool"][phys, g:g + 1]),
         "page_table": np.arange(n, dtype=np.int32)[None, :],
         "seq_lens": inp["seq_lens"][b:b + 1].cpu().numpy(),
-        "meta_dev": wl.kv_bits_numpy(meta[phys, g]),
+        "meta_dev": wl.kv_bits_numpy(unit_meta(inp, meta, b, g)),
         "n": n,
     }
 
@@ -143,6 +148,48 @@ def test_every_unit_matches_oracle_selection(full):
           f"lists differing inside the band {len(differ)}", flush=True)
 
 
+def _same_step(inp, res, other, what):
+    """Scores of every mapped page, page lists, outputs and log-sum-exps of
+    two runs of the step equal bit for bit."""
+    for b, n in enumerate(inp["n_pages_host"]):
+        n = int(n)
+        assert np.array_equal(res["scores"][b, :, :n].view(np.int32),
+                              other["scores"][b, :, :n].view(np.int32)), (what, b)
+    assert np.array_equal(res["sel"], other["sel"]), what
+    assert np.array_equal(res["sel_count"], other["sel_count"]), what
+    assert np.array_equal(res["out"], other["out"]), what
+    assert np.array_equal(res["lse"], other["lse"]), what
+
+
+def test_refresh_step_and_other_layout_equal_checked_step(full):
+    w, inp, res = full
+    other = "physical" if w.meta_layout == "logical" else "logical"
+    print(f"[full-size] {w.name}: refresh step, {other} layout", flush=True)
+    g = geometry(inp, "kv", w.meta_layout)
+    meta = res["meta"].clone()
+    for b, n in enumerate(inp["n_pages_host"]):
+        # as built before the last token was appended
+        if w.meta_layout == "logical":
+            meta[b, :, int(n) - 1] = 1.0
+        else:
+            meta[int(inp["page_table"][b, int(n) - 1])] = 1.0
+    step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
+                      inp["scale"])
+    out, lse = step.sparse(inp["q"], inp["k_pool"], inp["v_pool"], meta, inp["page_table"],
+                           inp["seq_lens"], inp["sink"], refresh_tail=True)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(meta), bits(res["meta"]))
+    _same_step(inp, res, {"scores": step.scores.cpu().numpy(), "sel": step.sel.cpu().numpy(),
+                          "sel_count": step.sel_count.cpu().numpy(),
+                          "out": out.cpu().numpy().astype(np.float64),
+                          "lse": lse.cpu().numpy().astype(np.float64)}, "refresh")
+    del meta, step, out, lse
+    res_o = run_step(inp, meta_layout=other)
+    _same_step(inp, res, res_o, f"{other} layout")
+    del res_o
+    torch.cuda.empty_cache()
+
+
 def test_sampled_units_match_oracle(full):
     w, inp, res = full
     worst, n_amb = 0.0, 0
@@ -186,13 +233,12 @@ def test_sampled_units_match_oracle_with_8bit_metadata(full):
     the sampled units bit for bit against the oracle's directed rounding,
     scores against fp64 on the 8-bit values, page lists and outputs."""
     w, inp, _ = full
-    res = run_step(inp, meta_format="fp8")
+    res = run_step(inp, meta_format="fp8", meta_layout=FP8_LAYOUT)
     for b, g in _sample_units(w, k=2):
         print(f"[full-size fp8] {w.name} unit b={b} g={g}", flush=True)
         hu = unit_host(inp, b, g, meta_format="fp8")
         n = int(inp["n_pages_host"][b])
-        phys = inp["page_table"][b, :n].long()
-        dev = res["meta"][phys, g].cpu().numpy()
+        dev = unit_meta(inp, res["meta"], b, g).cpu().numpy()
         kmax, kmin = ref.unit_page_meta(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
                                         hu["seq_lens"], 0, 0, hu["page_size"])
         cmax, cmin = ref.fp8_bounds(kmax, kmin)

@@ -6,7 +6,8 @@ replay on queries changed in place matches the eager step on them.
 
 Steps covered: the fused top-k step with the last page refreshed inside the
 score launch and several splits merged in the decode launch, the same with
-one split, the top-delta step, and the fp32-pool (vector-ALU) kernels."""
+one split, the top-delta step, the fp32-pool (vector-ALU) kernels, and the
+metadata in the logical layout (the benchmark's step)."""
 
 import pytest
 import torch
@@ -28,6 +29,7 @@ CASES = [
        ctx_range=(600, 2400), budget_pages=20, n_sink=1, n_local=2, sink_logits=True,
        kv_dtype="f32", seed=51, n_splits=3, dense_splits=4, max_pages=160), dict()),
     (wl.B32_64K, dict()),                         # the benchmark's step
+    (SMALL[2], dict(layout="logical", n_splits=1)),  # logical metadata layout, one split
 ]
 
 
@@ -46,7 +48,7 @@ def test_graph_replays_equal_eager(case):
     w, kw = case
     print(f"case {w.name} {kw}", flush=True)
     inp = wl.make_inputs(w, device="cuda")
-    g = geometry(inp)
+    g = geometry(inp, "kv", kw.get("layout", w.meta_layout))
     meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
     step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local,
                       kw.get("n_splits", w.n_splits), w.dense_splits, inp["scale"],

@@ -14,11 +14,12 @@ Per case:
 - top-delta at a drawn delta: fused equals unfused bit for bit; the selection
   equals the oracle's rule on the device's own scores; outputs within the gate;
 - the dense decode within the gate of exact softmax attention;
-- with pool-dtype and with 8-bit metadata: the refresh of the last pages
-  inside the score launch equals the build followed by the score, bit for
-  bit; the 8-bit codes equal the oracle's directed rounding; scores on them
-  within SCORE_REL of fp64 and the top-k selection identical outside the
-  ambiguity band.
+- with pool-dtype and with 8-bit metadata, in the physical and the logical
+  metadata layout: the refresh of the last pages inside the score launch
+  equals the build followed by the score, bit for bit; the 8-bit codes equal
+  the oracle's directed rounding; scores on them within SCORE_REL of fp64 and
+  the top-k selection identical outside the ambiguity band; the logical
+  layout's metadata and scores equal the physical layout's bit for bit.
 """
 
 import numpy as np
@@ -27,8 +28,9 @@ import torch
 
 import oracle as ref
 import workloads as wl
-from _gpu_helpers import (SCORE_REL, check_meta_unit, check_selection, check_unit_outputs,
-                          gate, geometry, rel_l2, score_rel_err, unit_host)
+from _gpu_helpers import (SCORE_REL, bits, check_meta_unit, check_selection,
+                          check_unit_outputs, gate, geometry, rel_l2, score_rel_err, unit_host,
+                          unit_meta)
 from sparse_long_context_page_amd import DecodeStep, build_meta, ops
 
 pytestmark = pytest.mark.gpu
@@ -211,30 +213,46 @@ def test_random_geometry(case):
          f"dense {worst_dense:.2e} (gate {gate(w):.0e}); top-delta units below budget: {fewer}")
 
 
+@pytest.mark.parametrize("meta_layout", ["physical", "logical"])
 @pytest.mark.parametrize("meta_format", ["kv", "fp8"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0].name for c in CASES])
-def test_random_geometry_refresh_and_meta_format(case, meta_format):
+def test_random_geometry_refresh_and_meta_format(case, meta_format, meta_layout):
     w, tighten, _ = case
-    _say(f"case {w.name} tighten={tighten} meta={meta_format}")
+    _say(f"case {w.name} tighten={tighten} meta={meta_format} layout={meta_layout}")
     inp = _inputs(w, tighten)
-    g = geometry(inp, meta_format)
+    g = geometry(inp, meta_format, meta_layout)
     full = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
     want = torch.empty((g.batch, g.num_kv_heads, g.max_pages), device="cuda")
     ops.ps_score_pages(g, inp["q"], full, inp["page_table"], inp["seq_lens"], want)
     stale = full.clone()
-    tails = [int(inp["page_table"][b, int(n) - 1]) for b, n in enumerate(inp["n_pages_host"])]
-    if meta_format == "fp8":
-        stale[tails] = 0x38  # 1.0, as if built before the last token was appended
-    else:
-        stale[tails] = 1.0
+    # the last pages' metadata as if built before the last token was appended
+    one = 0x38 if meta_format == "fp8" else 1.0  # 1.0 in E4M3 or in the pool dtype
+    for b, n in enumerate(inp["n_pages_host"]):
+        if meta_layout == "logical":
+            stale[b, :, int(n) - 1] = one
+        else:
+            stale[int(inp["page_table"][b, int(n) - 1])] = one
     got = torch.full_like(want, float("nan"))
     _say("  refresh score")
     ops.ps_refresh_score_pages(g, inp["q"], inp["k_pool"], stale, inp["page_table"],
                                inp["seq_lens"], got)
     torch.cuda.synchronize()
-    assert torch.equal(stale, full)
+    assert torch.equal(bits(stale), bits(full))
     for b, n in enumerate(inp["n_pages_host"]):
         assert torch.equal(got[b, :, :int(n)], want[b, :, :int(n)]), b
+    if meta_layout == "logical":
+        # the same metadata and scores as the physical layout, bit for bit
+        gp = geometry(inp, meta_format, "physical")
+        phys_meta = build_meta(gp, inp["k_pool"], inp["page_table"], inp["seq_lens"])
+        phys_scores = torch.empty_like(want)
+        ops.ps_score_pages(gp, inp["q"], phys_meta, inp["page_table"], inp["seq_lens"],
+                           phys_scores)
+        torch.cuda.synchronize()
+        for b, n in enumerate(inp["n_pages_host"]):
+            for kv in range(w.num_kv_heads):
+                assert torch.equal(bits(unit_meta(inp, full, b, kv)),
+                                   bits(unit_meta(inp, phys_meta, b, kv))), (b, kv)
+            assert torch.equal(want[b, :, :int(n)], phys_scores[b, :, :int(n)]), b
 
     step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
                       inp["scale"])
@@ -250,14 +268,13 @@ def test_random_geometry_refresh_and_meta_format(case, meta_format):
     worst = 0.0
     for b in range(w.batch):
         n = int(inp["n_pages_host"][b])
-        phys = inp["page_table"][b, :n].long().cpu()
         for kv in range(w.num_kv_heads):
             hu = unit_host(inp, b, kv, meta_format=meta_format)
             if meta_format == "fp8":
                 kmax, kmin = ref.unit_page_meta(hu["k_pool"], hu["kv_dtype"], hu["page_table"],
                                                 hu["seq_lens"], 0, 0, hu["page_size"])
                 cmax, cmin = ref.fp8_bounds(kmax, kmin)
-                dev = meta_h[phys, kv].numpy()
+                dev = unit_meta(inp, meta_h, b, kv).numpy()
                 np.testing.assert_array_equal(dev[:, 0], cmax, err_msg=f"kmax b={b} g={kv}")
                 np.testing.assert_array_equal(dev[:, 1], cmin, err_msg=f"kmin b={b} g={kv}")
             else:

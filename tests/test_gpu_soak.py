@@ -21,7 +21,7 @@ REPLAYS = 2000
 def test_in_launch_merge_equals_combine_over_replays():
     w = wl.B32_64K
     inp = wl.make_inputs(w, device="cuda")
-    g = geometry(inp)
+    g = geometry(inp, "kv", w.meta_layout)
     meta = build_meta(g, inp["k_pool"], inp["page_table"], inp["seq_lens"])
     step = DecodeStep(g, w.budget_pages, w.n_sink, w.n_local, w.n_splits, w.dense_splits,
                       inp["scale"])

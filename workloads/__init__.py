@@ -66,6 +66,9 @@ class Workload:
     seed: int = 0
     n_splits: int = 8                      # split-KV count of the sparse decode
     dense_splits: int = 32                 # split-KV count of the dense decode
+    # metadata layout the workload is run with ("physical" | "logical"),
+    # like the split counts a measured choice, not part of the inputs
+    meta_layout: str = "physical"
 
     @property
     def group(self) -> int:
@@ -84,13 +87,14 @@ B8_16K = Workload("b8_16k_needles_sink_page", batch=8, num_q_heads=12, num_kv_he
                   seed=1002, n_splits=8, dense_splits=32)
 B32_64K = Workload("b32_64k_needles_local4", batch=32, num_q_heads=12, num_kv_heads=2,
                     head_dim=128, context=65536, budget_pages=128, n_local=4, needles=8,
-                    seed=1003, n_splits=4, dense_splits=64)
+                    seed=1003, n_splits=4, dense_splits=64, meta_layout="logical")
 SINK = Workload("b16_32k_learned_sink", batch=16, num_q_heads=64, num_kv_heads=8, head_dim=64,
                 context=32768, budget_pages=64, sink_logits=True, seed=1004, n_splits=1,
                 dense_splits=32)
 RAGGED = Workload("b64_ragged_4k_128k_shared_pool", batch=64, num_q_heads=28, num_kv_heads=4,
                   head_dim=128, ctx_range=(4096, 131072), budget_pages=128, needles=8,
-                  permuted_pool=True, max_pages=8192, seed=1005, n_splits=1, dense_splits=64)
+                  permuted_pool=True, max_pages=8192, seed=1005, n_splits=1, dense_splits=64,
+                  meta_layout="logical")
 
 # The headline shape with one query head per KV head, a forced sink page whose
 # keys follow the needle recipe and the last 4 pages forced: the top-delta
@@ -100,7 +104,7 @@ RAGGED = Workload("b64_ragged_4k_128k_shared_pool", batch=64, num_q_heads=28, nu
 TOPDELTA_BINDS = Workload("b32_64k_g1_sink_needle_topdelta", batch=32, num_q_heads=2,
                           num_kv_heads=2, head_dim=128, context=65536, budget_pages=128,
                           n_sink=1, n_local=4, needles=8, sink_page_needle=True, seed=1006,
-                          n_splits=4, dense_splits=64)
+                          n_splits=4, dense_splits=64, meta_layout="logical")
 
 WORKLOADS = {w.name: w for w in (TINY, TINY_DENSE, B8_16K, B32_64K, SINK, RAGGED,
                                  TOPDELTA_BINDS)}
