@@ -9,9 +9,12 @@ independent input batches are drawn and the timed steps cycle through them,
 so each step reads data that the previous steps evicted from the 256 MB
 memory-side cache (the working set of one step is about 204 MB at the
 b32/64k workload). The K timed steps are replays of one HIP graph holding
-one step per input set (K // R replays, plus K % R one-step graphs), each
-replay between its own HIP events: `value` is the median per-step time over
-those replays, `ms_per_step` the mean over the whole timed region. Before
+G steps, whole passes over the input sets in order, at least 16 (a decode
+step sits in a model's captured forward once per layer, and the graph's
+launch cost is shared the same way): K // G replays, plus K % G one-step
+graphs, each replay between its own HIP events. `value` is the median
+per-step time over those replays, `ms_per_step` the mean over the whole
+timed region. Before
 timing, one step is checked against the fp64 oracle on sampled (request, KV
 head) units; no timing is printed if that check fails.
 
@@ -56,13 +59,13 @@ CONFIGS = ("tiny", "tiny_dense", "b8_16k_needles_sink_page", HEADLINE, "b16_32k_
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=320)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--configs", default="all",
                     help="workloads measured besides the headline under 'configs': all, none, "
                          "or a comma-separated list of names")
-    ap.add_argument("--config-steps", type=int, default=100,
+    ap.add_argument("--config-steps", type=int, default=160,
                     help="timed steps of each workload under 'configs'")
     ap.add_argument("--sets", type=int, default=None,
                     help="independent input batches cycled (default: enough that one pass "
@@ -107,6 +110,13 @@ def parse():
 
 
 MALL_BYTES = 256 << 20  # memory-side (Infinity) cache of the chip
+
+# A step is timed inside a graph of at least this many steps, as a decode
+# step sits in the captured forward of a model once per layer: the input sets
+# are cycled in order (each set's bytes are evicted from the memory-side cache
+# between two of its uses) and the graph's launch cost is shared by the steps
+# as a forward's layers share it.
+MIN_GRAPH_STEPS = 16
 
 
 def default_sets(w, meta_format, acc):
@@ -158,6 +168,18 @@ def run_dense_step(s):
     inp, step = s["inp"], s["step"]
     return step.dense(inp["q"], inp["k_pool"], inp["v_pool"], inp["page_table"],
                       inp["seq_lens"], inp["sink"])
+
+
+def capture_steps(fn, sets, torch):
+    """One graph of whole passes over the input sets, at least
+    MIN_GRAPH_STEPS steps; returns (graph, steps in it)."""
+    passes = -(-MIN_GRAPH_STEPS // len(sets))
+
+    def body(_):
+        for _ in range(passes):
+            for s in sets:
+                fn(s)
+    return capture(body, None, torch), passes * len(sets)
 
 
 def capture(fn, s, torch):
@@ -497,7 +519,7 @@ def timed_steps(multi, singles, r, steps, torch):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        (multi if i < n_multi else singles[i - n_multi]).replay()
+        (multi if i < n_multi else singles[(i - n_multi) % len(singles)]).replay()
         b.record()
         ev.append((a, b, r if i < n_multi else 1))
     torch.cuda.synchronize()
@@ -561,25 +583,23 @@ def main():
         return
 
     # -- graph-captured step loop (the timed region) -----------------------
-    # One graph holds one decode step per input set, in order (R steps), as a
-    # step sits inside a captured model forward; K steps are K // R replays
-    # of it plus K % R one-step graphs. Every step is the whole hot path.
+    # One graph holds G decode steps, whole passes over the input sets in
+    # order (at least MIN_GRAPH_STEPS), as steps sit inside a captured model
+    # forward; K steps are K // G replays of it plus K % G one-step graphs.
+    # Every step is the whole hot path.
     graphs = [capture(run_sparse_step, s, torch) for s in sets]
     graphs[0].replay()
     torch.cuda.synchronize()
     if not torch.equal(s0["step"].out, out_eager):
         raise SystemExit("graph replay differs from the eager step")
 
-    def all_sets(_):
-        for s in sets:
-            run_sparse_step(s)
-    multi = capture(all_sets, None, torch)
+    multi, r_graph = capture_steps(run_sparse_step, sets, torch)
     for i in range(args.warmup):
         graphs[i % len(graphs)].replay()
     multi.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    gpu_ms, per_step = timed_steps(multi, graphs, len(sets), args.steps, torch)
+    gpu_ms, per_step = timed_steps(multi, graphs, r_graph, args.steps, torch)
     wall_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = gpu_ms / args.steps
     step_us = pct(per_step, 0.5)  # the median replay
@@ -812,7 +832,8 @@ def main():
                    "metadata_layout": layout_of(args, w),
                    "n_splits": w.n_splits, "input_sets": len(sets),
                    "path": path,
-                   "graph_captured": f"{len(sets)} steps (one per input set) per graph"},
+                   "graph_captured": f"{r_graph} steps ({r_graph // len(sets)} passes over "
+                                     f"the {len(sets)} input sets) per graph"},
         "effective_hbm_gbps": round(eff_gbps, 1),
         "hbm_frac_of_peak": round(eff_gbps / PEAK_HBM_GBPS, 4),
         "touched_bytes": touched,
@@ -950,15 +971,12 @@ def config_line(args, w, workers, torch, wl, ps, acc):
               else dense_parity(s0, w, units, wl))
     graphs = [capture(run, s, torch) for s in sets]
 
-    def all_sets(_):
-        for s in sets:
-            run(s)
-    multi = capture(all_sets, None, torch)
+    multi, r_graph = capture_steps(run, sets, torch)
     for i in range(args.warmup):
         graphs[i % r].replay()
     multi.replay()
     torch.cuda.synchronize()
-    total_ms, per = timed_steps(multi, graphs, r, args.config_steps, torch)
+    total_ms, per = timed_steps(multi, graphs, r_graph, args.config_steps, torch)
     step_us = pct(per, 0.5)
 
     lens = [int(x) for x in s0["inp"]["seq_lens_host"]]
@@ -983,7 +1001,7 @@ def config_line(args, w, workers, torch, wl, ps, acc):
            "effective_hbm_gbps": round(gbps, 1),
            "hbm_frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
            "path": path, "n_splits": w.n_splits if path == "sparse" else w.dense_splits,
-           "input_sets": r, "parity": parity,
+           "input_sets": r, "steps_per_graph": r_graph, "parity": parity,
            "config": {"batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                       "head_dim": w.head_dim,
                       "context": w.context if w.context else list(w.ctx_range),
@@ -1045,14 +1063,11 @@ def topdelta_binds_line(args, torch, wl, ps, acc):
     for kind, ss in (("topdelta", sets), ("topk", base)):
         graphs = [capture(run_sparse_step, s, torch) for s in ss]
 
-        def all_sets(_, ss=ss):
-            for s in ss:
-                run_sparse_step(s)
-        multi = capture(all_sets, None, torch)
+        multi, r_graph = capture_steps(run_sparse_step, ss, torch)
         for i in range(args.warmup):
             graphs[i % r].replay()
         torch.cuda.synchronize()
-        _, per = timed_steps(multi, graphs, r, args.config_steps, torch)
+        _, per = timed_steps(multi, graphs, r_graph, args.config_steps, torch)
         res[kind] = pct(per, 0.5)
         del graphs, multi
     for s in sets:  # leave every set as one whole top-delta step leaves it
@@ -1108,14 +1123,11 @@ def topdelta_line(args, w, sets, step_us_topk, torch, wl, ps):
     parity = parity_gate(sets_d[0], w, sample_units(w, args.parity_units), wl)
     kept = sets_d[0]["step"].sel_count.cpu().numpy()
 
-    def all_sets(_):
-        for s in sets_d:
-            run_sparse_step(s)
-    multi = capture(all_sets, None, torch)
+    multi, r_graph = capture_steps(run_sparse_step, sets_d, torch)
     for _ in range(3):
         multi.replay()
     torch.cuda.synchronize()
-    reps = max(args.steps // len(sets_d), 1)
+    reps = max(args.steps // r_graph, 1)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -1123,7 +1135,7 @@ def topdelta_line(args, w, sets, step_us_topk, torch, wl, ps):
         multi.replay()
     e1.record()
     torch.cuda.synchronize()
-    step_us = e0.elapsed_time(e1) / (reps * len(sets_d)) * 1e3
+    step_us = e0.elapsed_time(e1) / (reps * r_graph) * 1e3
 
     n_k = 40
 
@@ -1166,14 +1178,11 @@ def fp8_line(args, w, sets, step_us_kv, torch, wl, ps, acc):
     torch.cuda.synchronize()
     parity = parity_gate(sets8[0], w, sample_units(w, args.parity_units), wl)
 
-    def all_sets(_):
-        for s in sets8:
-            run_sparse_step(s)
-    multi = capture(all_sets, None, torch)
+    multi, r_graph = capture_steps(run_sparse_step, sets8, torch)
     for _ in range(3):
         multi.replay()
     torch.cuda.synchronize()
-    reps = max(args.steps // len(sets8), 1)
+    reps = max(args.steps // r_graph, 1)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -1181,7 +1190,7 @@ def fp8_line(args, w, sets, step_us_kv, torch, wl, ps, acc):
         multi.replay()
     e1.record()
     torch.cuda.synchronize()
-    step_us = e0.elapsed_time(e1) / (reps * len(sets8)) * 1e3
+    step_us = e0.elapsed_time(e1) / (reps * r_graph) * 1e3
 
     n_k = 40
 
