@@ -69,6 +69,16 @@ int main() {
   ps_geom ps16 = g;
   ps16.page_size = 32;
   expect("page size", ps_score_pages(&ps16, F, X, I, I, F, nullptr), PS_ERR_UNSUPPORTED);
+  ps_geom layout = g;
+  layout.meta_layout = 2;
+  expect("meta layout", ps_score_pages(&layout, F, X, I, I, F, nullptr), PS_ERR_SHAPE);
+  layout.meta_layout = -1;
+  expect("meta layout", ps_score_pages(&layout, F, X, I, I, F, nullptr), PS_ERR_SHAPE);
+  // logical metadata B * Hkv * max_pages * 2 * D * 4 bytes beyond int64; the
+  // physical layout of the same geometry passes the size checks
+  ps_geom huge = geom(0x7fffffff, 8, 8, 128, (1 << 26) - 1, 128, PS_F32);
+  huge.meta_layout = PS_META_LOGICAL;
+  expect("logical overflow", ps_score_pages(&huge, F, X, I, I, F, nullptr), PS_ERR_OVERFLOW);
 
   // every entry point: a missing pointer, then a valid call (one launch)
   int before = g_launches;
@@ -118,9 +128,15 @@ int main() {
   expect("full", ps_full_decode(&g, F, X, X, I, I, 0.1f, 8, F, F, nullptr), PS_OK);
   expect("combine null", ps_combine(&g, F, F, 4, nullptr, nullptr, nullptr, nullptr), PS_ERR_NULL);
   expect("combine", ps_combine(&g, F, F, 4, nullptr, F, nullptr, nullptr), PS_OK);
+  // the metadata entry points with the logical layout
+  ps_geom logical = g;
+  logical.meta_layout = PS_META_LOGICAL;
+  expect("meta logical", ps_build_page_meta(&logical, X, I, I, nullptr, 64, X, nullptr), PS_OK);
+  expect("score logical", ps_score_pages(&logical, F, X, I, I, F, nullptr), PS_OK);
+  expect("refresh logical", ps_refresh_score_pages(&logical, F, X, X, I, I, F, nullptr), PS_OK);
   const int launched = g_launches - before;
-  if (launched != 11) {
-    fprintf(stderr, "%d launches, expected 11\n", launched);
+  if (launched != 14) {
+    fprintf(stderr, "%d launches, expected 14\n", launched);
     ++failures;
   }
 
