@@ -535,11 +535,11 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
     // best at 32 x 4096 pages, 2 and 16 worse). With the metadata in logical
     // order a wavefront's prologue is one round trip shorter, and twice the
     // wavefronts with half the tiles each measured faster (32 x 4096 pages:
-    // score 26.4 -> 25.0 us); in the physical layout that lost (learned sink
-    // +2 us, 8-bit metadata +6 us).
+    // score 26.4 -> 25.0 us); in the physical layout, and with 8-bit codes
+    // in either, that lost (learned sink +2 us, 8-bit metadata +4 to +6 us).
     const int tiles_per_unit = (s.max_pages + 15) / 16;
     const int64_t tiles = (int64_t)tiles_per_unit * s.batch * s.hkv;
-    const int64_t waves_target = s.meta_logical ? 4096 : 2048;
+    const int64_t waves_target = (s.meta_logical && !s.meta8) ? 4096 : 2048;
     const int tpw =
         (int)std::min<int64_t>(kMaxTiles, std::max<int64_t>(1, tiles / waves_target));
     const int per_block = kMfmaWaves * tpw * 16;
