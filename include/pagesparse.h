@@ -381,7 +381,9 @@ int ps_combine(const ps_geom* geom, const float* part_acc, const float* part_ml,
 /* Human-readable name of a ps_status (static storage; never NULL). */
 const char* ps_strerror(int status);
 
-/* ABI version of this library: (major << 16) | minor. */
+/* ABI version of this library: (major << 16) | minor. This header is 2.0
+ * (ps_geom gained meta_layout: a caller built against 1.x passes a shorter
+ * struct, so the major version changed). */
 int ps_abi_version(void);
 
 #ifdef __cplusplus

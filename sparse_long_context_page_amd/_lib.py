@@ -45,6 +45,8 @@ PS_META_FP8_E4M3 = 1
 PS_META_PHYSICAL = 0
 PS_META_LOGICAL = 1
 
+ABI_MAJOR = 2  # the ps_abi_version() major that PsGeom matches
+
 
 class PsGeom(ctypes.Structure):
     _fields_ = [
@@ -113,6 +115,10 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_char_p if name == "ps_strerror" else ctypes.c_int
+    major = lib.ps_abi_version() >> 16
+    if major != ABI_MAJOR:  # PsGeom above mirrors this major version's ps_geom
+        raise NativeLibraryMissing(
+            f"{LIB_PATH} has ABI {major}.x, this binding needs {ABI_MAJOR}.x; rebuild it")
     _lib = lib
     return lib
 
