@@ -84,7 +84,7 @@ TINY = Workload("tiny", batch=1, num_q_heads=4, num_kv_heads=1, head_dim=64, con
 TINY_DENSE = TINY.replace(name="tiny_dense", budget_pages=64, n_splits=8)
 B8_16K = Workload("b8_16k_needles_sink_page", batch=8, num_q_heads=12, num_kv_heads=2,
                   head_dim=128, context=16384, budget_pages=128, n_sink=1, needles=4,
-                  seed=1002, n_splits=8, dense_splits=32)
+                  seed=1002, n_splits=8, dense_splits=32, meta_layout="logical")
 B32_64K = Workload("b32_64k_needles_local4", batch=32, num_q_heads=12, num_kv_heads=2,
                     head_dim=128, context=65536, budget_pages=128, n_local=4, needles=8,
                     seed=1003, n_splits=4, dense_splits=64, meta_layout="logical")
