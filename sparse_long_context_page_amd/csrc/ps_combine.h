@@ -44,6 +44,55 @@ __device__ __forceinline__ void combine_row(const float* __restrict__ acc,
                                             float sig, float* __restrict__ o, float* lse_out) {
   auto ld = [](const float* p) { return load_partial<COHERENT>(p); };
   const int lane = threadIdx.x % kWave;
+  constexpr int kDPerLane = 2;  // head_dim <= 128
+  constexpr int kBatch = 8;
+  if (n_splits <= kBatch) {
+    // Few splits (the merge inside the decode launch): every partial is
+    // requested at once, one round trip instead of one per stage below; the
+    // arithmetic is the general path's, operation for operation.
+    float ms = -INFINITY, ls = 0.0f;
+    if (lane < n_splits) {
+      ms = ld(ml + 2 * lane);
+      ls = ld(ml + 2 * lane + 1);
+    }
+    float v[kBatch][kDPerLane];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+#pragma unroll
+      for (int k = 0; k < kDPerLane; ++k) {
+        const int d = lane + k * kWave;
+        v[j][k] = (j < n_splits && d < d_) ? ld(acc + (int64_t)j * d_ + d) : 0.0f;
+      }
+    }
+    float mx = fmax_(wave_max_f32(ms), sig);
+    if (mx == -INFINITY) {
+      for (int d = lane; d < d_; d += kWave) o[d] = 0.0f;
+      if (lse_out && lane == 0) *lse_out = -INFINITY;
+      return;
+    }
+    float l = (lane < n_splits && ms != -INFINITY) ? __builtin_fmaf(expf(ms - mx), ls, 0.0f)
+                                                   : 0.0f;
+    l = wave_sum_f32(l);
+    if (sig != -INFINITY) l += expf(sig - mx);
+    const float inv = 1.0f / l;
+    const float w = (lane < n_splits && ms != -INFINITY) ? expf(ms - mx) : 0.0f;
+    float a[kDPerLane] = {0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      const float wj = __shfl(w, j);
+      if (j < n_splits) {
+#pragma unroll
+        for (int k = 0; k < kDPerLane; ++k) a[k] = __builtin_fmaf(wj, v[j][k], a[k]);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kDPerLane; ++k) {
+      const int d = lane + k * kWave;
+      if (d < d_) o[d] = a[k] * inv;
+    }
+    if (lse_out && lane == 0) *lse_out = mx + logf(l);
+    return;
+  }
   float mx = -INFINITY;
   for (int s = lane; s < n_splits; s += kWave) mx = fmax_(mx, ld(ml + 2 * s));
   mx = fmax_(wave_max_f32(mx), sig);
@@ -63,8 +112,6 @@ __device__ __forceinline__ void combine_row(const float* __restrict__ acc,
 
   // a chunk of up to 64 split weights is held one per lane and broadcast with
   // shuffles; the accumulator rows of 8 splits are loaded before they are used
-  constexpr int kDPerLane = 2;  // head_dim <= 128
-  constexpr int kBatch = 8;
   float a[kDPerLane] = {0.0f, 0.0f};
   for (int s0 = 0; s0 < n_splits; s0 += kWave) {
     const int sl = s0 + lane;
