@@ -540,8 +540,13 @@ hipError_t launch_score_pages(const Shape& s, const float* q, const void* meta,
     const int tiles_per_unit = (s.max_pages + 15) / 16;
     const int64_t tiles = (int64_t)tiles_per_unit * s.batch * s.hkv;
     const int64_t waves_target = (s.meta_logical && !s.meta8) ? 4096 : 2048;
-    const int tpw =
-        (int)std::min<int64_t>(kMaxTiles, std::max<int64_t>(1, tiles / waves_target));
+    // In the logical layout runs are also capped at 8 tiles: with requests of
+    // very different lengths (tiles count max_pages, not the lengths) the
+    // longest requests' wavefronts would otherwise stream 16 tiles each
+    // (ragged batch of 4k to 128k tokens: refresh+score 116.7-119.3 -> 114.5 us;
+    // a cap of 4 lost, 128 us).
+    const int cap = (s.meta_logical && !s.meta8) ? 8 : kMaxTiles;
+    const int tpw = (int)std::min<int64_t>(cap, std::max<int64_t>(1, tiles / waves_target));
     const int per_block = kMfmaWaves * tpw * 16;
     const int chunks = (s.max_pages + per_block - 1) / per_block;
     const int64_t blocks = (int64_t)chunks * s.batch * s.hkv;
