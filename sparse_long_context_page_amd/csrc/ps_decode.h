@@ -1,8 +1,9 @@
 // Split-KV decode over every page (dense), a page list (sparse), or the
 // pages the workgroup selects itself (top-k or top-delta): per split, the
 // running max, normaliser and unnormalised accumulator of the softmax of
-// scale*q.k for every query head of one KV head; with one split, optionally
-// the merged output. ("Don't read the haystack", sections "Part one: hitting
+// scale*q.k for every query head of one KV head; optionally the merged
+// output (with one split, or with several in the selecting modes, where the
+// last split of a unit to finish merges). ("Don't read the haystack", sections "Part one: hitting
 // the wall on purpose" and "Part two: the skipping"; "Attention: Undivided &
 // Uncompressed", section "Traffic", for the rescaling merge.) Two kernels:
 // decode_kernel (fp32 pools, vector ALUs, described here) and
@@ -440,16 +441,16 @@ __global__ __launch_bounds__(kDecWaves * kWave) void decode_kernel(
 // coordinates of a lane are 8 consecutive d of one 16-byte load straight from
 // the pool), B = the group's queries scaled by scale*log2(e) (column = head,
 // padded to 16 with zeros), split exactly into hi + mid + lo bf16 terms in
-// LDS once per workgroup and read from there as each product is issued. Lane (token group, head) then holds 4 logits of one
-// head; the page max per head is a 3-step shuffle, the running max is uniform
-// per head and raised lazily (by more than 8 in log2 units), and p =
-// 2^(x - m) is handed to the V owners through LDS. P.V runs on the vector
-// ALUs with V in row layout (lane = (row group, 8 columns)), every lane
-// accumulating all G heads for its rows and columns. The queries are
-// requested first; each wavefront resolves its page ids (list entry, then
-// table entry) a block of 4 ahead, keeps the next page's K and V in flight
-// while the current page is attended, and leaves its accumulators unreduced
-// in LDS for the workgroup merge (no cross-row shuffles).
+// LDS once per workgroup and read from there as each product is issued. Lane
+// (token group, head) then holds 4 logits of one head; the page max per head
+// is a 2-step shuffle, the running max is uniform per head and raised lazily
+// (by more than 8 in log2 units), and p = 2^(x - m) stays in the lane as the
+// A operand of P.V on the matrix cores (v_mfma_f32_16x16x16_bf16, p split
+// into hi + lo bf16; B = V staged in LDS and read transposed, 16 columns per
+// product). The queries are requested first; each wavefront resolves its page
+// ids (list entry, then table entry) two blocks of P pages ahead, keeps the
+// next block's K and V in flight while the current one is attended, and
+// leaves its state in LDS for the workgroup merge.
 __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
