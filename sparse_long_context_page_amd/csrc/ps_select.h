@@ -25,6 +25,8 @@ namespace ps {
 
 constexpr int kSelDigitBits = 8;
 constexpr int kSelBins = 1 << kSelDigitBits;
+constexpr int kBpl = kSelBins / kWave;  // histogram bins per lane in the scan
+static_assert(kBpl >= 1 && kSelBins % kWave == 0, "bins per lane");
 constexpr int kSelRankMax = kWave;  // threshold bins up to this size are ranked directly
 
 template <int WAVES>
@@ -170,19 +172,22 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
     }
     for (int i = tid; i < kSelBins; i += kThreads) sh.hist[(pass + 1) % 3][i] = 0;
     __syncthreads();
-    // Lane l holds bins 4l..4l+3. The threshold bin d holds the remaining-th
-    // largest key: keys in bins above d < remaining <= keys from d up.
-    int hb[4];
+    // Lane l holds bins kBpl*l .. kBpl*l + kBpl - 1. The threshold bin d holds
+    // the remaining-th largest key: keys in bins above d < remaining <= keys
+    // from d up.
+    int hb[kBpl];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) hb[i] = h[4 * lane + i];
-    const int mine = hb[0] + hb[1] + hb[2] + hb[3];
-    const int incl = wave_prefix_sum(mine);  // keys in bins 0 .. 4*lane+3
+    for (int i = 0; i < kBpl; ++i) hb[i] = h[kBpl * lane + i];
+    int mine = 0;
+#pragma unroll
+    for (int i = 0; i < kBpl; ++i) mine += hb[i];
+    const int incl = wave_prefix_sum(mine);  // keys in bins 0 .. kBpl*lane+kBpl-1
     int acc = __builtin_amdgcn_readlane(incl, kWave - 1) - incl;  // keys in bins above
     int found_d = -1, found_rem = 0, found_bin = 0;
 #pragma unroll
-    for (int i = 3; i >= 0; --i) {
+    for (int i = kBpl - 1; i >= 0; --i) {
       if (found_d < 0 && acc < remaining && acc + hb[i] >= remaining) {
-        found_d = 4 * lane + i;
+        found_d = kBpl * lane + i;
         found_rem = remaining - acc;
         found_bin = hb[i];
       }
