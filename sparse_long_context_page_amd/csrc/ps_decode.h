@@ -497,7 +497,9 @@ void decode_mfma_kernel(
   __shared__ __align__(16) uint16_t qsp[3][8][D + 32];  // split scaled queries
   __shared__ __align__(16) uint16_t vt[W][16][D + 8];   // V page of each wavefront
   __shared__ float sm_m[W][G], sm_mt[W][G], sm_l[W][G];
-  __shared__ float sm_acc[W][G][D];
+  // rows padded by 4: the heads 4 apart that one store writes then fall on
+  // different banks
+  __shared__ float sm_acc[W][G][D + 4];
   // selecting modes: the selection's workspace and this split's share of the
   // list
   constexpr bool SEL = MODE >= kSelect;
