@@ -73,7 +73,9 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
 // thread calls tau_fn.issue() before the scores are requested and
 // tau_fn.prefetch() after (the threshold's loads: table entries, then key
 // rows), and tau = tau_fn() once the cut is known, so the threshold's round
-// trips overlap the passes (it may hold barriers).
+// trips overlap the passes (it may hold barriers; at least one workgroup
+// barrier separates prefetch() from it, so LDS written in prefetch() is
+// visible to every thread there).
 //
 // The kept candidates are the r best in the order (key descending, page
 // ascending). Radix passes narrow the r-th key's bits; once its bin holds at
@@ -335,9 +337,12 @@ __device__ __forceinline__ int select_unit(const float* __restrict__ row, int n,
 // e5) + (e6 + e7)). The maximum per head across the workgroup is exact in any
 // order.
 // issue() requests the page-table entries of the first forced tokens and the
-// queries (called before the selection requests its scores); operator()()
-// then requests the key rows, computes, and returns the threshold. Both are
-// called by every thread of the workgroup; operator()() holds two barriers.
+// queries (called before the selection requests its scores); prefetch()
+// requests those tokens' key rows and widens the queries into LDS (called
+// after the scores are requested); operator()() computes and returns the
+// threshold once the selection's passes are done (after at least one of its
+// barriers). All three are called by every thread of the workgroup;
+// operator()() holds one barrier.
 // DPP lane move of a double (both 32-bit halves), and the max over the 64
 // lanes (uniform result; exact in any order).
 template <int CTRL>
@@ -431,6 +436,18 @@ struct TopDeltaThreshold {
     const T* krow = k_pool + (((int64_t)phys0 * hkv + g) * kPage + tt) * D + (t % kParts) * kCoords;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) kv0[i] = ld16(krow + i * kVec);
+    // the queries, widened into LDS here (their load was issued before the
+    // table entries waited for above): the selection's barriers before the
+    // threshold is evaluated publish them, so the evaluation needs no
+    // barrier of its own
+    if (t < ng() * D / 4) {  // coordinates 4t .. 4t+3, within one segment
+      const int qh = (4 * t) / D, qd = (4 * t) % D;
+      double* dq = &sh->q[qh][(qd / kCoords) * (kCoords + kTdSegPad) + qd % kCoords];
+      dq[0] = (double)qv.x;
+      dq[1] = (double)qv.y;
+      dq[2] = (double)qv.z;
+      dq[3] = (double)qv.w;
+    }
   }
 
   __device__ double operator()() {
@@ -440,14 +457,6 @@ struct TopDeltaThreshold {
     const int wave = t / kWave;
     const int part = t % kParts;
     const int n_tok = tokens();
-    if (t < ng() * D / 4) {  // coordinates 4t .. 4t+3, within one segment
-      const int qh = (4 * t) / D, qd = (4 * t) % D;
-      double* dq = &sh->q[qh][(qd / kCoords) * (kCoords + kTdSegPad) + qd % kCoords];
-      dq[0] = (double)qv.x;
-      dq[1] = (double)qv.y;
-      dq[2] = (double)qv.z;
-      dq[3] = (double)qv.w;
-    }
     double mx[kG];
 #pragma unroll
     for (int h = 0; h < kG; ++h) mx[h] = -INFINITY;
@@ -469,7 +478,6 @@ struct TopDeltaThreshold {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) kv[i] = ld16(krow + i * kVec);
       }
-      if (base == 0) __syncthreads();  // sh->q complete
       double k64[kCoords];
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
