@@ -3,9 +3,10 @@
 // running max, normaliser and unnormalised accumulator of the softmax of
 // scale*q.k for every query head of one KV head; optionally the merged
 // output (with one split, or with several in the selecting modes, where the
-// last split of a unit to finish merges). ("Don't read the haystack", sections "Part one: hitting
-// the wall on purpose" and "Part two: the skipping"; "Attention: Undivided &
-// Uncompressed", section "Traffic", for the rescaling merge.) Two kernels:
+// last split of a unit to finish merges). ("Don't read the haystack",
+// sections "Part one: hitting the wall on purpose" and "Part two: the
+// skipping"; "Attention: Undivided & Uncompressed", section "Traffic", for
+// the rescaling merge.) Two kernels:
 // decode_kernel (fp32 pools, vector ALUs, described here) and
 // decode_mfma_kernel (bf16 pools, matrix cores, described at its definition).
 //
