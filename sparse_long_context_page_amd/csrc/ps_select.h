@@ -393,7 +393,8 @@ struct TopDeltaThreshold {
   static constexpr int kVec = Elem<T>::kPerVec;
   static constexpr int kLoads = kCoords / kVec;   // 16-byte key loads per thread
   static_assert(kLoads >= 1 && kCoords % kVec == 0, "key row split");
-  static_assert(kParts == 8 && kCoords % 4 == 0, "8 padded query segments, 4 coordinates per write");
+  static_assert(kParts == 8 && kCoords % 4 == 0,
+                "8 padded query segments, 4 coordinates per write");
   static_assert(kWave % kParts == 0, "a token's eight threads are lanes 8i..8i+7 of a wavefront");
   static_assert(kG * D / 4 <= kThreads, "one float4 of the queries per thread");
 
