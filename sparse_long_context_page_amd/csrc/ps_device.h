@@ -41,6 +41,13 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// A 16-byte load marked non-temporal (data read once).
+__device__ __forceinline__ uint4 ld16nt(const void* p) {
+  typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+  const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ void st16(void* p, const uint4& v) {
   *reinterpret_cast<uint4*>(p) = v;
 }
